@@ -1,0 +1,182 @@
+"""Oracle block allocator — test infrastructure only (see the package docstring).
+
+What it follows:
+  * Fixed-size blocks handed out on demand from one shared pool, one block table per request
+    mapping logical page -> physical block, blocks returned to the pool when the request
+    ends ("vLLM + PagedAttention：打造高并发LLM推理引擎", the four numbered steps under
+    "它是怎么工作的？"; "PagedAttention 与 vLLM 推理加速", §2.2 and §2.3).
+  * A request's token n lives in logical page n // block_size at offset n % block_size; the
+    physical block comes from the table (same page, §2.3 worked example: 7 tokens with
+    4-token blocks occupy pages 0 and 1, and page 1 has one unused slot).
+  * Several requests' tables may point at the same physical blocks (shared system prompt),
+    kept alive by reference counts; a write to a shared block first copies it
+    (copy-on-write) ("PagedAttention 与 vLLM 推理加速", §3.2 (3); "LLM Systems 24: Efficient
+    LLM Inference with PagedAttention and vLLM", §3 Conclusion).
+  * Running out of blocks is reported to the caller, who may preempt (same §3 Conclusion).
+
+Readings where the pages leave a choice open (each also listed in the design notes):
+  * Which free block is used next is not fixed by the pages.  The pool is a LIFO stack whose
+    initial pop order is the caller's ``free_order`` (default 0, 1, ..., N-1); freeing a
+    sequence walks its table in logical order and pushes each block whose count drops to 0,
+    so its last logical block is the first to be reused.
+  * ``append`` handles sequences in the order given.  A sequence whose length is a multiple
+    of the block size takes a fresh block; otherwise, if its last block is shared
+    (count > 1), it takes a fresh block, records the pair (old, new) for the caller to copy,
+    and gives up one reference to the old block; a sequence that finds count == 1 writes in
+    place.  The slot of the appended token is ``table[-1] * block_size + length %
+    block_size``.
+  * Every call either succeeds completely or changes nothing.
+"""
+from __future__ import annotations
+
+import copy
+
+
+class OracleError(Exception):
+    code = "ERROR"
+
+
+class InvalidArg(OracleError):
+    code = "INVALID_ARG"
+
+
+class OutOfBlocks(OracleError):
+    code = "OUT_OF_BLOCKS"
+
+
+class UnknownSeq(OracleError):
+    code = "UNKNOWN_SEQ"
+
+
+class DuplicateSeq(OracleError):
+    code = "DUPLICATE_SEQ"
+
+
+class OracleAllocator:
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise InvalidArg("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(x) for x in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise InvalidArg("free_order must be a permutation of range(num_blocks)")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        # Top of the stack is the end of the list, so the first pop returns order[0].
+        self.free = list(reversed(order))
+        self.ref = [0] * num_blocks
+        self.tables = {}
+        self.lens = {}
+
+    # -- helpers -----------------------------------------------------------------------
+    def _pop(self) -> int:
+        if not self.free:
+            raise OutOfBlocks("no free block")
+        b = self.free.pop()
+        self.ref[b] = 1
+        return b
+
+    def _snapshot(self):
+        return (list(self.free), list(self.ref), copy.deepcopy(self.tables), dict(self.lens))
+
+    def _restore(self, snap):
+        self.free, self.ref, self.tables, self.lens = snap
+
+    def _slot(self, seq) -> int:
+        n = self.lens[seq]
+        return self.tables[seq][n // self.block_size] * self.block_size + n % self.block_size
+
+    # -- operations --------------------------------------------------------------------
+    def add(self, seq, num_tokens: int):
+        """New sequence holding ``num_tokens`` tokens; returns their slots in order."""
+        if num_tokens < 0:
+            raise InvalidArg("num_tokens must be >= 0")
+        if seq in self.tables:
+            raise DuplicateSeq(seq)
+        need = -(-num_tokens // self.block_size)
+        if need > len(self.free):
+            raise OutOfBlocks(f"need {need} blocks, {len(self.free)} free")
+        self.tables[seq] = [self._pop() for _ in range(need)]
+        self.lens[seq] = 0
+        slots = []
+        for _ in range(num_tokens):
+            slots.append(self._slot(seq))
+            self.lens[seq] += 1
+        return slots
+
+    def fork(self, parent, child):
+        """``child`` shares every block of ``parent`` (one more reference each)."""
+        if parent not in self.tables:
+            raise UnknownSeq(parent)
+        if child in self.tables:
+            raise DuplicateSeq(child)
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        for b in self.tables[child]:
+            self.ref[b] += 1
+
+    def append(self, seqs):
+        """One new token for each sequence, in order.  Returns (slots, cow_pairs)."""
+        seqs = list(seqs)
+        for s in seqs:
+            if s not in self.tables:
+                raise UnknownSeq(s)
+        if len(set(seqs)) != len(seqs):
+            raise InvalidArg("a sequence appears twice in one append")
+        snap = self._snapshot()
+        slots, pairs = [], []
+        try:
+            for s in seqs:
+                table = self.tables[s]
+                if self.lens[s] % self.block_size == 0:
+                    table.append(self._pop())
+                elif self.ref[table[-1]] > 1:
+                    old = table[-1]
+                    new = self._pop()
+                    self.ref[old] -= 1
+                    table[-1] = new
+                    pairs.append((old, new))
+                slots.append(self._slot(s))
+                self.lens[s] += 1
+        except OutOfBlocks:
+            self._restore(snap)
+            raise
+        return slots, pairs
+
+    def free_seq(self, seq):
+        """End a sequence: drop one reference per block; blocks reaching 0 go back."""
+        if seq not in self.tables:
+            raise UnknownSeq(seq)
+        for b in self.tables[seq]:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.tables[seq]
+        del self.lens[seq]
+
+    # -- queries -----------------------------------------------------------------------
+    def block_tables(self, seqs, max_blocks: int):
+        """Row-per-sequence tables padded with -1, and the sequence lengths."""
+        rows, lens = [], []
+        for s in seqs:
+            if s not in self.tables:
+                raise UnknownSeq(s)
+            t = self.tables[s]
+            if len(t) > max_blocks:
+                raise InvalidArg(f"sequence {s} has {len(t)} blocks > {max_blocks}")
+            rows.append(t + [-1] * (max_blocks - len(t)))
+            lens.append(self.lens[s])
+        return rows, lens
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def refcount(self, block: int) -> int:
+        if not 0 <= block < self.num_blocks:
+            return -1
+        return self.ref[block]
+
+    def usage(self):
+        """(tokens stored, slots in allocated blocks); a shared block counts once."""
+        tokens = sum(self.lens.values())
+        used = sum(1 for r in self.ref if r > 0)
+        return tokens, used * self.block_size

@@ -1,0 +1,253 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module is shared by the CPU oracle's tests, the GPU path's tests, ``smoke()`` and
+``bench.py``.  It only draws random numbers and shapes them into arrays: it contains none of
+the method's arithmetic (no block allocation, no slot mapping, no cache write, no attention).
+Each side builds its own block tables and caches from these draws.
+
+Workload shapes follow the pages' setting: LLaMA-7B / LLaMA-13B head geometry and 16-token
+blocks ("PagedAttention 与 vLLM 推理加速", §1 and §2.2; "vLLM + PagedAttention：打造高并发LLM
+推理引擎", the block-size example under "它是怎么工作的？"), mixed context lengths from
+continuous batching, grouped-query long contexts and a shared system-prompt prefix
+("PagedAttention 与 vLLM 推理加速", §3.2 (3)).
+
+Random streams: ``SeedSequence(1000 + cfg_id).spawn(5)`` gives, in order, the streams for
+(context lengths, physical placement, q, k, v).  Lengths and placement use NumPy's PCG64;
+q/k/v are drawn N(0, 1) in float32 by a seeded ``torch.Generator`` on the target device and
+rounded to the KV dtype by torch's round-to-nearest-even cast.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+DTYPE_SIZE = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    """One decode workload.
+
+    ``lengths`` describes the context length each sequence attends to at its first decode
+    step (the cached tokens plus the token appended in that step):
+      ("fixed", (l0, l1, ...)) | ("uniform", lo, hi) inclusive |
+      ("lognormal", median, sigma, lo, hi) rounded and clipped |
+      ("prefix_uniform", lo, hi): a shared prefix of ``prefix_len`` tokens plus a per-sequence
+      suffix drawn uniformly in [lo, hi].
+    """
+
+    name: str
+    cfg_id: int
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    batch: int
+    lengths: tuple
+    prefix_len: int = 0
+    partition_size: int = 512
+    steps: int = 1
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+    @property
+    def dsize(self) -> int:
+        return DTYPE_SIZE[self.dtype]
+
+
+def _cfg5(bs: int, cow: bool) -> DecodeConfig:
+    # A 1024-token prefix ends on a block boundary for every swept block size; the
+    # copy-on-write variant shortens it by half a block so that the last shared block is
+    # partially filled and the first append of each sharer has to copy it.
+    prefix = 1024 - (bs // 2 if cow else 0)
+    return DecodeConfig(
+        name=f"shared_prefix_bs{bs}" + ("_cow" if cow else ""), cfg_id=5, dtype="f16",
+        num_q_heads=32, num_kv_heads=32, head_dim=128, block_size=bs,
+        num_blocks=131072 // bs, batch=128, lengths=("prefix_uniform", 64, 512),
+        prefix_len=prefix)
+
+
+CONFIGS = {
+    # 2 heads, head_dim 8, block 4, 8 physical blocks, contexts 7 and 5, fp32.
+    "tiny": DecodeConfig("tiny", 1, "f32", 2, 2, 8, 4, 8, 2, ("fixed", (7, 5))),
+    # LLaMA-7B attention shape: 32 heads x 128, bf16 KV, contexts uniform in [128, 2048].
+    "llama7b": DecodeConfig("llama7b", 2, "bf16", 32, 32, 128, 16, 16384, 64,
+                            ("uniform", 128, 2048)),
+    # LLaMA-13B attention shape: 40 heads x 128, fp16 KV, continuous-batching length mix.
+    "llama13b": DecodeConfig("llama13b", 3, "f16", 40, 40, 128, 16, 16384, 256,
+                             ("lognormal", 512, 1.0, 16, 4096), steps=64),
+    # Grouped-query long context: 64 query heads over 8 KV heads, 32k tokens, split-K.
+    "gqa_long": DecodeConfig("gqa_long", 4, "bf16", 64, 8, 128, 16, 33792, 16,
+                             ("fixed", (32768,) * 16)),
+}
+for _bs in (8, 16, 32):
+    for _cow in (False, True):
+        _c = _cfg5(_bs, _cow)
+        CONFIGS[_c.name] = _c
+
+
+def get_config(name: str, **overrides) -> DecodeConfig:
+    cfg = CONFIGS[name]
+    return dataclasses.replace(cfg, **overrides) if overrides else cfg
+
+
+def seed_streams(cfg_id: int):
+    """(lengths, placement, q, k, v) seed sequences for one configuration id."""
+    return np.random.SeedSequence(1000 + cfg_id).spawn(5)
+
+
+def _torch_seed(ss: np.random.SeedSequence) -> int:
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def draw_lengths(cfg: DecodeConfig) -> np.ndarray:
+    """Context length attended by each sequence at its first decode step (int64, [batch])."""
+    rng = np.random.Generator(np.random.PCG64(seed_streams(cfg.cfg_id)[0]))
+    kind = cfg.lengths[0]
+    if kind == "fixed":
+        vals = np.asarray(cfg.lengths[1], dtype=np.int64)
+        full = np.resize(vals, max(cfg.batch, len(vals)))
+    elif kind == "uniform":
+        lo, hi = cfg.lengths[1], cfg.lengths[2]
+        full = rng.integers(lo, hi, size=max(cfg.batch, 1024), endpoint=True)
+    elif kind == "lognormal":
+        median, sigma, lo, hi = cfg.lengths[1:]
+        z = rng.standard_normal(max(cfg.batch, 1024))
+        full = np.clip(np.rint(np.exp(np.log(median) + sigma * z)), lo, hi)
+    elif kind == "prefix_uniform":
+        lo, hi = cfg.lengths[1], cfg.lengths[2]
+        full = cfg.prefix_len + rng.integers(lo, hi, size=max(cfg.batch, 1024), endpoint=True)
+    else:
+        raise ValueError(kind)
+    # Drawing a fixed-size stream and slicing keeps a reduced batch a prefix of the full one.
+    return np.asarray(full[: cfg.batch], dtype=np.int64)
+
+
+def draw_free_order(cfg: DecodeConfig) -> np.ndarray:
+    """Seeded random permutation of the physical blocks: the order the pool hands them out."""
+    rng = np.random.Generator(np.random.PCG64(seed_streams(cfg.cfg_id)[1]))
+    return rng.permutation(cfg.num_blocks).astype(np.int32)
+
+
+_CHUNK = 1 << 22  # elements per draw; fixed so results do not depend on the total size
+
+
+def draw_normal(shape, seed_seq, dtype: torch.dtype, device) -> torch.Tensor:
+    """N(0, 1) float32 draws rounded (RNE) to ``dtype``, drawn in fixed-size chunks."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    gen = torch.Generator(device=device)
+    gen.manual_seed(_torch_seed(seed_seq))
+    out = torch.empty(n, dtype=dtype, device=device)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        out[s:e] = torch.randn(e - s, generator=gen, dtype=torch.float32, device=device).to(dtype)
+    return out.view(*shape)
+
+
+@dataclasses.dataclass
+class Workload:
+    """Everything one side needs to build its caches and run ``cfg.steps`` decode steps.
+
+    Token streams are in logical order.  Sequence ``b`` owns tokens
+    ``tok_offsets[b]:tok_offsets[b+1]`` of ``k_tok``/``v_tok``; with a shared prefix those come
+    after the ``prefix_len`` tokens of ``k_prefix``/``v_prefix``.  At decode step ``s`` sequence
+    ``b`` appends its token number ``lengths[b] - 1 + s`` (counting the prefix) and attends to
+    ``lengths[b] + s`` tokens with query ``q[s, b]``.
+    """
+
+    cfg: DecodeConfig
+    lengths: np.ndarray
+    free_order: np.ndarray
+    q: torch.Tensor
+    k_tok: torch.Tensor
+    v_tok: torch.Tensor
+    tok_offsets: np.ndarray
+    k_prefix: Optional[torch.Tensor]
+    v_prefix: Optional[torch.Tensor]
+
+    @property
+    def batch(self) -> int:
+        return int(self.lengths.shape[0])
+
+    def token_kv(self, b: int, lo: int, hi: int):
+        """K and V of tokens [lo, hi) of sequence b (prefix included), contiguous."""
+        p = self.cfg.prefix_len
+        ks, vs = [], []
+        if lo < p:
+            ks.append(self.k_prefix[lo:min(hi, p)])
+            vs.append(self.v_prefix[lo:min(hi, p)])
+        if hi > p:
+            o = int(self.tok_offsets[b])
+            a, z = max(lo, p) - p, hi - p
+            ks.append(self.k_tok[o + a:o + z])
+            vs.append(self.v_tok[o + a:o + z])
+        if len(ks) == 1:
+            return ks[0], vs[0]
+        return torch.cat(ks), torch.cat(vs)
+
+
+def make_workload(cfg: DecodeConfig, device="cpu") -> Workload:
+    lengths = draw_lengths(cfg)
+    free_order = draw_free_order(cfg)
+    ss = seed_streams(cfg.cfg_id)
+    dt = cfg.torch_dtype
+    hkv, d = cfg.num_kv_heads, cfg.head_dim
+    own = lengths - cfg.prefix_len + (cfg.steps - 1)
+    offs = np.zeros(cfg.batch + 1, dtype=np.int64)
+    offs[1:] = np.cumsum(own)
+    total = int(offs[-1])
+    kall = draw_normal((cfg.prefix_len + total, hkv, d), ss[3], dt, device)
+    vall = draw_normal((cfg.prefix_len + total, hkv, d), ss[4], dt, device)
+    q = draw_normal((cfg.steps, cfg.batch, cfg.num_q_heads, d), ss[2], dt, device)
+    p = cfg.prefix_len
+    return Workload(cfg, lengths, free_order, q, kall[p:], vall[p:], offs,
+                    kall[:p] if p else None, vall[:p] if p else None)
+
+
+# ---------------------------------------------------------------------------------------
+# Request schedule.  What the requests do, in order, to reach their first decode step and
+# then to decode: a list of request-level operations that each side replays with its own
+# allocator and cache.  Tokens written by an operation are the sequence's next tokens in
+# logical order.  ("add", seq, n): a new sequence with n tokens; ("fork", parent, child);
+# ("free", seq); ("append", [seq, ...]): one new token for each listed sequence.
+# ---------------------------------------------------------------------------------------
+PARENT = -1  # id of the sequence that holds a shared prefix before it is forked
+
+
+def setup_ops(w: Workload):
+    cfg, nb = w.cfg, w.batch
+    ops = []
+    if cfg.prefix_len:
+        ops.append(("add", PARENT, cfg.prefix_len))
+        for b in range(nb):
+            ops.append(("fork", PARENT, b))
+        ops.append(("free", PARENT))
+        own = w.lengths - cfg.prefix_len - 1
+        for r in range(int(own.max()) if nb else 0):
+            ops.append(("append", [b for b in range(nb) if own[b] > r]))
+    else:
+        for b in range(nb):
+            ops.append(("add", b, int(w.lengths[b]) - 1))
+    return ops
+
+
+def step_ops(w: Workload):
+    """One decode step: every sequence appends the token it decodes."""
+    return [("append", list(range(w.batch)))]
