@@ -1,0 +1,259 @@
+"""Paged decode attention benchmark on one MI355X.
+
+One step = one pass of the whole paged decode path over the batch:
+  host: every sequence appends one token (C++ allocator: slot, new block or copy-on-write)
+  H2D:  slot mapping, block tables and context lengths (pinned, asynchronous)
+  GPU:  copy-on-write block copies (when any), reshape_and_cache of the new K/V, paged
+        decode attention, partition merge.
+Inputs (queries, the new tokens' K/V, the existing cache) are resident in HBM before timing.
+
+Prints one JSON line.  ``value`` is the whole step's logical KV throughput (bytes of K and V
+that the batch attends to, per second); ``roofline`` rates the decode kernels alone, timed
+with HIP events on the stream they run on; ``cpu_baseline`` times the fp64 CPU oracle on a
+bounded sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="llama13b")
+    ap.add_argument("--partition", type=int, default=-1, help="-1 auto, 0 no split, >0 tokens")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (scales HBM counters)")
+    return ap.parse_args()
+
+
+def workload_desc(cfg, lengths):
+    lk = cfg.lengths
+    return {
+        "workload": f"paged decode, {cfg.name}: B={cfg.batch}, Hq={cfg.num_q_heads}, "
+                    f"Hkv={cfg.num_kv_heads}, D={cfg.head_dim}, block={cfg.block_size}, "
+                    f"{cfg.dtype} KV, lengths {lk[0]}{tuple(lk[1:])}, +1 token per step",
+        "batch": cfg.batch, "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+        "head_dim": cfg.head_dim, "block_size": cfg.block_size, "num_blocks": cfg.num_blocks,
+        "kv_dtype": cfg.dtype, "mean_context": float(np.mean(lengths)),
+        "max_context": int(np.max(lengths)), "prefix_len": cfg.prefix_len,
+    }
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle, untouched, on the first sequences of the batch at the first step."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    c = w.cfg
+    # Choose the sample: whole sequences from the start of the batch until their estimated
+    # cost reaches the budget (estimated from a one-sequence probe).
+    q_bits = oracle.bits_of(w.q[0].cpu(), c.dtype)
+
+    def build(nseq):
+        nb = sum(-(-int(w.lengths[b]) // c.block_size) for b in range(nseq)) + 1
+        a = oracle.OracleAllocator(nb, c.block_size)
+        kp = oracle.new_pool(nb, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
+        vp = oracle.new_pool(nb, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
+        for b in range(nseq):
+            n = int(w.lengths[b])
+            slots = a.add(b, n)
+            k, v = w.token_kv(b, 0, n)
+            oracle.cache_write(kp, oracle.bits_of(k.cpu(), c.dtype), slots)
+            oracle.cache_write(vp, oracle.bits_of(v.cpu(), c.dtype), slots)
+        mb = max(len(a.tables[b]) for b in range(nseq))
+        tables, lens = a.block_tables(range(nseq), mb)
+        return kp, vp, tables, lens
+
+    kp, vp, tables, lens = build(1)
+    t = time.perf_counter()
+    oracle.decode(q_bits[:1], kp, vp, tables, lens, c.scale, c.dtype)
+    per_token = (time.perf_counter() - t) / max(int(w.lengths[0]), 1)
+    nseq, acc = 0, 0.0
+    while nseq < w.batch and acc < budget_s:
+        acc += per_token * int(w.lengths[nseq])
+        nseq += 1
+    kp, vp, tables, lens = build(nseq)
+    t = time.perf_counter()
+    oracle.decode(q_bits[:nseq], kp, vp, tables, lens, c.scale, c.dtype)
+    dt = time.perf_counter() - t
+    tokens = int(np.sum(w.lengths[:nseq]))
+    kv_bytes = 2 * c.num_kv_heads * c.head_dim * c.dsize * tokens
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(kv_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "tokens_per_s": round(nseq / dt, 3),
+            "sample": f"fp64 oracle decode (gather + two-pass softmax) of the first {nseq} of "
+                      f"{w.batch} sequences at the first step ({tokens} context tokens, "
+                      f"{c.num_q_heads} heads), one run"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the paged decode path here runs on a single GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import paged_kv_cache_359_amd as pkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    total_steps = args.warmup + args.steps
+    cfg = W.get_config(args.config, steps=total_steps)
+    print(f"[bench] building {cfg.name}: {cfg.batch} sequences, {total_steps} steps", file=sys.stderr, flush=True)
+    w = W.make_workload(cfg, device=dev)
+    c = cfg
+    B, bs = w.batch, c.block_size
+
+    # ---- resident state: allocator + pools holding every sequence's existing context ----
+    alloc = pkv.PkvAlloc(c.num_blocks, bs, w.free_order)
+    shape = (c.num_blocks, c.num_kv_heads, bs, c.head_dim)
+    k_cache = torch.zeros(shape, dtype=c.torch_dtype, device=dev)
+    v_cache = torch.zeros(shape, dtype=c.torch_dtype, device=dev)
+    lens_host = {}
+    for op in W.setup_ops(w):
+        if op[0] == "add":
+            _, s, n = op
+            slots = alloc.pkv_seq_add(s, n)
+            lens_host[s] = n
+            if n:
+                k, v = w.token_kv(0 if s == W.PARENT else s, 0, n)
+                pkv.pkv_reshape_and_cache(k.contiguous(), v.contiguous(),
+                                          torch.from_numpy(slots).to(dev), k_cache, v_cache)
+        elif op[0] == "fork":
+            alloc.pkv_seq_fork(op[1], op[2])
+            lens_host[op[2]] = lens_host[op[1]]
+        elif op[0] == "free":
+            alloc.pkv_seq_free(op[1])
+            del lens_host[op[1]]
+        else:
+            seqs = op[1]
+            pos = np.array([lens_host[s] for s in seqs])
+            slots, pairs = alloc.pkv_seq_append(seqs)
+            if pairs.size:
+                pkv.pkv_copy_blocks(k_cache, v_cache, torch.from_numpy(pairs).to(dev))
+            idx = torch.from_numpy(w.tok_offsets[np.asarray(seqs)] + pos - c.prefix_len).to(dev)
+            pkv.pkv_reshape_and_cache(w.k_tok.index_select(0, idx), w.v_tok.index_select(0, idx),
+                                      torch.from_numpy(slots).to(dev), k_cache, v_cache)
+            for s in seqs:
+                lens_host[s] += 1
+
+    # ---- per-step inputs, resident in HBM: the appended token's K/V and the query ----
+    base = w.tok_offsets[:B] + (w.lengths - 1 - c.prefix_len)
+    step_idx = torch.from_numpy(base[None, :] + np.arange(total_steps)[:, None]).to(dev)
+    k_new = w.k_tok.index_select(0, step_idx.reshape(-1)).view(total_steps, B, c.num_kv_heads, c.head_dim)
+    v_new = w.v_tok.index_select(0, step_idx.reshape(-1)).view(total_steps, B, c.num_kv_heads, c.head_dim)
+    q = w.q
+    max_len_final = int(w.lengths.max()) + total_steps - 1
+    max_blocks = -(-max_len_final // bs)
+    ws_bytes = pkv.pkv_decode_workspace_bytes(B, c.num_q_heads, c.head_dim, max_len_final, args.partition)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, c.num_q_heads, c.head_dim), dtype=c.torch_dtype, device=dev)
+    ids = np.arange(B, dtype=np.int64)
+    # Double-buffered pinned staging for what the host produces each step.
+    stage = [dict(slots=torch.empty(B, dtype=torch.int64, pin_memory=True),
+                  pairs=torch.empty(2 * B, dtype=torch.int32, pin_memory=True),
+                  tables=torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True),
+                  lens=torch.empty(B, dtype=torch.int32, pin_memory=True),
+                  done=torch.cuda.Event()) for _ in range(2)]
+    for st in stage:
+        st["done"].record()
+    slots_d = torch.empty(B, dtype=torch.int64, device=dev)
+    pairs_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    tables_d = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
+    lens_d = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(total_steps)]
+    kv_per_token = 2 * c.num_kv_heads * c.head_dim * c.dsize
+    step_bytes = [kv_per_token * int(np.sum(w.lengths + s)) for s in range(total_steps)]
+
+    def step(s):
+        st = stage[s % 2]
+        st["done"].synchronize()  # the copies that last read this staging set are finished
+        sl, pr = st["slots"].numpy(), st["pairs"].numpy()
+        ncow = alloc.pkv_seq_append_into(ids, sl, pr)                         # a1
+        alloc.pkv_get_block_tables(ids, max_blocks, st["tables"].numpy(), st["lens"].numpy())
+        slots_d.copy_(st["slots"], non_blocking=True)                         # a2
+        tables_d.copy_(st["tables"], non_blocking=True)
+        lens_d.copy_(st["lens"], non_blocking=True)
+        if ncow:                                                              # a3
+            pairs_d.view(-1)[: 2 * ncow].copy_(st["pairs"][: 2 * ncow], non_blocking=True)
+        st["done"].record(stream)
+        if ncow:
+            pkv.pkv_copy_blocks(k_cache, v_cache, pairs_d[:ncow])
+        pkv.pkv_reshape_and_cache(k_new[s], v_new[s], slots_d, k_cache, v_cache)  # a4
+        ev[s][0].record(stream)
+        pkv.pkv_paged_attention_decode(out, q[s], k_cache, v_cache, tables_d, lens_d,  # a5, a6
+                                       max_len_final, c.scale, args.partition, workspace)
+        ev[s][1].record(stream)
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total_steps):
+        step(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+
+    K = args.steps
+    ms_per_step = (t1 - t0) * 1e3 / K
+    timed = range(args.warmup, total_steps)
+    kern_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in timed]
+    kern_avg_ms = float(np.mean(kern_ms))
+    bytes_avg = float(np.mean([step_bytes[s] for s in timed]))
+    achieved = bytes_avg / (kern_avg_ms * 1e-3) / 1e9
+    value = bytes_avg / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = B / (ms_per_step * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    res = {
+        "metric": "paged decode attention KV GB/s (% HBM peak) + tokens/s, LLaMA-13B shape, 1 GPU",
+        "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
+        "config": workload_desc(c, w.lengths),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 3),
+        "tokens_per_s": round(tokens_per_s, 1),
+        "decode_kernel_ms": round(kern_avg_ms, 5),
+        "decode_kernel_tokens_per_s": round(B / (kern_avg_ms * 1e-3), 1),
+        "partition_size": args.partition,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "paged_attention_decode (decode + partition merge)",
+                     "bytes_per_launch": round(bytes_avg)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * pkv — paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * The C ABI of the library libpkv.so.  Plain pointers and sizes only; no C++ or framework
+ * types cross it.  Two groups of calls:
+ *
+ *  - a host block allocator (pkv_alloc_*, pkv_seq_*): the KV Cache Manager of a paged
+ *    inference engine.  It owns the free pool of physical blocks, one block table per
+ *    sequence, reference counts for shared blocks, and copy-on-write on append.
+ *  - device operations (pkv_reshape_and_cache, pkv_copy_blocks,
+ *    pkv_paged_attention_decode): HIP kernels, enqueued asynchronously on the caller's
+ *    stream; the library never synchronises inside a call.
+ *
+ * Passages followed (page title, section):
+ *  - "vLLM + PagedAttention：打造高并发LLM推理引擎", the numbered steps under
+ *    "它是怎么工作的？": blocks are allocated on demand, each request keeps a page table from
+ *    token position to block, the attention kernel gathers K/V through that table, and a
+ *    finished request's blocks go back to the pool.
+ *  - "PagedAttention 与 vLLM 推理加速", §2.2–§2.4 (fixed-size blocks, block table, only the
+ *    last block partly empty) and §3.2 (3) (shared prefix blocks, copy-on-write).
+ *  - "LLM Systems 24: Efficient LLM Inference with PagedAttention and vLLM", §2.1.3 (the KV
+ *    Cache Manager allocates and frees physical blocks and maps logical to physical blocks)
+ *    and §3 Conclusion (reference counts with copy-on-write; running out of blocks leads
+ *    the caller to preempt).
+ *
+ * Layouts (the pages fix only a block's element count; these are this library's choices):
+ *  - K pool and V pool: [num_blocks][num_kv_heads][block_size][head_dim], dense row-major,
+ *    one pool each, element type given by pkv_dtype.  Token t of a sequence lives in
+ *    physical block table[t / block_size] at offset t % block_size.
+ *  - slot: block * block_size + offset, int64; -1 means "skip this token".
+ *  - block_tables: [num_seqs][max_blocks_per_seq] int32, row-major; entries past a
+ *    sequence's last block are -1 and never read.
+ *  - q, out: [num_seqs][num_q_heads][head_dim] in the cache's element type.
+ *  - Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * Errors: every call returns a pkv_status.  Nothing aborts or throws across the ABI.  A
+ * failed allocator call leaves the allocator unchanged.  A device call that fails host-side
+ * validation enqueues nothing; PKV_ERR_HIP reports a launch error seen after enqueueing.
+ *
+ * Threading: an allocator handle must not be used by two threads at once.  Device calls
+ * hold no global state and may run concurrently on different streams.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned pointer, bad permutation */
+  PKV_ERR_OUT_OF_BLOCKS = 2, /* not enough free blocks; nothing was changed */
+  PKV_ERR_UNKNOWN_SEQ = 3,   /* a sequence id that the allocator does not hold */
+  PKV_ERR_DUPLICATE_SEQ = 4, /* a sequence id that already exists */
+  PKV_ERR_UNSUPPORTED = 5,   /* a shape or dtype with no kernel instance */
+  PKV_ERR_WORKSPACE = 6,     /* workspace missing or smaller than pkv_decode_workspace_bytes */
+  PKV_ERR_HIP = 7            /* the HIP runtime reported an error */
+};
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/* Opaque host-side allocator.  Created and destroyed by the caller. */
+typedef struct pkv_alloc pkv_alloc;
+
+/* Human-readable name of a status code (static string). */
+const char* pkv_status_str(pkv_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t pkv_version(void);
+
+/* ======================================================================================
+ * Host block allocator
+ * ====================================================================================== */
+
+/* Create an allocator over num_blocks physical blocks of block_size token slots.
+ * free_order (nullable, host, num_blocks entries): a permutation of 0..num_blocks-1 giving
+ * the order in which blocks are first handed out (NULL = 0, 1, 2, ...).  The pool is a
+ * stack: blocks freed later are handed out before untouched ones, the most recently freed
+ * first.  *out receives the handle.  INVALID_ARG on non-positive sizes, a null out, or a
+ * free_order that is not a permutation. */
+pkv_status pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                            pkv_alloc** out);
+
+/* Destroy an allocator (NULL is ignored). */
+void pkv_alloc_destroy(pkv_alloc* a);
+
+/* Add sequence seq_id holding num_tokens (>= 0) tokens: takes ceil(num_tokens/block_size)
+ * blocks, in logical order, and writes the tokens' slots to slots_out (host, num_tokens
+ * entries; may be NULL only when num_tokens == 0).
+ * DUPLICATE_SEQ if seq_id exists; OUT_OF_BLOCKS if the pool is short. */
+pkv_status pkv_seq_add(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t* slots_out);
+
+/* Create child_id sharing every block of parent_id (each block gains one reference).
+ * UNKNOWN_SEQ if the parent is missing; DUPLICATE_SEQ if the child exists. */
+pkv_status pkv_seq_fork(pkv_alloc* a, int64_t parent_id, int64_t child_id);
+
+/* Append one token to each of the n sequences seq_ids (host), in order; the ids must be
+ * distinct (else INVALID_ARG).  For each sequence: a length that is a multiple of
+ * block_size takes a fresh block; otherwise a last block shared with another sequence is
+ * replaced by a fresh block and the pair (old, new) is reported for the caller to copy
+ * (copy-on-write) before writing; an unshared last block is written in place.
+ * slots_out (host, n int64): the slot of each appended token.
+ * cow_pairs_out (host, 2n int32): (src, dst) block pairs, *n_cow_out of them.
+ * All-or-nothing: OUT_OF_BLOCKS leaves everything unchanged. */
+pkv_status pkv_seq_append(pkv_alloc* a, const int64_t* seq_ids, int32_t n, int64_t* slots_out,
+                          int32_t* cow_pairs_out, int32_t* n_cow_out);
+
+/* End a sequence: each of its blocks loses a reference; blocks with none left return to
+ * the pool in logical order (so its last block is the next one handed out). */
+pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id);
+
+/* Copy the block tables of n sequences into tables_out (host, n * max_blocks int32,
+ * row-major, padded with -1) and their lengths into lens_out (host, n int32; nullable).
+ * INVALID_ARG if a sequence holds more than max_blocks blocks. */
+pkv_status pkv_get_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
+                                int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
+
+/* Length (tokens) of one sequence. */
+pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out);
+
+/* Number of free blocks (-1 for a null handle). */
+int32_t pkv_num_free_blocks(const pkv_alloc* a);
+
+/* Reference count of a physical block (-1 if out of range or a null handle). */
+int32_t pkv_block_refcount(const pkv_alloc* a, int32_t block);
+
+/* tokens_stored: sum of all sequence lengths (a shared token counts once per sequence);
+ * slots_allocated: block_size times the number of blocks referenced at least once. */
+pkv_status pkv_usage(const pkv_alloc* a, int64_t* tokens_stored, int64_t* slots_allocated);
+
+/* ======================================================================================
+ * Device operations (all pointers are device pointers unless stated; stream is a
+ * hipStream_t, NULL = the null stream).  Pointers must be 16-byte aligned.
+ * ====================================================================================== */
+
+/* Cache write ("vLLM + PagedAttention", step 1–2 under "它是怎么工作的？": new tokens go
+ * into the blocks their table assigns).  For each token t < num_tokens with
+ * s = slot_mapping[t] >= 0: K[s / block_size][h][s % block_size][:] = key[t][h][:] for
+ * every KV head h, and the same for V.  key, value: [num_tokens][num_kv_heads][head_dim]
+ * contiguous.  Exact bit copy.  Slots must be distinct and < num_blocks * block_size;
+ * slots outside [0, num_blocks*block_size) are skipped.  num_tokens == 0 is a no-op. */
+pkv_status pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slot_mapping,
+                                 void* k_cache, void* v_cache, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, pkv_dtype dtype, void* stream);
+
+/* Copy-on-write block copies ("PagedAttention 与 vLLM 推理加速", §3.2 (3)): for each of the
+ * n_pairs pairs (src, dst) in pairs ([n_pairs][2] int32, device), copy the whole block src
+ * (every head, every slot) to block dst, in both pools.  Destinations must be distinct and
+ * must not be sources.  Pairs with an id outside [0, num_blocks) are skipped. */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, pkv_dtype dtype, void* stream);
+
+/* Bytes of workspace pkv_paged_attention_decode needs for this shape.  partition_size as
+ * for the decode call (-1 = the automatic choice).  0 when no split is needed. */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/* Paged decode attention ("vLLM + PagedAttention", step 3 under "它是怎么工作的？";
+ * "PagedAttention 与 vLLM 推理加速", §2.3).  For each sequence b and query head h, with
+ * g = h / (num_q_heads / num_kv_heads) and n = context_lens[b]:
+ *     out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) V_t,   t = 0 .. n-1,
+ * where K_t, V_t are read from block block_tables[b][t / block_size] at offset
+ * t % block_size, KV head g.  n == 0 gives zeros.  Accumulation in fp32; out is rounded
+ * to the cache's element type (round to nearest even).
+ *
+ * partition_size: 0 = one pass per (sequence, head); > 0 = split each context into
+ * partitions of that many tokens (a multiple of 16 and of block_size), each reduced to
+ * (max, sum, partial output) in the workspace and merged by a second kernel; -1 = automatic
+ * (512-token partitions).  The result does not depend on physical block placement.
+ * max_context_len: an upper bound of context_lens (sizes the grid; larger lengths are
+ * clamped to it and to max_blocks_per_seq * block_size).  Table entries outside
+ * [0, num_blocks) are treated as empty blocks and never dereferenced.
+ * workspace / workspace_bytes: device scratch of at least pkv_decode_workspace_bytes(...)
+ * bytes (may be NULL when that is 0).
+ * Supported: dtype f32, f16, bf16; head_dim 8, 64, 128; block_size 4, 8, 16, 32;
+ * num_q_heads a multiple of num_kv_heads.  Grouped-query attention with 16-bit elements,
+ * head_dim 64 or 128 and block_size >= 8 runs on matrix cores (MFMA). */
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, pkv_dtype dtype, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

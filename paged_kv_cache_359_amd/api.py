@@ -1,0 +1,227 @@
+"""Python binding of libpkv.so: argument marshalling only.
+
+Every function here calls the C entry point of the same name (include/pkv.h); all work
+happens in the library.  PyTorch supplies device memory and the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+
+PKV_OK = 0
+STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_OUT_OF_BLOCKS",
+                3: "PKV_ERR_UNKNOWN_SEQ", 4: "PKV_ERR_DUPLICATE_SEQ", 5: "PKV_ERR_UNSUPPORTED",
+                6: "PKV_ERR_WORKSPACE", 7: "PKV_ERR_HIP"}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = int(status)
+        self.name = STATUS_NAMES.get(self.status, str(status))
+        super().__init__(f"{call}: {self.name}")
+
+
+def _check(status: int, call: str):
+    if status != PKV_OK:
+        raise PkvError(status, call)
+
+
+def _ptr(arr: np.ndarray, ctype):
+    return arr.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def pkv_status_str(status: int) -> str:
+    return _lib.load().pkv_status_str(int(status)).decode()
+
+
+def pkv_version() -> int:
+    return int(_lib.load().pkv_version())
+
+
+# ---------------------------------------------------------------------------------------
+# Host block allocator
+# ---------------------------------------------------------------------------------------
+class PkvAlloc:
+    """Owns one ``pkv_alloc`` handle; methods map to the ``pkv_seq_*`` / ``pkv_*`` calls."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self._lib = _lib.load()
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        h = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(free_order, dtype=np.int32)
+            if order.shape != (self.num_blocks,):
+                raise ValueError("free_order must have num_blocks entries")
+        _check(self._lib.pkv_alloc_create(self.num_blocks, self.block_size,
+                                          None if order is None else _ptr(order, ctypes.c_int32),
+                                          ctypes.byref(h)), "pkv_alloc_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pkv_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def pkv_seq_add(self, seq_id: int, num_tokens: int) -> np.ndarray:
+        slots = np.empty(max(int(num_tokens), 0), dtype=np.int64)
+        _check(self._lib.pkv_seq_add(self._h, int(seq_id), int(num_tokens),
+                                     _ptr(slots, ctypes.c_int64) if slots.size else None),
+               "pkv_seq_add")
+        return slots
+
+    def pkv_seq_fork(self, parent_id: int, child_id: int):
+        _check(self._lib.pkv_seq_fork(self._h, int(parent_id), int(child_id)), "pkv_seq_fork")
+
+    def pkv_seq_append(self, seq_ids):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64).reshape(-1)
+        n = ids.size
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        pairs = np.empty(max(2 * n, 2), dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(self._lib.pkv_seq_append(self._h, _ptr(ids, ctypes.c_int64) if n else None, n,
+                                        _ptr(slots, ctypes.c_int64), _ptr(pairs, ctypes.c_int32),
+                                        ctypes.byref(ncow)), "pkv_seq_append")
+        return slots[:n], pairs[: 2 * ncow.value].reshape(-1, 2)
+
+    def pkv_seq_append_into(self, ids: np.ndarray, slots: np.ndarray, pairs: np.ndarray) -> int:
+        """Allocation-free variant for hot loops: caller-provided int64 ids/slots and int32
+        pairs buffers (2 * n entries).  Returns the number of copy-on-write pairs."""
+        ncow = ctypes.c_int32(0)
+        _check(self._lib.pkv_seq_append(self._h, _ptr(ids, ctypes.c_int64), ids.size,
+                                        _ptr(slots, ctypes.c_int64), _ptr(pairs, ctypes.c_int32),
+                                        ctypes.byref(ncow)), "pkv_seq_append")
+        return ncow.value
+
+    def pkv_seq_free(self, seq_id: int):
+        _check(self._lib.pkv_seq_free(self._h, int(seq_id)), "pkv_seq_free")
+
+    def pkv_get_block_tables(self, seq_ids, max_blocks: int, tables_out=None, lens_out=None):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64).reshape(-1)
+        n = ids.size
+        tables = tables_out if tables_out is not None else np.empty((n, max_blocks), np.int32)
+        lens = lens_out if lens_out is not None else np.empty(n, np.int32)
+        _check(self._lib.pkv_get_block_tables(self._h, _ptr(ids, ctypes.c_int64) if n else None,
+                                              n, int(max_blocks),
+                                              _ptr(tables, ctypes.c_int32) if tables.size else None,
+                                              _ptr(lens, ctypes.c_int32) if n else None),
+               "pkv_get_block_tables")
+        return tables, lens
+
+    def pkv_seq_length(self, seq_id: int) -> int:
+        out = ctypes.c_int32(0)
+        _check(self._lib.pkv_seq_length(self._h, int(seq_id), ctypes.byref(out)), "pkv_seq_length")
+        return out.value
+
+    def pkv_num_free_blocks(self) -> int:
+        return int(self._lib.pkv_num_free_blocks(self._h))
+
+    def pkv_block_refcount(self, block: int) -> int:
+        return int(self._lib.pkv_block_refcount(self._h, int(block)))
+
+    def pkv_usage(self):
+        tok, slots = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check(self._lib.pkv_usage(self._h, ctypes.byref(tok), ctypes.byref(slots)), "pkv_usage")
+        return tok.value, slots.value
+
+
+# ---------------------------------------------------------------------------------------
+# Device operations (torch tensors on the GPU; launched on the current stream)
+# ---------------------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t):
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def pkv_reshape_and_cache(key, value, slot_mapping, k_cache, v_cache):
+    """key/value [T, Hkv, D]; slot_mapping [T] int64; caches [N, Hkv, bs, D]."""
+    import torch
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    n, hkv, bs, d = k_cache.shape
+    t = key.shape[0]
+    if key.shape != (t, hkv, d) or value.shape != key.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if not (key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    if slot_mapping.numel() != t:
+        raise ValueError("slot_mapping length")
+    _check(_lib.load().pkv_reshape_and_cache(
+        _dev(key) if t else None, _dev(value) if t else None, _dev(slot_mapping) if t else None,
+        _dev(k_cache), _dev(v_cache), t, hkv, d, bs, n, _dtype_code(k_cache), _stream(k_cache)),
+        "pkv_reshape_and_cache")
+
+
+def pkv_copy_blocks(k_cache, v_cache, pairs):
+    """pairs: device int32 [n, 2] of (src, dst) block ids."""
+    import torch
+    if pairs.dtype != torch.int32:
+        raise TypeError("pairs must be int32")
+    n, hkv, bs, d = k_cache.shape
+    npairs = pairs.shape[0] if pairs.numel() else 0
+    _check(_lib.load().pkv_copy_blocks(_dev(k_cache), _dev(v_cache),
+                                       _dev(pairs) if npairs else None, npairs, hkv, d, bs, n,
+                                       _dtype_code(k_cache), _stream(k_cache)), "pkv_copy_blocks")
+
+
+def pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                               partition_size=-1) -> int:
+    return int(_lib.load().pkv_decode_workspace_bytes(int(num_seqs), int(num_q_heads),
+                                                      int(head_dim), int(max_context_len),
+                                                      int(partition_size)))
+
+
+def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
+                               max_context_len: int, scale: float, partition_size: int = -1,
+                               workspace=None):
+    """out/q [B, Hq, D]; caches [N, Hkv, bs, D]; block_tables [B, max_blocks] int32;
+    context_lens [B] int32; workspace: a uint8 device tensor (or None when none is needed)."""
+    import torch
+    nb, hq, d = q.shape
+    n, hkv, bs, d2 = k_cache.shape
+    if d2 != d or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == out.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != nb or context_lens.shape != (nb,):
+        raise ValueError("table shape")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace), workspace.numel() * workspace.element_size()
+    if nb == 0:
+        return out
+    _check(_lib.load().pkv_paged_attention_decode(
+        _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
+        nb, hq, hkv, d, bs, n, block_tables.shape[1], int(max_context_len), float(scale),
+        _dtype_code(k_cache), int(partition_size), ws_ptr, ws_bytes, _stream(q)),
+        "pkv_paged_attention_decode")
+    return out

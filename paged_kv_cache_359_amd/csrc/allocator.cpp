@@ -1,0 +1,241 @@
+// Host block allocator: the KV Cache Manager side of paged attention.
+//
+// One pool of fixed-size physical blocks shared by all sequences, one block table per
+// sequence mapping logical page -> physical block, blocks handed out on demand as a
+// sequence grows and returned when it ends ("vLLM + PagedAttention：打造高并发LLM推理引擎",
+// steps 1, 2 and 4 under "它是怎么工作的？"; "PagedAttention 与 vLLM 推理加速", §2.2–§2.4;
+// "LLM Systems 24: Efficient LLM Inference with PagedAttention and vLLM", §2.1.3).
+// Blocks shared by several sequences (a common system prompt) carry a reference count and
+// are copied before a sharer writes into them ("PagedAttention 与 vLLM 推理加速", §3.2 (3);
+// "LLM Systems 24", §3 Conclusion).  Running out of blocks is reported, never partially
+// applied, so the caller can preempt a sequence and retry (same Conclusion).
+//
+// Per decode step the work is O(number of sequences appended): a length check, at most one
+// stack pop, and one slot computation each.  Plain single-threaded host code, no HIP.
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pkv.h"
+
+namespace {
+
+struct Sequence {
+  std::vector<int32_t> table;  // logical page -> physical block
+  int32_t len = 0;             // tokens stored
+};
+
+}  // namespace
+
+struct pkv_alloc {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // back() is handed out next
+  std::vector<int32_t> ref;         // references per physical block
+  std::unordered_map<int64_t, Sequence> seqs;
+
+  int32_t pop() {
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    ref[b] = 1;
+    return b;
+  }
+  int64_t slot_of(const Sequence& s) const {
+    // Token number s.len sits in logical page len / bs at offset len % bs.
+    return int64_t(s.table[s.len / block_size]) * block_size + s.len % block_size;
+  }
+};
+
+extern "C" {
+
+pkv_status pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                            pkv_alloc** out) {
+  if (!out || num_blocks <= 0 || block_size <= 0) return PKV_ERR_INVALID_ARG;
+  *out = nullptr;
+  pkv_alloc* a = new (std::nothrow) pkv_alloc();
+  if (!a) return PKV_ERR_INVALID_ARG;
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->ref.assign(num_blocks, 0);
+  a->free_stack.resize(num_blocks);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete a;
+        return PKV_ERR_INVALID_ARG;
+      }
+      seen[b] = 1;
+    }
+  }
+  // Stack top is the back, so the first pop returns free_order[0].
+  for (int32_t i = 0; i < num_blocks; ++i)
+    a->free_stack[num_blocks - 1 - i] = free_order ? free_order[i] : i;
+  *out = a;
+  return PKV_OK;
+}
+
+void pkv_alloc_destroy(pkv_alloc* a) { delete a; }
+
+pkv_status pkv_seq_add(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t* slots_out) {
+  if (!a || num_tokens < 0 || (num_tokens > 0 && !slots_out)) return PKV_ERR_INVALID_ARG;
+  if (a->seqs.count(seq_id)) return PKV_ERR_DUPLICATE_SEQ;
+  const int64_t need = (int64_t(num_tokens) + a->block_size - 1) / a->block_size;
+  if (need > int64_t(a->free_stack.size())) return PKV_ERR_OUT_OF_BLOCKS;
+  Sequence s;
+  s.table.reserve(need);
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(a->pop());
+  for (int32_t t = 0; t < num_tokens; ++t) {
+    slots_out[t] = a->slot_of(s);
+    ++s.len;
+  }
+  a->seqs.emplace(seq_id, std::move(s));
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_fork(pkv_alloc* a, int64_t parent_id, int64_t child_id) {
+  if (!a) return PKV_ERR_INVALID_ARG;
+  auto it = a->seqs.find(parent_id);
+  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+  if (a->seqs.count(child_id)) return PKV_ERR_DUPLICATE_SEQ;
+  Sequence child = it->second;  // copy table and length
+  for (int32_t b : child.table) ++a->ref[b];
+  a->seqs.emplace(child_id, std::move(child));
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_append(pkv_alloc* a, const int64_t* seq_ids, int32_t n, int64_t* slots_out,
+                          int32_t* cow_pairs_out, int32_t* n_cow_out) {
+  if (!a || n < 0 || !n_cow_out) return PKV_ERR_INVALID_ARG;
+  if (n > 0 && (!seq_ids || !slots_out || !cow_pairs_out)) return PKV_ERR_INVALID_ARG;
+  // Validate everything and count the blocks this call needs before changing anything.
+  std::vector<Sequence*> rows(n);
+  {
+    std::unordered_set<int64_t> distinct;
+    distinct.reserve(size_t(n) * 2);
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = a->seqs.find(seq_ids[i]);
+      if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+      rows[i] = &it->second;
+    }
+    for (int32_t i = 0; i < n; ++i)
+      if (!distinct.insert(seq_ids[i]).second) return PKV_ERR_INVALID_ARG;
+  }
+  int64_t need = 0;
+  std::unordered_map<int32_t, int32_t> dropped;  // simulated reference losses from CoW
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence& s = *rows[i];
+    if (s.len % a->block_size == 0) {
+      ++need;
+    } else {
+      int32_t last = s.table.back();
+      int32_t& d = dropped[last];
+      if (a->ref[last] - d > 1) {
+        ++need;
+        ++d;
+      }
+    }
+  }
+  if (need > int64_t(a->free_stack.size())) return PKV_ERR_OUT_OF_BLOCKS;
+
+  int32_t ncow = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Sequence& s = *rows[i];
+    if (s.len % a->block_size == 0) {
+      s.table.push_back(a->pop());
+    } else if (a->ref[s.table.back()] > 1) {
+      // Copy-on-write: the sharer moves to a private copy; the others keep the original.
+      int32_t old = s.table.back();
+      int32_t fresh = a->pop();
+      --a->ref[old];
+      s.table.back() = fresh;
+      cow_pairs_out[2 * ncow] = old;
+      cow_pairs_out[2 * ncow + 1] = fresh;
+      ++ncow;
+    }
+    slots_out[i] = a->slot_of(s);
+    ++s.len;
+  }
+  *n_cow_out = ncow;
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id) {
+  if (!a) return PKV_ERR_INVALID_ARG;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+  for (int32_t b : it->second.table)
+    if (--a->ref[b] == 0) a->free_stack.push_back(b);
+  a->seqs.erase(it);
+  return PKV_OK;
+}
+
+pkv_status pkv_get_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
+                                int32_t max_blocks, int32_t* tables_out, int32_t* lens_out) {
+  if (!a || n < 0 || max_blocks < 0) return PKV_ERR_INVALID_ARG;
+  if (n > 0 && (!seq_ids || (max_blocks > 0 && !tables_out))) return PKV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    if (int64_t(it->second.table.size()) > max_blocks) return PKV_ERR_INVALID_ARG;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence& s = a->seqs.find(seq_ids[i])->second;
+    int32_t* row = tables_out + int64_t(i) * max_blocks;
+    const size_t k = s.table.size();
+    if (k) std::memcpy(row, s.table.data(), k * sizeof(int32_t));
+    std::fill(row + k, row + max_blocks, -1);
+    if (lens_out) lens_out[i] = s.len;
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out) {
+  if (!a || !len_out) return PKV_ERR_INVALID_ARG;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+  *len_out = it->second.len;
+  return PKV_OK;
+}
+
+int32_t pkv_num_free_blocks(const pkv_alloc* a) {
+  return a ? int32_t(a->free_stack.size()) : -1;
+}
+
+int32_t pkv_block_refcount(const pkv_alloc* a, int32_t block) {
+  if (!a || block < 0 || block >= a->num_blocks) return -1;
+  return a->ref[block];
+}
+
+pkv_status pkv_usage(const pkv_alloc* a, int64_t* tokens_stored, int64_t* slots_allocated) {
+  if (!a || !tokens_stored || !slots_allocated) return PKV_ERR_INVALID_ARG;
+  int64_t tok = 0;
+  for (const auto& kv : a->seqs) tok += kv.second.len;
+  int64_t used = a->num_blocks - int64_t(a->free_stack.size());
+  *tokens_stored = tok;
+  *slots_allocated = used * a->block_size;
+  return PKV_OK;
+}
+
+const char* pkv_status_str(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_OUT_OF_BLOCKS: return "PKV_ERR_OUT_OF_BLOCKS";
+    case PKV_ERR_UNKNOWN_SEQ: return "PKV_ERR_UNKNOWN_SEQ";
+    case PKV_ERR_DUPLICATE_SEQ: return "PKV_ERR_DUPLICATE_SEQ";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    default: return "PKV_ERR_UNKNOWN_STATUS";
+  }
+}
+
+int32_t pkv_version(void) { return 100; }
+
+}  // extern "C"

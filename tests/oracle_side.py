@@ -10,18 +10,23 @@ import workloads as W
 class OracleState:
     """Oracle allocator plus K/V pools (raw bits) for one workload."""
 
-    def __init__(self, w: W.Workload, free_order=None, fill: int = 0):
+    def __init__(self, w: W.Workload, free_order=None, fill: int = 0, cache: bool = True):
         c = w.cfg
         self.w = w
+        self.cache = cache
         order = w.free_order if free_order is None else free_order
         self.alloc = oracle.OracleAllocator(c.num_blocks, c.block_size, order)
-        self.k_pool = oracle.new_pool(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim,
-                                      c.dtype, fill)
-        self.v_pool = oracle.new_pool(c.num_blocks, c.num_kv_heads, c.block_size, c.head_dim,
-                                      c.dtype, fill)
+        self.k_pool = self.v_pool = None
+        if cache:
+            self.k_pool = oracle.new_pool(c.num_blocks, c.num_kv_heads, c.block_size,
+                                          c.head_dim, c.dtype, fill)
+            self.v_pool = oracle.new_pool(c.num_blocks, c.num_kv_heads, c.block_size,
+                                          c.head_dim, c.dtype, fill)
         self.log = []  # (op, slots, cow_pairs) per operation, for comparisons
 
     def _write(self, seq, lo, hi, slots):
+        if not self.cache:
+            return
         b = 0 if seq == W.PARENT else seq
         k, v = self.w.token_kv(b, lo, hi)
         dt = self.w.cfg.dtype
@@ -46,8 +51,9 @@ class OracleState:
                 seqs = op[1]
                 pos = [self.alloc.lens[s] for s in seqs]
                 slots, pairs = self.alloc.append(seqs)
-                oracle.copy_blocks(self.k_pool, pairs)
-                oracle.copy_blocks(self.v_pool, pairs)
+                if self.cache:
+                    oracle.copy_blocks(self.k_pool, pairs)
+                    oracle.copy_blocks(self.v_pool, pairs)
                 for s, p, sl in zip(seqs, pos, slots):
                     self._write(s, p, p + 1, [sl])
                 self.log.append((op, slots, pairs))

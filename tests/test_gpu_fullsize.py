@@ -1,0 +1,71 @@
+"""Full-size workloads in the launch configuration the benchmark times (automatic 512-token
+partitions), checked against the oracle where it can compute outputs one by one:
+  * the allocator's whole request schedule (every slot, every copy-on-write pair, every
+    table) replayed on the oracle allocator: bit-exact;
+  * sampled cache rows read back from the pools: bit-exact against the token they hold;
+  * sampled (sequence, head) outputs against the plain fp64 definition over that sequence's
+    contiguous K/V: within 5e-3 (fp16/bf16 K/V).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_side, oracle_side
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL = {"f32": 1e-5, "f16": 5e-3, "bf16": 5e-3}
+FULL = ["llama7b", "llama13b", "gqa_long", "shared_prefix_bs8_cow", "shared_prefix_bs16_cow",
+        "shared_prefix_bs32_cow", "shared_prefix_bs16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = W.get_config(name, steps=1)
+    print(f"[case] full-size {name}", flush=True)
+    w = W.make_workload(cfg, device="cuda")
+    g = gpu_side.build(w)
+    o = oracle_side.OracleState(w, cache=False)
+    o.run(W.setup_ops(w))
+    o.run(W.step_ops(w))
+    assert len(g.log) == len(o.log)
+    for (op_g, s_g, p_g), (op_o, s_o, p_o) in zip(g.log, o.log):
+        assert op_g == op_o and s_g == list(s_o) and p_g == [list(p) for p in p_o]
+    tg, lg = g.tables()
+    to, lo = o.tables()
+    assert np.array_equal(tg, to) and np.array_equal(lg, lo)
+    assert np.array_equal(lg, w.lengths)
+
+    rng = np.random.default_rng(0)
+    bs, dt = cfg.block_size, cfg.dtype
+    # Sampled cache rows: token t of sequence b sits at slot table[t // bs] * bs + t % bs.
+    for _ in range(64):
+        b = int(rng.integers(w.batch))
+        t = int(rng.integers(int(lo[b])))
+        blk = int(to[b][t // bs])
+        k, v = w.token_kv(b, t, t + 1)
+        assert torch.equal(g.k_cache[blk, :, t % bs, :], k[0])
+        assert torch.equal(g.v_cache[blk, :, t % bs, :], v[0])
+
+    out = g.decode(partition_size=-1)
+    assert bool(torch.isfinite(out).all())
+    order = np.argsort(w.lengths)
+    picks = {(int(order[0]), 0), (int(order[-1]), cfg.num_q_heads - 1)}
+    while len(picks) < 24:
+        picks.add((int(rng.integers(w.batch)), int(rng.integers(cfg.num_q_heads))))
+    q = oracle.to_f64(oracle.bits_of(w.q[0].cpu(), dt), dt)
+    worst = 0.0
+    for b, h in sorted(picks):
+        n = int(w.lengths[b])
+        k, v = w.token_kv(b, 0, n)
+        g_ = h // cfg.group
+        kk = oracle.to_f64(oracle.bits_of(k[:, g_].cpu(), dt), dt)
+        vv = oracle.to_f64(oracle.bits_of(v[:, g_].cpu(), dt), dt)
+        ref = oracle.attention_contiguous(q[b, h], kk, vv, cfg.scale)
+        err = np.abs(out[b, h].double().cpu().numpy() - ref).max()
+        worst = max(worst, err)
+        assert err <= TOL[dt], (b, h, n, err)
+    print(f"  worst sampled max abs err {worst:.3g}", flush=True)

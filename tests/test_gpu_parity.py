@@ -1,0 +1,180 @@
+"""GPU path against the CPU oracle, element by element, on identical seeded inputs.
+
+Bars (written here, applied below):
+  * block tables, slot mapping, copy-on-write pairs and the whole K/V pools: bit-exact;
+  * attention output: max |gpu - oracle| <= 1e-5 for fp32 K/V, <= 5e-3 for fp16/bf16 K/V.
+The pools start filled with a quiet-NaN bit pattern, so an unused slot that leaked into an
+output would show up as NaN.  Sizes are chosen so the oracle finishes in seconds while still
+spanning several partitions, blocks and a ragged last block.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_side, oracle_side
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL = {"f32": 1e-5, "f16": 5e-3, "bf16": 5e-3}
+
+
+def both(name, **overrides):
+    cfg = W.get_config(name, **overrides)
+    print(f"[case] {cfg.name} {overrides}", flush=True)
+    w = W.make_workload(cfg, device="cuda")
+    g = gpu_side.build(w)
+    o = oracle_side.build(gpu_side.to_cpu(w), fill=gpu_side.SENTINEL_BITS[cfg.dtype])
+    return w, g, o
+
+
+def pool_bits(t, dtype):
+    return oracle.bits_of(t.cpu(), dtype)
+
+
+def check_structures(w, g, o):
+    assert [(op, s, [list(p) for p in pr]) for op, s, pr in g.log] == \
+        [(op, list(s), [list(p) for p in pr]) for op, s, pr in o.log]
+    tg, lg = g.tables()
+    to, lo = o.tables()
+    assert np.array_equal(tg, to) and np.array_equal(lg, lo)
+    dt = w.cfg.dtype
+    assert np.array_equal(pool_bits(g.k_cache, dt), o.k_pool)
+    assert np.array_equal(pool_bits(g.v_cache, dt), o.v_pool)
+
+
+def check_decode(w, g, o, parts):
+    ref = o.decode()
+    assert np.abs(ref).max() < 2.0  # keeps the output's own rounding well inside the bar
+    dt = w.cfg.dtype
+    for p in parts:
+        out = g.decode(partition_size=p).double().cpu().numpy()
+        assert np.all(np.isfinite(out)), p
+        err = np.abs(out - ref).max()
+        print(f"  partition {p}: max abs err {err:.3g}", flush=True)
+        assert err <= TOL[dt], (p, err)
+
+
+REDUCED = [
+    ("tiny", {}, [-1, 0, 16]),
+    ("llama7b", dict(batch=6, num_blocks=1024), [-1, 0, 256]),
+    ("llama13b", dict(batch=8, num_blocks=2048, steps=1), [-1, 0, 128]),
+    ("gqa_long", dict(batch=2, lengths=("fixed", (4100, 999)), num_blocks=400), [-1, 0, 1024]),
+    ("shared_prefix_bs8_cow", dict(batch=5, num_blocks=1024), [-1, 0, 64]),
+    ("shared_prefix_bs16_cow", dict(batch=5, num_blocks=512), [-1, 32]),
+    ("shared_prefix_bs32_cow", dict(batch=5, num_blocks=256), [-1, 0, 32]),
+    ("shared_prefix_bs16", dict(batch=4, num_blocks=512), [-1]),
+]
+
+
+@pytest.mark.parametrize("name,overrides,parts", REDUCED, ids=[r[0] for r in REDUCED])
+def test_workload_parity(name, overrides, parts):
+    w, g, o = both(name, **overrides)
+    check_structures(w, g, o)
+    check_decode(w, g, o, parts)
+
+
+# Every kernel instance family: dtypes x head_dim x block_size x group size.
+SHAPES = []
+for dtype in ("f32", "f16", "bf16"):
+    for d in (8, 64, 128):
+        for bs in (4, 8, 16, 32):
+            SHAPES.append((dtype, d, bs, 2, 2))
+for dtype in ("f16", "bf16"):
+    for d in (64, 128):
+        for bs in (4, 8, 16, 32):
+            for hq, hkv in ((8, 4), (8, 1), (16, 2), (32, 1)):
+                SHAPES.append((dtype, d, bs, hq, hkv))
+SHAPES += [("f32", 128, 16, 8, 2), ("f32", 8, 4, 4, 1)]
+
+
+@pytest.mark.parametrize("dtype,d,bs,hq,hkv", SHAPES)
+def test_shape_sweep(dtype, d, bs, hq, hkv):
+    lengths = ("fixed", (1, 2, bs - 1, bs, bs + 1, 17, 100, 257))
+    cfg = dict(dtype=dtype, head_dim=d, block_size=bs, num_q_heads=hq, num_kv_heads=hkv,
+               batch=8, lengths=lengths, num_blocks=(sum(lengths[1]) // bs + 16) * 2)
+    w, g, o = both("tiny", **cfg)
+    check_structures(w, g, o)
+    parts = [-1, 0, max(16, bs), 64 if 64 % bs == 0 else bs * 2]
+    check_decode(w, g, o, parts)
+
+
+def test_repeatable_and_partition_exactness():
+    w, g, o = both("llama13b", batch=6, num_blocks=1024, steps=1)
+    a = g.decode(partition_size=-1)
+    for _ in range(3):
+        assert torch.equal(g.decode(partition_size=-1), a)  # no atomics: bit-identical
+    # One partition covering every context takes the same path as no split at all.
+    mc = int(max(w.lengths))
+    p = ((mc + 511) // 512) * 512
+    assert torch.equal(g.decode(partition_size=0), g.decode(partition_size=p))
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("llama7b", dict(batch=5, num_blocks=700)),
+    ("gqa_long", dict(batch=2, lengths=("fixed", (3000, 777)), num_blocks=300)),
+    ("tiny", dict(batch=6, lengths=("fixed", (3, 9, 30, 1, 16, 64)), num_blocks=64)),
+])
+def test_placement_permutation_is_bit_identical(name, overrides):
+    cfg = W.get_config(name, **overrides)
+    w = W.make_workload(cfg, device="cuda")
+    outs = []
+    for seed in range(3):
+        order = np.random.default_rng(seed).permutation(cfg.num_blocks).astype(np.int32)
+        g = gpu_side.GpuState(w, free_order=order)
+        g.run(W.setup_ops(w))
+        g.run(W.step_ops(w))
+        outs.append([g.decode(partition_size=p) for p in (-1, 0, 64)])
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)
+
+
+def test_shared_blocks_equal_duplicated_blocks():
+    """Forked sharers of a prefix give bit-identical output to sequences owning copies."""
+    cfg = W.get_config("shared_prefix_bs16", batch=4, num_blocks=600)
+    w = W.make_workload(cfg, device="cuda")
+    g = gpu_side.build(w)
+    shared = g.decode(partition_size=-1)
+    # Same tokens, no sharing: write each sequence's whole context on its own.
+    d = gpu_side.GpuState(w)
+    for b in range(w.batch):
+        n = int(w.lengths[b])
+        slots = d.alloc.pkv_seq_add(b, n)
+        k, v = w.token_kv(b, 0, n)
+        d._write(k, v, slots)
+        d.lens[b] = n
+    t, l = d.tables()
+    dup = d.decode(partition_size=-1, tables=t, lens=l)
+    assert torch.equal(shared, dup)
+
+
+def test_empty_context_and_invalid_table_entries():
+    cfg = W.get_config("llama7b", batch=4, num_blocks=600, num_q_heads=8, num_kv_heads=8)
+    w, g, o = both("llama7b", batch=4, num_blocks=600, num_q_heads=8, num_kv_heads=8)
+    tables, lens = o.tables()
+    # A sequence with no context: all-zero output; the others are untouched.
+    lens0 = lens.copy()
+    lens0[1] = 0
+    out = g.decode(tables=tables, lens=lens0).double().cpu().numpy()
+    ref = oracle.decode(oracle.bits_of(w.q[0].cpu(), cfg.dtype), o.k_pool, o.v_pool, tables,
+                        lens0, cfg.scale, cfg.dtype)
+    assert np.all(out[1] == 0)
+    assert np.abs(out - ref).max() <= TOL[cfg.dtype]
+    # Out-of-range block ids count as empty blocks: equal to attention without those tokens.
+    bad = tables.copy()
+    bad[2, 1] = -7
+    bad[3, 0] = cfg.num_blocks + 5
+    bs = cfg.block_size
+    for p in (-1, 0, 64):
+        out = g.decode(tables=bad, lens=lens, partition_size=p).double().cpu().numpy()
+        q = oracle.to_f64(oracle.bits_of(w.q[0].cpu(), cfg.dtype), cfg.dtype)
+        for b, blk in ((2, 1), (3, 0)):
+            keep = [t for t in range(int(lens[b])) if t // bs != blk]
+            for h in range(cfg.num_q_heads):
+                k = oracle.to_f64(oracle.gather(o.k_pool, tables[b], int(lens[b]), h), cfg.dtype)[keep]
+                v = oracle.to_f64(oracle.gather(o.v_pool, tables[b], int(lens[b]), h), cfg.dtype)[keep]
+                r = oracle.attention_contiguous(q[b, h], k, v, cfg.scale)
+                assert np.abs(out[b, h] - r).max() <= TOL[cfg.dtype]
