@@ -70,6 +70,10 @@ typedef struct pkv_alloc pkv_alloc;
 /* Human-readable name of a status code (static string). */
 const char* pkv_status_str(pkv_status status);
 
+/* Text of the last HIP runtime error that a device call on this thread reported as
+ * PKV_ERR_HIP ("" if none).  Valid until the next failing call on the same thread. */
+const char* pkv_last_error(void);
+
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t pkv_version(void);
 

@@ -14,6 +14,7 @@ P_i64 = ctypes.POINTER(ctypes.c_int64)
 SIGNATURES = {
     "pkv_status_str": (ctypes.c_char_p, [c_i32]),
     "pkv_version": (c_i32, []),
+    "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_alloc_create": (c_i32, [c_i32, c_i32, P_i32, ctypes.POINTER(c_vp)]),
     "pkv_alloc_destroy": (None, [c_vp]),
     "pkv_seq_add": (c_i32, [c_vp, c_i64, c_i32, P_i64]),
@@ -38,9 +39,16 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load the library once.  Raises if it has not been built: there is no fallback."""
+    """Load the library once.  Raises if it has not been built: there is no fallback.
+
+    PyTorch is imported first: it maps its own HIP runtime (soname libamdhip64.so.7), and
+    the library's dependency on that soname then binds to the same runtime.  Loading the
+    library first would map a second HIP/HSA runtime from the ROCm install next to torch's,
+    and the two would neither share streams nor, in practice, both see the device.
+    """
     global _lib
     if _lib is None:
+        import torch  # noqa: F401  (see above: one HIP runtime per process)
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_359_amd.build` "

@@ -22,7 +22,10 @@ class PkvError(RuntimeError):
     def __init__(self, status: int, call: str):
         self.status = int(status)
         self.name = STATUS_NAMES.get(self.status, str(status))
-        super().__init__(f"{call}: {self.name}")
+        detail = ""
+        if self.status == 7:
+            detail = " (" + _lib.load().pkv_last_error().decode() + ")"
+        super().__init__(f"{call}: {self.name}{detail}")
 
 
 def _check(status: int, call: str):

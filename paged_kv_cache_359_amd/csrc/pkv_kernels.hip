@@ -19,6 +19,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <cstdio>
 #include <type_traits>
 
 #include "pkv.h"
@@ -692,13 +693,25 @@ bool use_mfma(pkv_dtype dt, int d, int bs, int group) {
   return dt != PKV_F32 && (d == 64 || d == 128) && bs >= 8 && group > 1;
 }
 
-pkv_status hip_status() {
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+// Text of the last HIP error a call of this thread reported (see pkv_last_error).
+thread_local char g_last_error[256] = "";
+
+// Clears an error left by earlier, unrelated runtime calls so that a launch is judged only
+// by its own outcome.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+pkv_status launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return PKV_OK;
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", what, hipGetErrorString(e));
+  return PKV_ERR_HIP;
 }
 
 }  // namespace
 
 extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error; }
 
 pkv_status pkv_reshape_and_cache(const void* key, const void* value, const int64_t* slot_mapping,
                                  void* k_cache, void* v_cache, int32_t num_tokens,
@@ -718,12 +731,13 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, const int64
   const int64_t total = int64_t(num_tokens) * heads_vecs;
   const int64_t grid = (total + 255) / 256;
   if (grid > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+  clear_stale_error();
   hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(unsigned(grid)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(key),
                      static_cast<const uint4*>(value), slot_mapping, static_cast<uint4*>(k_cache),
                      static_cast<uint4*>(v_cache), total, int32_t(heads_vecs), row_vecs, block_size,
                      int64_t(num_blocks) * block_size);
-  return hip_status();
+  return launch_status("reshape_and_cache");
 }
 
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
@@ -740,10 +754,11 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
   const int64_t blk_vecs = blk_bytes / 16;
   int64_t ychunks = (blk_vecs + 255) / 256;
   if (ychunks > 64) ychunks = 64;
+  clear_stale_error();
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(unsigned(n_pairs), unsigned(ychunks)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
                      static_cast<uint4*>(v_cache), pairs, blk_vecs, num_blocks);
-  return hip_status();
+  return launch_status("copy_blocks");
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -833,15 +848,17 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
     grid = dim3(unsigned(num_q_heads), unsigned(max_parts), unsigned(num_seqs));
   }
   if (!k) return PKV_ERR_UNSUPPORTED;
+  clear_stale_error();
   hipLaunchKernelGGL(k, grid, dim3(256), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  if (launch_status("paged_attention_decode") != PKV_OK) return PKV_ERR_HIP;
   if (max_parts > 1) {
     kernel_fn r = dtype == PKV_F32   ? pick_reduce<DT_F32>(head_dim)
                   : dtype == PKV_F16 ? pick_reduce<DT_F16>(head_dim)
                                      : pick_reduce<DT_BF16>(head_dim);
     hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(128), 0, st, a);
+    return launch_status("reduce_partitions");
   }
-  return hip_status();
+  return PKV_OK;
 }
 
 }  // extern "C"

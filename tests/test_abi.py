@@ -138,3 +138,18 @@ def test_allocator_errors():
     assert a.pkv_num_free_blocks() == 4
     assert lib().pkv_num_free_blocks(None) == -1
     assert lib().pkv_block_refcount(None, 0) == -1
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the library (in a fresh process, before anything imports torch) must not map
+    a second HIP runtime next to the one torch uses."""
+    import subprocess
+    import sys
+    code = ("import paged_kv_cache_359_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "libs = {l.split()[-1] for l in maps if 'libamdhip64' in l or 'libhsa-runtime64' in l}\n"
+            "print(len([x for x in libs if 'amdhip64' in x]), len([x for x in libs if 'hsa-runtime' in x]))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root,
+                         check=True).stdout.split()
+    assert out == ["1", "1"], out

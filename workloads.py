@@ -189,6 +189,8 @@ class Workload:
     def token_kv(self, b: int, lo: int, hi: int):
         """K and V of tokens [lo, hi) of sequence b (prefix included), contiguous."""
         p = self.cfg.prefix_len
+        if hi <= lo:
+            return self.k_tok[:0], self.v_tok[:0]
         ks, vs = [], []
         if lo < p:
             ks.append(self.k_prefix[lo:min(hi, p)])
