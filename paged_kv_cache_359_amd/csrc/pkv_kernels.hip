@@ -35,6 +35,7 @@ typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf164_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -42,6 +43,14 @@ constexpr float kNegInf = -__builtin_inff();
 template <int DT> constexpr int elt_size() { return DT == DT_F32 ? 4 : 2; }
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte load of K/V data that is read once per call: issued non-temporal, so the stream
+// does not displace reusable lines (block tables, queries) from the caches.  On MI355X this
+// takes a plain streaming read from about 5.6 to about 7 TB/s.
+__device__ __forceinline__ uint4 load_stream(const char* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // ---- element conversions ---------------------------------------------------------------
 template <int DT>
@@ -244,8 +253,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
         const bool valid = (unsigned)id < (unsigned)a.num_blocks;
         ok[j] = valid && tok < t1;
         const size_t off = size_t(valid ? id : 0) * blk_bytes + lane_off + size_t(tok % BS) * D * ES;
-        kr[j] = *reinterpret_cast<const uint4*>(kbase + off);
-        vr[j] = *reinterpret_cast<const uint4*>(vbase + off);
+        kr[j] = load_stream(kbase + off);
+        vr[j] = load_stream(vbase + off);
       }
     } else {
       need_mask = true;  // per-lane block ids: always mask (generic path)
@@ -256,8 +265,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
         const bool valid = (unsigned)id < (unsigned)a.num_blocks;
         ok[j] = valid && tok < t1;
         const size_t off = size_t(valid ? id : 0) * blk_bytes + lane_off + size_t(tok % BS) * D * ES;
-        kr[j] = *reinterpret_cast<const uint4*>(kbase + off);
-        vr[j] = *reinterpret_cast<const uint4*>(vbase + off);
+        kr[j] = load_stream(kbase + off);
+        vr[j] = load_stream(vbase + off);
       }
     }
     float s[J];
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       const bool valid = (unsigned)id < (unsigned)a.num_blocks;
       const char* p = kbase + size_t(valid ? id : 0) * blk_bytes + head_off + size_t(tok % BS) * D * 2;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kr[kk] = *reinterpret_cast<const uint4*>(p + ((4 * kk + g4) * 8) * 2);
+      for (int kk = 0; kk < KK; ++kk) kr[kk] = load_stream(p + ((4 * kk + g4) * 8) * 2);
     }
     // V: coalesced rows, token cs + j*TPL + lane/LPT.
     uint4 vr[JV];
@@ -438,7 +447,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       const bool valid = (unsigned)id < (unsigned)a.num_blocks;
       vok[j] = valid && tok < t1;
       const char* p = vbase + size_t(valid ? id : 0) * blk_bytes + head_off + size_t(tok % BS) * D * 2;
-      vr[j] = *reinterpret_cast<const uint4*>(p + (lane % LPT) * 16);
+      vr[j] = load_stream(p + (lane % LPT) * 16);
     }
     // S = K . Q^T
     float4_t s = float4_t{0.f, 0.f, 0.f, 0.f};
