@@ -15,6 +15,7 @@ bounded sample of the same batch.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +24,29 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_359_amd", "csrc", "pkv_kernels.hip")
+
+
+def counted_traffic(config_name):
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
+    of this workload (scaled by a 1 GiB copy's counts), or None when there is none or the
+    kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"paged_decode_{config_name}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return {"bytes_per_launch": int(fields["traffic_bytes_per_launch"]),
+            "over_algorithmic": float(fields["traffic_over_algorithmic"]),
+            "algorithmic_bytes_per_launch": int(fields["algorithmic_bytes_per_launch"]),
+            "source": os.path.relpath(path, ROOT)}
 
 
 def parse():
@@ -239,6 +263,7 @@ def main():
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, args.cpu_seconds)
 
+    traffic = counted_traffic(c.name)
     res = {
         "metric": "paged decode attention KV GB/s (% HBM peak) + tokens/s, LLaMA-13B shape, 1 GPU",
         "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -251,7 +276,9 @@ def main():
         "decode_kernel_tokens_per_s": round(B / (kern_avg_ms * 1e-3), 1),
         "partition_size": args.partition,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "traffic_detail": traffic,
                      "kernel": "paged_attention_decode (decode + partition merge)",
                      "bytes_per_launch": round(bytes_avg)},
         "cpu_baseline": cpu,
