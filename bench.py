@@ -189,7 +189,8 @@ def main():
     q = w.q
     max_len_final = int(w.lengths.max()) + total_steps - 1
     max_blocks = -(-max_len_final // bs)
-    ws_bytes = pkv.pkv_decode_workspace_bytes(B, c.num_q_heads, c.head_dim, max_len_final, args.partition)
+    ws_bytes = pkv.pkv_decode_workspace_bytes(B, c.num_q_heads, c.num_kv_heads, c.head_dim, bs,
+                                              max_len_final, c.dtype, args.partition)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, c.num_q_heads, c.head_dim), dtype=c.torch_dtype, device=dev)
     ids = np.arange(B, dtype=np.int64)

@@ -161,10 +161,12 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t num_blocks, pkv_dtype dtype, void* stream);
 
-/* Bytes of workspace pkv_paged_attention_decode needs for this shape.  partition_size as
- * for the decode call (-1 = the automatic choice).  0 when no split is needed. */
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                  int32_t max_context_len, int32_t partition_size);
+/* Bytes of workspace pkv_paged_attention_decode needs for this shape, max_context_len and
+ * partition_size (same meanings as for the decode call): num_seqs * num_q_heads * P *
+ * (head_dim + 2) floats when contexts are split into P > 1 partitions, else 0. */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                  pkv_dtype dtype, int32_t partition_size);
 
 /* Paged decode attention ("vLLM + PagedAttention", step 3 under "它是怎么工作的？";
  * "PagedAttention 与 vLLM 推理加速", §2.3).  For each sequence b and query head h, with
@@ -174,15 +176,22 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * t % block_size, KV head g.  n == 0 gives zeros.  Accumulation in fp32; out is rounded
  * to the cache's element type (round to nearest even).
  *
- * partition_size: 0 = one pass per (sequence, head); > 0 = split each context into
- * partitions of that many tokens (a multiple of 16 and of block_size), each reduced to
- * (max, sum, partial output) in the workspace and merged by a second kernel; -1 = automatic
- * (512-token partitions).  The result does not depend on physical block placement.
- * max_context_len: an upper bound of context_lens (sizes the grid; larger lengths are
- * clamped to it and to max_blocks_per_seq * block_size).  Table entries outside
- * [0, num_blocks) are treated as empty blocks and never dereferenced.
+ * partition_size: 0 = one workgroup per (sequence, head or head group) covering the whole
+ * context; > 0 = split each context into partitions of that many tokens (a multiple of 16
+ * and of block_size), each reduced to (max, sum, partial output) in the workspace and merged
+ * by a second kernel; -1 = automatic: the fewest equal partitions (a multiple of 32 tokens,
+ * at least 512) that give the launch about 1024 workgroups (no split when the batch already
+ * has that many (sequence, head) rows), decided from the shape and max_context_len only.  All choices compute the
+ * same quantity; results differ only in fp32 rounding order.  For a given shape, length set
+ * and partition_size the result is bit-for-bit reproducible and does not depend on
+ * physical block placement.
+ * max_context_len: an upper bound of context_lens (sizes the launch without reading device
+ * memory on the host; larger lengths are clamped to it and to
+ * max_blocks_per_seq * block_size).  Table entries outside [0, num_blocks) are treated as
+ * empty blocks and never dereferenced.
  * workspace / workspace_bytes: device scratch of at least pkv_decode_workspace_bytes(...)
- * bytes (may be NULL when that is 0).
+ * bytes, 16-byte aligned (may be NULL when that is 0); its contents need no initialisation
+ * and are overwritten.
  * Supported: dtype f32, f16, bf16; head_dim 8, 64, 128; block_size 4, 8, 16, 32;
  * num_q_heads a multiple of num_kv_heads.  Grouped-query attention with 16-bit elements,
  * head_dim 64 or 128 and block_size >= 8 runs on matrix cores (MFMA). */

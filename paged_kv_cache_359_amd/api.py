@@ -142,12 +142,16 @@ class PkvAlloc:
 # ---------------------------------------------------------------------------------------
 # Device operations (torch tensors on the GPU; launched on the current stream)
 # ---------------------------------------------------------------------------------------
-def _dtype_code(t) -> int:
+def _dtype_code_of(dtype) -> int:
     import torch
     m = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-    if t.dtype not in m:
-        raise TypeError(f"unsupported dtype {t.dtype}")
-    return m[t.dtype]
+    if dtype not in m:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return m[dtype]
+
+
+def _dtype_code(t) -> int:
+    return _dtype_code_of(t.dtype)
 
 
 def _stream(t) -> int:
@@ -194,11 +198,14 @@ def pkv_copy_blocks(k_cache, v_cache, pairs):
                                        _dtype_code(k_cache), _stream(k_cache)), "pkv_copy_blocks")
 
 
-def pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
-                               partition_size=-1) -> int:
+def pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                               max_context_len, dtype, partition_size=-1) -> int:
+    """dtype: "f32" | "f16" | "bf16" or a torch dtype."""
+    code = DTYPE_CODES[dtype] if isinstance(dtype, str) else _dtype_code_of(dtype)
     return int(_lib.load().pkv_decode_workspace_bytes(int(num_seqs), int(num_q_heads),
-                                                      int(head_dim), int(max_context_len),
-                                                      int(partition_size)))
+                                                      int(num_kv_heads), int(head_dim),
+                                                      int(block_size), int(max_context_len),
+                                                      code, int(partition_size)))
 
 
 def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,

@@ -4,17 +4,19 @@
 //    高并发LLM推理引擎", steps 1–2 under "它是怎么工作的？").
 //  * copy_blocks: whole-block copies for copy-on-write ("PagedAttention 与 vLLM 推理加速",
 //    §3.2 (3)).
-//  * decode_valu / decode_mfma: one query token per (sequence, head) attends over its
-//    cached K/V, gathered block by block through the block table (same blog post, step 3;
-//    "PagedAttention 与 vLLM 推理加速", §2.3), tiled so that scores are never written to
-//    memory and the softmax is computed online ("vLLM 推理加速：PagedAttention、
-//    FlashAttention 与动态批处理", FlashAttention section: IO-aware tiling that never
-//    materialises the score matrix).
-//  * reduce_partitions: merges per-partition (max, sum, output) triples of long contexts.
+//  * decode: one query token per (sequence, head) attends over its cached K/V, gathered block
+//    by block through the block table (same blog post, step 3; "PagedAttention 与 vLLM 推理
+//    加速", §2.3), tiled so that scores are never written to memory and the softmax is
+//    computed online ("vLLM 推理加速：PagedAttention、FlashAttention 与动态批处理",
+//    FlashAttention section: IO-aware tiling that never materialises the score matrix).
+//    Two inner loops: VALU (any head layout; DPP row reductions) and MFMA (grouped-query
+//    heads sharing one K/V tile form the columns of small matrix products).  One workgroup
+//    per (sequence, head or head group, partition); reduce_partitions merges partitions.
 //
 // Pool layout: [num_blocks][num_kv_heads][block_size][head_dim] for K and for V.  One
 // (block, head) tile is block_size * head_dim contiguous elements (4 KiB for 16 tokens of
-// 128 fp16), so every load below is a 16-byte, fully used, coalesced load.
+// 128 fp16), so every K/V load below is a 16-byte (or, for 64-wide bf16/fp16 V rows, 8-byte),
+// fully used, coalesced load.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -29,27 +31,48 @@ namespace pkv {
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf164_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
-template <int DT> constexpr int elt_size() { return DT == DT_F32 ? 4 : 2; }
+constexpr int elt_size(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+// ---- work geometry shared by host and device ---------------------------------------------
+// VALU inner loop: a lane holds 16 bytes of a token row, LPT lanes hold one row, a wave-wide
+// load covers TPL rows, and one chunk is CT = TPL * J tokens (J loads per lane).
+constexpr int valu_vec(int dt) { return 16 / elt_size(dt); }
+constexpr int valu_lpt(int dt, int d) { return d / valu_vec(dt); }
+constexpr int valu_tpl(int dt, int d) { return 64 / valu_lpt(dt, d); }
+constexpr int valu_j(int dt, int d) { return valu_tpl(dt, d) >= 16 ? 1 : 16 / valu_tpl(dt, d); }
+constexpr int valu_chunk_tokens(int dt, int d) { return valu_tpl(dt, d) * valu_j(dt, d); }
+// MFMA inner loop: 32 tokens per chunk (two 16-token S tiles), up to 16 query heads.
+constexpr int kMfmaChunk = 32;
+// Automatic partitioning: split contexts only as far as needed to give the launch about
+// kAutoWorkgroups workgroups, into equal partitions of a multiple of kAutoQuantum tokens (a
+// multiple of every chunk and block size) and never shorter than kAutoMinPartition tokens.
+// Measured on MI355X: whole contexts for 2048+ (sequence, head) rows; 8 partitions of
+// about 4k tokens for 16 sequences x 8 KV heads at 32k tokens.
+constexpr int kAutoWorkgroups = 1024;
+constexpr int kAutoQuantum = 32;
+constexpr int kAutoMinPartition = 512;
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 16-byte load of K/V data that is read once per call: issued non-temporal, so the stream
-// does not displace reusable lines (block tables, queries) from the caches.  On MI355X this
-// takes a plain streaming read from about 5.6 to about 7 TB/s.
+// K/V data is read once per call: issued non-temporal, the stream does not displace reusable
+// lines (block tables, queries) from the caches.  On MI355X this takes a plain streaming
+// read from about 5.6 to about 7 TB/s.
 __device__ __forceinline__ uint4 load_stream(const char* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream8(const char* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
 }
 
 // ---- element conversions ---------------------------------------------------------------
@@ -141,6 +164,8 @@ __device__ __forceinline__ float xor_sum_16_32(float x) {
   return x;
 }
 
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // ---- launch parameters -------------------------------------------------------------------
 struct DecodeArgs {
   void* out;
@@ -149,6 +174,7 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* tables;
   const int32_t* lens;
+  // partitioned mode
   float* part_o;  // [B][Hq][max_parts][D]
   float* part_m;  // [B][Hq][max_parts]   (log2 domain)
   float* part_l;  // [B][Hq][max_parts]
@@ -170,28 +196,110 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int b) {
 }
 
 // =========================================================================================
-// VALU decode.  One workgroup of NW waves per (sequence, query head, partition).  A lane
-// loads 16 bytes of a token row; LPT lanes cover one row (16 lanes for 128 fp16), so one
-// wave-wide load reads TPL consecutive token rows of the same (block, head) tile: 1 KiB of
-// contiguous memory for 128-wide fp16.  The waves of a workgroup take 16-token chunks of the
-// partition in turn.  Each group of LPT lanes ("row") keeps its own online-softmax state
-// (running max m, running sum l, unnormalised output o) for the tokens it sees, so the
-// inner loop needs no communication beyond the DPP sum of the dot product; the NW*TPL row
-// states are merged once at the end through LDS.
+// VALU inner loop.  One wave streams the chunk of CT tokens starting at cs (tokens >= t1 are
+// masked): J loads of 16 bytes per lane for K and for V, a fully used 1 KiB per wave-wide load
+// for 128-wide fp16.  Each group of LPT lanes (a "row") keeps its own online-softmax state
+// (running max m, running sum l, unnormalised output o) for the tokens it sees, so the loop
+// needs no communication beyond the DPP sum of the dot product.
 // =========================================================================================
+template <int DT, int D, int BS>
+struct Valu {
+  static constexpr int ES = elt_size(DT);
+  static constexpr int VEC = valu_vec(DT);
+  static constexpr int LPT = valu_lpt(DT, D);
+  static_assert(LPT >= 1 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "unsupported head_dim");
+  static constexpr int TPL = valu_tpl(DT, D);
+  static constexpr int J = valu_j(DT, D);
+  static constexpr int CT = valu_chunk_tokens(DT, D);
+  static constexpr bool UNIFORM = TPL <= BS;  // a wave-wide load stays inside one block
+  static constexpr int NBC = (UNIFORM && BS < CT) ? CT / BS : 1;
+
+  struct State {
+    float m, l, o[VEC];
+  };
+
+  __device__ static void init(State& s) {
+    s.m = kNegInf;
+    s.l = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) s.o[i] = 0.f;
+  }
+
+  // kb / vb: pool base plus this lane's (KV head, column) offset.
+  __device__ static void chunk(const DecodeArgs& a, const int32_t* tbl, const char* kb,
+                               const char* vb, size_t blk_bytes, int row, int cs, int t1,
+                               const uint4& qv, State& st) {
+    bool need_mask = cs + CT > t1;  // wave-uniform
+    uint4 kr[J], vr[J];
+    bool ok[J];
+    if constexpr (UNIFORM) {
+      int ids[NBC];
+#pragma unroll
+      for (int k = 0; k < NBC; ++k) {
+        const int first = cs + k * BS;  // first token of the k-th block of this chunk
+        ids[k] = uniform(first < t1 ? tbl[first / BS] : -1);
+        need_mask |= (unsigned)ids[k] >= (unsigned)a.num_blocks;
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int id = ids[NBC > 1 ? (j * TPL) / BS : 0];
+        const int tok = cs + j * TPL + row;
+        const bool valid = (unsigned)id < (unsigned)a.num_blocks;
+        ok[j] = valid && tok < t1;
+        const size_t off = size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * ES;
+        kr[j] = load_stream(kb + off);
+        vr[j] = load_stream(vb + off);
+      }
+    } else {
+      need_mask = true;  // per-lane block ids: always mask (generic path)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int tok = cs + j * TPL + row;
+        const int id = tok < t1 ? tbl[tok / BS] : -1;
+        const bool valid = (unsigned)id < (unsigned)a.num_blocks;
+        ok[j] = valid && tok < t1;
+        const size_t off = size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * ES;
+        kr[j] = load_stream(kb + off);
+        vr[j] = load_stream(vb + off);
+      }
+    }
+    float s[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) s[j] = group_sum<LPT>(dot16<DT>(kr[j], qv, 0.f)) * a.scale_log2;
+    if (need_mask) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        s[j] = ok[j] ? s[j] : kNegInf;
+        if (!ok[j]) vr[j] = make_uint4(0, 0, 0, 0);  // unused slots may hold anything
+      }
+    }
+    float cm = s[0];
+#pragma unroll
+    for (int j = 1; j < J; ++j) cm = fmaxf(cm, s[j]);
+    const float mn = fmaxf(st.m, cm);
+    const float mu = mn == kNegInf ? 0.f : mn;  // no token seen yet: keep everything at 0
+    const float alpha = exp2_hw(st.m - mu);
+    st.m = mn;
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) st.o[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float pj = exp2_hw(s[j] - mu);
+      st.l += pj;
+      axpy16<DT, VEC>(st.o, pj, vr[j]);
+    }
+  }
+
+};
+
+// VALU decode: one workgroup of NW waves per (sequence, query head, partition);
+// the waves take the partition's chunks in turn and merge their NW * TPL row states through
+// LDS at the end.
 template <int DT, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
-  constexpr int ES = elt_size<DT>();
-  constexpr int VEC = 16 / ES;              // elements per 16-byte load
-  constexpr int LPT = D / VEC;              // lanes per token row
-  static_assert(LPT >= 1 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "unsupported head_dim");
-  constexpr int TPL = 64 / LPT;             // token rows per wave-wide load
-  constexpr int J = TPL >= 16 ? 1 : 16 / TPL;
-  constexpr int CT = TPL * J;               // tokens per chunk
-  constexpr bool UNIFORM = TPL <= BS;       // a wave-wide load stays inside one block
-  constexpr int NBC = (UNIFORM && BS < CT) ? CT / BS : 1;  // blocks per chunk (uniform case)
-  constexpr int NS = NW * TPL;              // row states per workgroup
-
+  using V = Valu<DT, D, BS>;
+  constexpr int NS = NW * V::TPL;  // row states per workgroup
   __shared__ float s_o[NS][D];
   __shared__ float s_m[NS];
   __shared__ float s_l[NS];
@@ -213,97 +321,29 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
   const int nparts = (ctx + a.part_size - 1) / a.part_size;
 
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row = lane / LPT;
-  const int col = lane % LPT;
+  const int wave = uniform(tid >> 6);
+  const int row = lane / V::LPT;
+  const int col = lane % V::LPT;
   const int kvh = h / a.group;
   const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
-  const char* kbase = static_cast<const char*>(a.k_cache);
-  const char* vbase = static_cast<const char*>(a.v_cache);
-  // Byte offset of (block 0, this KV head, slot 0, this lane's 16 bytes).
-  const size_t lane_off = (size_t(kvh) * BS * D + size_t(col) * VEC) * ES;
-  const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * ES;
-
+  const size_t lane_off = (size_t(kvh) * BS * D + size_t(col) * V::VEC) * V::ES;
+  const char* kb = static_cast<const char*>(a.k_cache) + lane_off;
+  const char* vb = static_cast<const char*>(a.v_cache) + lane_off;
+  const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * V::ES;
   const uint4 qv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
-                                                    (out_row + size_t(col) * VEC) * ES);
-  float m = kNegInf, l = 0.f;
-  float o[VEC];
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) o[i] = 0.f;
+                                                    (out_row + size_t(col) * V::VEC) * V::ES);
+  typename V::State st;
+  V::init(st);
+  const int nchunks = (t1 - t0 + V::CT - 1) / V::CT;
+  for (int c = wave; c < nchunks; c += NW)
+    V::chunk(a, tbl, kb, vb, blk_bytes, row, t0 + c * V::CT, t1, qv, st);
 
-  const int nchunks = (t1 - t0 + CT - 1) / CT;
-  for (int c = wave; c < nchunks; c += NW) {
-    const int cs = t0 + c * CT;
-    bool need_mask = cs + CT > t1;  // wave-uniform
-    uint4 kr[J], vr[J];
-    bool ok[J];
-    if constexpr (UNIFORM) {
-      int ids[NBC];
+  const int si = wave * V::TPL + row;
 #pragma unroll
-      for (int k = 0; k < NBC; ++k) {
-        const int first = cs + k * BS;  // first token of the k-th block of this chunk
-        int id = (first < t1) ? tbl[first / BS] : -1;
-        ids[k] = __builtin_amdgcn_readfirstlane(id);
-        need_mask |= (unsigned)ids[k] >= (unsigned)a.num_blocks;
-      }
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int id = ids[NBC > 1 ? (j * TPL) / BS : 0];
-        const int tok = cs + j * TPL + row;
-        const bool valid = (unsigned)id < (unsigned)a.num_blocks;
-        ok[j] = valid && tok < t1;
-        const size_t off = size_t(valid ? id : 0) * blk_bytes + lane_off + size_t(tok % BS) * D * ES;
-        kr[j] = load_stream(kbase + off);
-        vr[j] = load_stream(vbase + off);
-      }
-    } else {
-      need_mask = true;  // per-lane block ids: always mask (generic path)
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int tok = cs + j * TPL + row;
-        int id = (tok < t1) ? tbl[tok / BS] : -1;
-        const bool valid = (unsigned)id < (unsigned)a.num_blocks;
-        ok[j] = valid && tok < t1;
-        const size_t off = size_t(valid ? id : 0) * blk_bytes + lane_off + size_t(tok % BS) * D * ES;
-        kr[j] = load_stream(kbase + off);
-        vr[j] = load_stream(vbase + off);
-      }
-    }
-    float s[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) s[j] = group_sum<LPT>(dot16<DT>(kr[j], qv, 0.f)) * a.scale_log2;
-    if (need_mask) {
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        s[j] = ok[j] ? s[j] : kNegInf;
-        if (!ok[j]) vr[j] = make_uint4(0, 0, 0, 0);  // unused slots may hold anything
-      }
-    }
-    float cm = s[0];
-#pragma unroll
-    for (int j = 1; j < J; ++j) cm = fmaxf(cm, s[j]);
-    const float mn = fmaxf(m, cm);
-    const float mu = mn == kNegInf ? 0.f : mn;  // no token seen yet: keep everything at 0
-    const float alpha = exp2_hw(m - mu);
-    m = mn;
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) o[i] *= alpha;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const float pj = exp2_hw(s[j] - mu);
-      l += pj;
-      axpy16<DT, VEC>(o, pj, vr[j]);
-    }
-  }
-
-  // Merge the NS row states of this workgroup.
-  const int si = wave * TPL + row;
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) s_o[si][col * VEC + i] = o[i];
+  for (int i = 0; i < V::VEC; ++i) s_o[si][col * V::VEC + i] = st.o[i];
   if (col == 0) {
-    s_m[si] = m;
-    s_l[si] = l;
+    s_m[si] = st.m;
+    s_l[si] = st.l;
   }
   __syncthreads();
   for (int d = tid; d < D; d += NW * 64) {
@@ -331,40 +371,180 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
 }
 
 // =========================================================================================
-// MFMA decode for grouped-query attention (16-bit K/V, head_dim 64 or 128).  One workgroup
-// of 4 waves per (sequence, KV head, partition, group of up to 16 query heads).  The G query
-// heads that share a KV head are the 16 columns (padded) of one small matrix product:
-//   S[16 tokens x 16 heads]  = K_chunk[16 x D] . Q^T[D x 16]       (v_mfma 16x16x32)
-//   O^T[D x 16 heads]       += V_chunk^T[D x 16] . P^T[16 x 16]     (v_mfma 16x16x16)
-// With this orientation the S accumulator of lane l already holds P^T in the operand layout
-// the second product needs (column = head l%16, four consecutive tokens), and every lane
-// accumulates output for the single head l%16, so the online-softmax rescale is lane-local.
-// K goes straight from HBM into the A operand (16-byte loads, four per lane per chunk); V is
-// staged through LDS, row-major with a 16-byte pad per row, and read back transposed.
+// MFMA inner loop for grouped-query attention (16-bit K/V, head_dim 64 or 128).  The query
+// heads sharing a KV head (up to 16 per row) are the columns of two small products per
+// 32-token chunk:
+//   S[16 tokens x 16 heads]  = K_half[16 x D] . Q^T[D x 16]       (v_mfma 16x16x32), twice
+//   O^T[D x 16 heads]       += V^T[D x 32 tokens] . P^T[32 x 16]   (v_mfma 16x16x32), E times
+// The S accumulator of lane l holds scores of head l%16 for tokens 4*(l/16)+i of each half;
+// taking those eight tokens, in that order, as the lane's eight contraction indices of the
+// second product puts P^T in its operand layout without moving data.  The V^T operand needs,
+// per lane, the same eight tokens for one output column: each lane loads the 16-byte (E
+// elements) slice [E*c, E*c + E) of those eight token rows, which is already a fully used
+// coalesced load (16 lanes cover a row), and picks element r of each row to form the operand
+// of output tile r, whose column c stands for d = E*c + r.  So V is transposed in registers
+// with one byte-permute per operand word and never goes through LDS.  Lane l ends up holding
+// the outputs of head l%16 for d in [4E*(l/16), 4E*(l/16) + 4E), contiguous.
 // For bf16 the probabilities are split into a bf16 high part and a bf16 remainder (two
-// products) so that P keeps ~16 significant bits; fp16 P keeps 11.
+// products), so P keeps ~16 significant bits; fp16 P keeps 11.
 // =========================================================================================
 template <int DT, int D, int BS>
-__global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
+struct Mfma {
   static_assert(DT == DT_F16 || DT == DT_BF16, "16-bit only");
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-  constexpr int NW = 4;
-  constexpr int KK = D / 32;        // k-steps of the S product
-  constexpr int NN = D / 16;        // 16-wide output tiles
-  constexpr int LPT = D / 8;        // lanes per V row in the coalesced load
-  constexpr int TPL = 64 / LPT;     // V rows per wave-wide load
-  constexpr int JV = 16 / TPL;      // V loads per chunk
-  constexpr int PITCH = D + 8;      // LDS row pitch in elements (16-byte pad)
-  constexpr int NBC = BS < 16 ? 16 / BS : 1;
-  constexpr bool SPLIT_P = DT == DT_BF16;
+  static_assert(BS >= 8, "block_size >= 8");
+  static constexpr int KK = D / 32;   // k-steps of the S product
+  static constexpr int E = D / 16;    // elements per lane per V row = output tiles
+  static constexpr int NBH = BS < 16 ? 16 / BS : 1;  // blocks per 16-token half
+  static constexpr bool SPLIT_P = DT == DT_BF16;
   using vec8 = typename std::conditional<DT == DT_F16, half8_t, bf168_t>::type;
-  using vec4 = typename std::conditional<DT == DT_F16, half4_t, bf164_t>::type;
   using elt = typename std::conditional<DT == DT_F16, _Float16, __bf16>::type;
 
-  // V tiles while streaming; the merge buffers afterwards.
-  constexpr int TILE_BYTES = NW * 16 * PITCH * 2;
-  constexpr int MERGE_BYTES = NW * 16 * (D + 2) * 4;
-  __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES];
+  struct State {
+    float4_t acc[E];
+    float m, l;
+  };
+
+  __device__ static void init(State& st) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) st.acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = kNegInf;
+    st.l = 0.f;
+  }
+
+  // Q^T operand: lane holds q[h0 + lane%16][32kk + 8*(lane/16) .. + 8] for each k-step.
+  __device__ static void load_q(const DecodeArgs& a, size_t q_row0, int nh, int lane, vec8 (&qop)[KK]) {
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const bool hv = n16 < nh;
+    const char* qp = static_cast<const char*>(a.q) + ((q_row0 + (hv ? n16 : 0)) * D) * 2;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 w = hv ? *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2) : make_uint4(0, 0, 0, 0);
+      qop[kk] = __builtin_bit_cast(vec8, w);
+    }
+  }
+
+  __device__ static float4_t mma(const vec8& x, const vec8& y, const float4_t& c) {
+    if constexpr (DT == DT_F16) return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+  }
+
+  // kb / vb: pool base plus this KV head's offset.  cs: a multiple of 16.
+  __device__ static void chunk(const DecodeArgs& a, const int32_t* tbl, const char* kb,
+                               const char* vb, size_t blk_bytes, int cs, int t1, int lane,
+                               const vec8 (&qop)[KK], State& st) {
+    const int n16 = lane & 15, g4 = lane >> 4;
+    bool need_mask = cs + kMfmaChunk > t1;  // wave-uniform
+    int ids[2][NBH];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int k = 0; k < NBH; ++k) {
+        const int first = cs + 16 * hf + k * (BS < 16 ? BS : 16);
+        ids[hf][k] = uniform(first < t1 ? tbl[first / BS] : -1);
+        need_mask |= (unsigned)ids[hf][k] >= (unsigned)a.num_blocks;
+      }
+    // K rows cs + 16hf + n16, 8 elements per k-step.
+    uint4 kr[2][KK];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int tok = cs + 16 * hf + n16;
+      const int id = ids[hf][NBH > 1 ? n16 / BS : 0];
+      const bool valid = (unsigned)id < (unsigned)a.num_blocks;
+      const char* p = kb + size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * 2;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kr[hf][kk] = load_stream(p + (32 * kk + 8 * g4) * 2);
+    }
+    // V rows cs + 16hf + 4g4 + i, elements [E*n16, E*n16 + E).
+    uint32_t vr[2][4][E / 2];
+    bool vok[2][4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * hf + 4 * g4 + i;
+        const int tok = cs + r;
+        const int id = ids[hf][NBH > 1 ? (4 * g4 + i) / BS : 0];
+        const bool valid = (unsigned)id < (unsigned)a.num_blocks;
+        vok[hf][i] = valid && tok < t1;
+        const char* p = vb + size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * 2 + E * n16 * 2;
+        if constexpr (E == 8) {
+          const uint4 w = load_stream(p);
+          vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
+        } else {
+          const uint2 w = load_stream8(p);
+          vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
+        }
+      }
+    // S = K . Q^T for both halves.
+    float4_t s[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      s[hf] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) s[hf] = mma(__builtin_bit_cast(vec8, kr[hf][kk]), qop[kk], s[hf]);
+    }
+    float sv[2][4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[hf][i] = s[hf][i] * a.scale_log2;
+        if (need_mask) {
+          if (!vok[hf][i]) {
+            sv[hf][i] = kNegInf;
+#pragma unroll
+            for (int q = 0; q < E / 2; ++q) vr[hf][i][q] = 0u;  // unused slots may hold anything
+          }
+        }
+      }
+    float cm = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    cm = xor_max_16_32(cm);
+    const float mn = fmaxf(st.m, cm);
+    const float mu = mn == kNegInf ? 0.f : mn;
+    const float alpha = exp2_hw(st.m - mu);
+    st.m = mn;
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = exp2_hw(sv[j >> 2][j & 3] - mu);
+    st.l = st.l * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+#pragma unroll
+    for (int r = 0; r < E; ++r) st.acc[r] *= alpha;
+    vec8 phi, plo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      phi[j] = elt(p[j]);
+      if constexpr (SPLIT_P) plo[j] = elt(p[j] - float(phi[j]));
+    }
+    // O^T += V^T . P^T, one output tile per element position r of the lane's V slices.
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = vr[(2 * q) >> 2][(2 * q) & 3][r >> 1];
+        const uint32_t hi = vr[(2 * q + 1) >> 2][(2 * q + 1) & 3][r >> 1];
+        w[q] = (r & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      const vec8 vop = __builtin_bit_cast(vec8, make_uint4(w[0], w[1], w[2], w[3]));
+      st.acc[r] = mma(vop, phi, st.acc[r]);
+      if constexpr (SPLIT_P) st.acc[r] = mma(vop, plo, st.acc[r]);
+    }
+  }
+
+  // Output d of element (r, v) of the lane's accumulators: E * (4 * (lane / 16) + v) + r.
+  __device__ static int out_d(int g4, int v, int r) { return E * (4 * g4 + v) + r; }
+};
+
+// MFMA decode: one workgroup of 4 waves per (sequence, KV head, partition, group
+// of up to 16 query heads); the waves take the partition's 32-token chunks in turn and merge
+// through LDS at the end.
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
+  using M = Mfma<DT, D, BS>;
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) float smem[NW * 16 * (D + 2)];
 
   const int nhg = (a.group + 15) / 16;
   const int kvh = blockIdx.x / nhg;
@@ -387,157 +567,44 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   const int nparts = (ctx + a.part_size - 1) / a.part_size;
 
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n16 = lane & 15;   // MFMA column / row index
-  const int g4 = lane >> 4;    // MFMA lane group
+  const int wave = uniform(tid >> 6);
+  const int n16 = lane & 15, g4 = lane >> 4;
   const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
-  const char* kbase = static_cast<const char*>(a.k_cache);
-  const char* vbase = static_cast<const char*>(a.v_cache);
-  const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
   const size_t head_off = size_t(kvh) * BS * D * 2;
+  const char* kb = static_cast<const char*>(a.k_cache) + head_off;
+  const char* vb = static_cast<const char*>(a.v_cache) + head_off;
+  const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
 
-  // Q^T operand: lane holds q[h0 + n16][(4kk + g4)*8 .. +8] for each k-step kk.
-  vec8 qop[KK];
-  {
-    const bool hv = n16 < nh;
-    const char* qp = static_cast<const char*>(a.q) + ((q_row0 + (hv ? n16 : 0)) * D) * 2;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      uint4 w = hv ? *reinterpret_cast<const uint4*>(qp + ((4 * kk + g4) * 8) * 2) : make_uint4(0, 0, 0, 0);
-      qop[kk] = __builtin_bit_cast(vec8, w);
-    }
-  }
+  typename M::vec8 qop[M::KK];
+  M::load_q(a, q_row0, nh, lane, qop);
+  typename M::State st;
+  M::init(st);
+  const int nchunks = (t1 - t0 + kMfmaChunk - 1) / kMfmaChunk;
+  for (int c = wave; c < nchunks; c += NW) M::chunk(a, tbl, kb, vb, blk_bytes, t0 + c * kMfmaChunk, t1, lane, qop, st);
+  st.l = xor_sum_16_32(st.l);  // m already agrees across the four lane groups
 
-  elt* vt = reinterpret_cast<elt*>(smem) + wave * 16 * PITCH;  // this wave's V tile
-  float4_t acc[NN];
+  float* mo = smem;                       // [NW][16][D]
+  float* mm = mo + NW * 16 * D;           // [NW][16]
+  float* ml = mm + NW * 16;               // [NW][16]
 #pragma unroll
-  for (int n = 0; n < NN; ++n) acc[n] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, l = 0.f;
-
-  const int nchunks = (t1 - t0 + 15) / 16;
-  for (int c = wave; c < nchunks; c += NW) {
-    const int cs = t0 + c * 16;
-    bool need_mask = cs + 16 > t1;  // wave-uniform
-    int ids[NBC];
+  for (int r = 0; r < M::E; ++r)
 #pragma unroll
-    for (int k = 0; k < NBC; ++k) {
-      const int first = cs + k * (BS < 16 ? BS : 16);
-      int id = (first < t1) ? tbl[first / BS] : -1;
-      ids[k] = __builtin_amdgcn_readfirstlane(id);
-      need_mask |= (unsigned)ids[k] >= (unsigned)a.num_blocks;
-    }
-    // K: token cs + n16, 8 elements per k-step.
-    uint4 kr[KK];
-    {
-      const int tok = cs + n16;
-      const int id = ids[NBC > 1 ? n16 / BS : 0];
-      const bool valid = (unsigned)id < (unsigned)a.num_blocks;
-      const char* p = kbase + size_t(valid ? id : 0) * blk_bytes + head_off + size_t(tok % BS) * D * 2;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kr[kk] = load_stream(p + ((4 * kk + g4) * 8) * 2);
-    }
-    // V: coalesced rows, token cs + j*TPL + lane/LPT.
-    uint4 vr[JV];
-    bool vok[JV];
-#pragma unroll
-    for (int j = 0; j < JV; ++j) {
-      const int r = j * TPL + lane / LPT;
-      const int tok = cs + r;
-      const int id = ids[NBC > 1 ? r / BS : 0];
-      const bool valid = (unsigned)id < (unsigned)a.num_blocks;
-      vok[j] = valid && tok < t1;
-      const char* p = vbase + size_t(valid ? id : 0) * blk_bytes + head_off + size_t(tok % BS) * D * 2;
-      vr[j] = load_stream(p + (lane % LPT) * 16);
-    }
-    // S = K . Q^T
-    float4_t s = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if constexpr (DT == DT_F16)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(vec8, kr[kk]), qop[kk], s, 0, 0, 0);
-      else
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(vec8, kr[kk]), qop[kk], s, 0, 0, 0);
-    }
-    // Stage V (zeroing rows of tokens that do not exist: they may hold anything).
-#pragma unroll
-    for (int j = 0; j < JV; ++j) {
-      const int r = j * TPL + lane / LPT;
-      uint4 w = vr[j];
-      if (need_mask && !vok[j]) w = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(vt + r * PITCH + (lane % LPT) * 8) = w;
-    }
-    // Scores of this lane: head n16, tokens cs + 4*g4 + i.
-    float sv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = s[i] * a.scale_log2;
-      if (need_mask) {
-        const int tok = cs + 4 * g4 + i;
-        const int id = ids[NBC > 1 ? (4 * g4 + i) / BS : 0];
-        const bool ok = tok < t1 && (unsigned)id < (unsigned)a.num_blocks;
-        sv[i] = ok ? sv[i] : kNegInf;
-      }
-    }
-    float cm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    cm = xor_max_16_32(cm);
-    const float mn = fmaxf(m, cm);
-    const float mu = mn == kNegInf ? 0.f : mn;
-    const float alpha = exp2_hw(m - mu);
-    m = mn;
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = exp2_hw(sv[i] - mu);
-    l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-    for (int n = 0; n < NN; ++n) acc[n] *= alpha;
-    vec4 phi, plo;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      phi[i] = elt(p[i]);
-      if constexpr (SPLIT_P) plo[i] = elt(p[i] - float(phi[i]));
-    }
-    __builtin_amdgcn_wave_barrier();
-    // O^T += V^T . P^T: lane reads V[4*g4 + i][16n + n16], i = 0..3.
-#pragma unroll
-    for (int n = 0; n < NN; ++n) {
-      vec4 vop;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vop[i] = vt[(4 * g4 + i) * PITCH + 16 * n + n16];
-      if constexpr (DT == DT_F16) {
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop, phi, acc[n], 0, 0, 0);
-      } else {
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, phi, acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, plo, acc[n], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  // Per-wave totals: l summed over the four lane groups (m already agrees across them).
-  l = xor_sum_16_32(l);
-  __syncthreads();  // all waves are done with their V tiles; reuse LDS for the merge
-  float* mo = reinterpret_cast<float*>(smem);             // [NW][16][D]
-  float* mm = mo + NW * 16 * D;                           // [NW][16]
-  float* ml = mm + NW * 16;                               // [NW][16]
-#pragma unroll
-  for (int n = 0; n < NN; ++n)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) mo[(wave * 16 + n16) * D + 16 * n + 4 * g4 + v] = acc[n][v];
+    for (int v = 0; v < 4; ++v) mo[(wave * 16 + n16) * D + M::out_d(g4, v, r)] = st.acc[r][v];
   if (g4 == 0) {
-    mm[wave * 16 + n16] = m;
-    ml[wave * 16 + n16] = l;
+    mm[wave * 16 + n16] = st.m;
+    ml[wave * 16 + n16] = st.l;
   }
   __syncthreads();
   for (int i = tid; i < nh * D; i += NW * 64) {
     const int hh = i / D, d = i % D;
-    float M = kNegInf;
+    float Mx = kNegInf;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w * 16 + hh]);
+    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, mm[w * 16 + hh]);
     float L = 0.f, O = 0.f;
-    if (M != kNegInf) {
+    if (Mx != kNegInf) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float sc = exp2_hw(mm[w * 16 + hh] - M);
+        const float sc = exp2_hw(mm[w * 16 + hh] - Mx);
         L += ml[w * 16 + hh] * sc;
         O += mo[(w * 16 + hh) * D + d] * sc;
       }
@@ -548,7 +615,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       const size_t pi = ((size_t(b) * a.num_q_heads + h0 + hh) * a.max_parts + part);
       a.part_o[pi * D + d] = O;
       if (d == 0) {
-        a.part_m[pi] = M;
+        a.part_m[pi] = Mx;
         a.part_l[pi] = L;
       }
     }
@@ -634,33 +701,48 @@ int dtype_size(pkv_dtype dt) { return dt == PKV_F32 ? 4 : 2; }
 
 bool valid_dtype(pkv_dtype dt) { return dt == PKV_F32 || dt == PKV_F16 || dt == PKV_BF16; }
 
-int resolve_partition(int32_t partition_size, int32_t ctx_limit) {
-  if (partition_size < 0) return 512;
-  if (partition_size == 0) {
-    int p = ((ctx_limit + 15) / 16) * 16;
-    return p < 16 ? 16 : p;
-  }
-  return partition_size;
+bool use_mfma(pkv_dtype dt, int d, int bs, int group) {
+  return dt != PKV_F32 && (d == 64 || d == 128) && bs >= 8 && group > 1;
+}
+
+// Tokens per partition for a shape (a multiple of 16 and of the block size).  0 = the whole
+// context; -1 = automatic: the fewest partitions that give the launch about kAutoWorkgroups
+// workgroups, at most one per kAutoMinPartition tokens of the longest context, their size
+// rounded up to a multiple of kAutoQuantum.  Decided from the shape and max_context_len only.
+int resolve_partition(int32_t partition_size, int32_t ctx_limit, int64_t rows) {
+  const int whole = ctx_limit < 16 ? 16 : (ctx_limit + 15) / 16 * 16;
+  if (partition_size > 0) return partition_size;
+  if (partition_size == 0) return whole;
+  const int64_t want = (kAutoWorkgroups + rows - 1) / rows;
+  const int64_t most = (int64_t(ctx_limit) + kAutoMinPartition - 1) / kAutoMinPartition;
+  const int64_t parts = want < most ? want : most;
+  if (parts <= 1) return whole;
+  const int64_t per = (int64_t(ctx_limit) + parts - 1) / parts;
+  return int((per + kAutoQuantum - 1) / kAutoQuantum * kAutoQuantum);
+}
+
+// Workgroups per (sequence, partition): one per query head (VALU) or per group of up to 16
+// query heads sharing a KV head (MFMA).
+int64_t rows_per_seq(pkv_dtype dt, int hq, int hkv, int d, int bs) {
+  const int group = hq / hkv;
+  return use_mfma(dt, d, bs, group) ? int64_t(hkv) * ((group + 15) / 16) : int64_t(hq);
 }
 
 typedef void (*kernel_fn)(DecodeArgs);
 
-template <int DT, int D, int BS>
-kernel_fn pick_valu() { return decode_valu<DT, D, BS, 4>; }
-
 template <int DT, int D>
 kernel_fn pick_valu_bs(int bs) {
   switch (bs) {
-    case 4: return pick_valu<DT, D, 4>();
-    case 8: return pick_valu<DT, D, 8>();
-    case 16: return pick_valu<DT, D, 16>();
-    case 32: return pick_valu<DT, D, 32>();
+    case 4: return decode_valu<DT, D, 4, 4>;
+    case 8: return decode_valu<DT, D, 8, 4>;
+    case 16: return decode_valu<DT, D, 16, 4>;
+    case 32: return decode_valu<DT, D, 32, 4>;
   }
   return nullptr;
 }
 
 template <int DT>
-kernel_fn pick_valu_d(int d, int bs) {
+kernel_fn pick_valu(int d, int bs) {
   switch (d) {
     case 8: return pick_valu_bs<DT, 8>(bs);
     case 64: return pick_valu_bs<DT, 64>(bs);
@@ -680,12 +762,19 @@ kernel_fn pick_mfma_bs(int bs) {
 }
 
 template <int DT>
-kernel_fn pick_mfma_d(int d, int bs) {
+kernel_fn pick_mfma(int d, int bs) {
   switch (d) {
     case 64: return pick_mfma_bs<DT, 64>(bs);
     case 128: return pick_mfma_bs<DT, 128>(bs);
   }
   return nullptr;
+}
+
+kernel_fn pick_decode(pkv_dtype dt, int d, int bs, bool mfma) {
+  if (mfma) return dt == PKV_F16 ? pick_mfma<DT_F16>(d, bs) : pick_mfma<DT_BF16>(d, bs);
+  return dt == PKV_F32   ? pick_valu<DT_F32>(d, bs)
+         : dt == PKV_F16 ? pick_valu<DT_F16>(d, bs)
+                         : pick_valu<DT_BF16>(d, bs);
 }
 
 template <int DT>
@@ -698,8 +787,9 @@ kernel_fn pick_reduce(int d) {
   return nullptr;
 }
 
-bool use_mfma(pkv_dtype dt, int d, int bs, int group) {
-  return dt != PKV_F32 && (d == 64 || d == 128) && bs >= 8 && group > 1;
+kernel_fn pick_reduce(pkv_dtype dt, int d) {
+  return dt == PKV_F32 ? pick_reduce<DT_F32>(d)
+         : dt == PKV_F16 ? pick_reduce<DT_F16>(d) : pick_reduce<DT_BF16>(d);
 }
 
 // Text of the last HIP error a call of this thread reported (see pkv_last_error).
@@ -770,11 +860,15 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
   return launch_status("copy_blocks");
 }
 
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                  int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const int p = resolve_partition(partition_size, max_context_len);
-  if (p <= 0) return 0;
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                  pkv_dtype dtype, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_context_len <= 0 || num_q_heads % num_kv_heads != 0 ||
+      !valid_dtype(dtype) || partition_size < -1)
+    return 0;
+  const int64_t rows = rows_per_seq(dtype, num_q_heads, num_kv_heads, head_dim, block_size);
+  const int p = resolve_partition(partition_size, max_context_len, int64_t(num_seqs) * rows);
   const int64_t max_parts = (int64_t(max_context_len) + p - 1) / p;
   if (max_parts <= 1) return 0;
   return size_t(num_seqs) * num_q_heads * max_parts * (size_t(head_dim) + 2) * sizeof(float);
@@ -809,19 +903,22 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
   const int64_t cap = int64_t(max_blocks_per_seq) * block_size;
   const int32_t ctx_limit = int32_t(max_context_len < cap ? max_context_len : cap);
   const int group = num_q_heads / num_kv_heads;
-  const int part = resolve_partition(partition_size, ctx_limit);
+  const bool mfma = use_mfma(dtype, head_dim, block_size, group);
+  const int64_t rows = rows_per_seq(dtype, num_q_heads, num_kv_heads, head_dim, block_size);
+  // The partition follows max_context_len exactly as pkv_decode_workspace_bytes does; the
+  // clamp to the table's capacity can only lower the partition count.
+  const int part = resolve_partition(partition_size, max_context_len, int64_t(num_seqs) * rows);
   const int64_t max_parts64 = ctx_limit > 0 ? (int64_t(ctx_limit) + part - 1) / part : 1;
   if (max_parts64 > 65535 || num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
   const int max_parts = int(max_parts64);
 
-  DecodeArgs a;
+  DecodeArgs a = {};
   a.out = out;
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.tables = block_tables;
   a.lens = context_lens;
-  a.part_o = a.part_m = a.part_l = nullptr;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = group;
@@ -831,7 +928,6 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
   a.part_size = part;
   a.max_parts = max_parts;
   a.scale_log2 = scale * 1.4426950408889634f;
-
   if (max_parts > 1) {
     const size_t need =
         size_t(num_seqs) * num_q_heads * max_parts * (size_t(head_dim) + 2) * sizeof(float);
@@ -841,29 +937,15 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
     a.part_m = w + size_t(num_seqs) * num_q_heads * max_parts * head_dim;
     a.part_l = a.part_m + size_t(num_seqs) * num_q_heads * max_parts;
   }
-
+  kernel_fn k = pick_decode(dtype, head_dim, block_size, mfma);
+  kernel_fn r = pick_reduce(dtype, head_dim);
+  if (!k || !r) return PKV_ERR_UNSUPPORTED;
+  const dim3 grid{unsigned(rows), unsigned(max_parts), unsigned(num_seqs)};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool mfma = use_mfma(dtype, head_dim, block_size, group);
-  kernel_fn k = nullptr;
-  dim3 grid;
-  if (mfma) {
-    k = dtype == PKV_F16 ? pick_mfma_d<DT_F16>(head_dim, block_size)
-                         : pick_mfma_d<DT_BF16>(head_dim, block_size);
-    grid = dim3(unsigned(num_kv_heads * ((group + 15) / 16)), unsigned(max_parts), unsigned(num_seqs));
-  } else {
-    k = dtype == PKV_F32   ? pick_valu_d<DT_F32>(head_dim, block_size)
-        : dtype == PKV_F16 ? pick_valu_d<DT_F16>(head_dim, block_size)
-                           : pick_valu_d<DT_BF16>(head_dim, block_size);
-    grid = dim3(unsigned(num_q_heads), unsigned(max_parts), unsigned(num_seqs));
-  }
-  if (!k) return PKV_ERR_UNSUPPORTED;
   clear_stale_error();
   hipLaunchKernelGGL(k, grid, dim3(256), 0, st, a);
   if (launch_status("paged_attention_decode") != PKV_OK) return PKV_ERR_HIP;
   if (max_parts > 1) {
-    kernel_fn r = dtype == PKV_F32   ? pick_reduce<DT_F32>(head_dim)
-                  : dtype == PKV_F16 ? pick_reduce<DT_F16>(head_dim)
-                                     : pick_reduce<DT_BF16>(head_dim);
     hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(128), 0, st, a);
     return launch_status("reduce_partitions");
   }

@@ -112,8 +112,8 @@ class GpuState:
         q = self.w.q[step] if q is None else q
         out = torch.empty_like(q)
         mc = int(np.max(lens)) if max_ctx is None and len(lens) else (max_ctx or 0)
-        nbytes = pkv.pkv_decode_workspace_bytes(q.shape[0], q.shape[1], c.head_dim, max(mc, 1),
-                                                partition_size)
+        nbytes = pkv.pkv_decode_workspace_bytes(q.shape[0], q.shape[1], c.num_kv_heads, c.head_dim,
+                                                c.block_size, max(mc, 1), c.dtype, partition_size)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device) if nbytes else None
         pkv.pkv_paged_attention_decode(out, q, self.k_cache, self.v_cache, t, l, mc, c.scale,
                                        partition_size, ws)

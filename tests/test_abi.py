@@ -78,6 +78,7 @@ def decode(**kw):
     (dict(maxctx=4096, maxb=256, part=512), 6),  # needs a workspace, none given
     (dict(maxctx=4096, maxb=256, part=512, ws=FAKE, wsb=100), 6),  # workspace too small
     (dict(maxctx=4096, maxb=256, part=16, nseq=70000), 5),  # grid limit
+    (dict(maxctx=4096, maxb=256, part=-1, nseq=2, hq=4, hkv=4), 6),  # auto splits 2x4 rows
 ])
 def test_decode_validation(kw, status):
     assert decode(**kw) == status
@@ -85,11 +86,24 @@ def test_decode_validation(kw, status):
 
 def test_workspace_bytes():
     f = pkv.pkv_decode_workspace_bytes
-    assert f(2, 4, 128, 512, 512) == 0          # one partition: nothing to merge
-    assert f(2, 4, 128, 513, 512) == 2 * 4 * 2 * 130 * 4
-    assert f(2, 4, 128, 4096, -1) == 2 * 4 * 8 * 130 * 4
-    assert f(2, 4, 128, 4096, 0) == 0           # no split
-    assert f(0, 4, 128, 4096, 512) == 0
+    # One (m, l, o) triple per (sequence, query head, partition) when there are several.
+    assert f(2, 4, 4, 128, 16, 512, "f16", 512) == 0        # one partition: nothing to merge
+    assert f(2, 4, 4, 128, 16, 513, "f16", 512) == 2 * 4 * 2 * 130 * 4
+    assert f(2, 4, 4, 128, 16, 4096, "f16", 0) == 0         # no split
+    assert f(0, 4, 4, 128, 16, 4096, "f16", 512) == 0
+    assert f(2, 4, 3, 128, 16, 64, "f16", 512) == 0         # Hq not a multiple of Hkv
+    # Automatic: split only as far as ~1024 workgroups need, into equal partitions (a
+    # multiple of 32 tokens, at least 512).
+    assert f(256, 40, 40, 128, 16, 4160, "f16", -1) == 0     # 10240 rows: whole contexts
+    assert f(64, 32, 32, 128, 16, 2048, "bf16", -1) == 0     # 2048 rows
+    # 16 sequences x 8 KV heads (MFMA rows of 8 query heads): 8 partitions of 4096 tokens.
+    assert f(16, 64, 8, 128, 16, 32768, "bf16", -1) == 16 * 64 * 8 * 130 * 4
+    # The same shape in fp32 runs one VALU workgroup per query head: 1024 rows, no split.
+    assert f(16, 64, 8, 128, 16, 32768, "f32", -1) == 0
+    # Few rows, short contexts: at most one partition per 512 tokens.
+    assert f(1, 4, 4, 128, 16, 1500, "f16", -1) == 1 * 4 * 3 * 130 * 4
+    # 32803 tokens in 8 partitions: ceil(32803 / 8) = 4101 -> 4128 tokens each, still 8.
+    assert f(16, 64, 8, 128, 16, 32803, "bf16", -1) == 16 * 64 * 8 * 130 * 4
 
 
 def test_cache_op_validation():
