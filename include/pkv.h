@@ -124,6 +124,12 @@ pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id);
 pkv_status pkv_get_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
                                 int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
 
+/* For each of the n sequences seq_ids (host): the number of leading block-table entries
+ * whose block is also referenced by another sequence (a shared prefix), into out (host, n
+ * int32).  Meant as the cached_blocks hint of pkv_paged_attention_decode. */
+pkv_status pkv_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
+                                    int32_t* out);
+
 /* Length (tokens) of one sequence. */
 pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out);
 
@@ -189,6 +195,12 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * memory on the host; larger lengths are clamped to it and to
  * max_blocks_per_seq * block_size).  Table entries outside [0, num_blocks) are treated as
  * empty blocks and never dereferenced.
+ * cached_blocks (nullable, device, num_seqs int32): a cache-policy hint.  K/V blocks are
+ * streamed with non-temporal loads, which is fastest for data read once; the first
+ * cached_blocks[b] table entries of sequence b (for example a prefix shared with other
+ * sequences, see pkv_shared_prefix_blocks) are read through the caches instead, so that
+ * sequences reading the same blocks at about the same time share them.  The result does not
+ * depend on it.
  * workspace / workspace_bytes: device scratch of at least pkv_decode_workspace_bytes(...)
  * bytes, 16-byte aligned (may be NULL when that is 0); its contents need no initialisation
  * and are overwritten.
@@ -197,7 +209,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * head_dim 64 or 128 and block_size >= 8 runs on matrix cores (MFMA). */
 pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* block_tables,
-                                      const int32_t* context_lens, int32_t num_seqs,
+                                      const int32_t* context_lens, const int32_t* cached_blocks,
+                                      int32_t num_seqs,
                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                       int32_t block_size, int32_t num_blocks,
                                       int32_t max_blocks_per_seq, int32_t max_context_len,

@@ -23,6 +23,7 @@ SIGNATURES = {
     "pkv_seq_free": (c_i32, [c_vp, c_i64]),
     "pkv_get_block_tables": (c_i32, [c_vp, P_i64, c_i32, c_i32, P_i32, P_i32]),
     "pkv_seq_length": (c_i32, [c_vp, c_i64, P_i32]),
+    "pkv_shared_prefix_blocks": (c_i32, [c_vp, P_i64, c_i32, P_i32]),
     "pkv_num_free_blocks": (c_i32, [c_vp]),
     "pkv_block_refcount": (c_i32, [c_vp, c_i32]),
     "pkv_usage": (c_i32, [c_vp, P_i64, P_i64]),
@@ -30,7 +31,7 @@ SIGNATURES = {
                                       c_i32, c_i32, c_vp]),
     "pkv_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pkv_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
-    "pkv_paged_attention_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
+    "pkv_paged_attention_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,
                                            c_i32, c_i32, c_vp, c_sz, c_vp]),
 }

@@ -122,6 +122,15 @@ class PkvAlloc:
                "pkv_get_block_tables")
         return tables, lens
 
+    def pkv_shared_prefix_blocks(self, seq_ids, out=None) -> np.ndarray:
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64).reshape(-1)
+        n = ids.size
+        res = out if out is not None else np.empty(n, np.int32)
+        _check(self._lib.pkv_shared_prefix_blocks(self._h, _ptr(ids, ctypes.c_int64) if n else None,
+                                                  n, _ptr(res, ctypes.c_int32) if n else None),
+               "pkv_shared_prefix_blocks")
+        return res
+
     def pkv_seq_length(self, seq_id: int) -> int:
         out = ctypes.c_int32(0)
         _check(self._lib.pkv_seq_length(self._h, int(seq_id), ctypes.byref(out)), "pkv_seq_length")
@@ -210,9 +219,10 @@ def pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, bl
 
 def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                                max_context_len: int, scale: float, partition_size: int = -1,
-                               workspace=None):
+                               workspace=None, cached_blocks=None):
     """out/q [B, Hq, D]; caches [N, Hkv, bs, D]; block_tables [B, max_blocks] int32;
-    context_lens [B] int32; workspace: a uint8 device tensor (or None when none is needed)."""
+    context_lens [B] int32; workspace: a uint8 device tensor (or None when none is needed);
+    cached_blocks: optional [B] int32 device tensor (cache-policy hint)."""
     import torch
     nb, hq, d = q.shape
     n, hkv, bs, d2 = k_cache.shape
@@ -224,6 +234,11 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
         raise TypeError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != nb or context_lens.shape != (nb,):
         raise ValueError("table shape")
+    cached_ptr = None
+    if cached_blocks is not None:
+        if cached_blocks.dtype != torch.int32 or cached_blocks.shape != (nb,):
+            raise ValueError("cached_blocks must be int32 [num_seqs]")
+        cached_ptr = _dev(cached_blocks) if nb else None
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace), workspace.numel() * workspace.element_size()
@@ -231,7 +246,7 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
         return out
     _check(_lib.load().pkv_paged_attention_decode(
         _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
-        nb, hq, hkv, d, bs, n, block_tables.shape[1], int(max_context_len), float(scale),
-        _dtype_code(k_cache), int(partition_size), ws_ptr, ws_bytes, _stream(q)),
+        cached_ptr, nb, hq, hkv, d, bs, n, block_tables.shape[1], int(max_context_len),
+        float(scale), _dtype_code(k_cache), int(partition_size), ws_ptr, ws_bytes, _stream(q)),
         "pkv_paged_attention_decode")
     return out

@@ -195,6 +195,21 @@ pkv_status pkv_get_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int3
   return PKV_OK;
 }
 
+pkv_status pkv_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
+                                    int32_t* out) {
+  if (!a || n < 0) return PKV_ERR_INVALID_ARG;
+  if (n > 0 && (!seq_ids || !out)) return PKV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (!a->seqs.count(seq_ids[i])) return PKV_ERR_UNKNOWN_SEQ;
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence& s = a->seqs.find(seq_ids[i])->second;
+    int32_t k = 0;
+    while (k < int32_t(s.table.size()) && a->ref[s.table[k]] > 1) ++k;
+    out[i] = k;
+  }
+  return PKV_OK;
+}
+
 pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out) {
   if (!a || !len_out) return PKV_ERR_INVALID_ARG;
   auto it = a->seqs.find(seq_id);

@@ -74,6 +74,10 @@ __device__ __forceinline__ uint2 load_stream8(const char* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(v.x, v.y);
 }
+// Blocks that other sequences read at about the same time (a shared prefix) are read
+// through the caches instead.
+__device__ __forceinline__ uint4 load_cached(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 load_cached8(const char* p) { return *reinterpret_cast<const uint2*>(p); }
 
 // ---- element conversions ---------------------------------------------------------------
 template <int DT>
@@ -174,7 +178,7 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* tables;
   const int32_t* lens;
-  // partitioned mode
+  const int32_t* cached;  // nullable: leading table entries per sequence read through the caches
   float* part_o;  // [B][Hq][max_parts][D]
   float* part_m;  // [B][Hq][max_parts]   (log2 domain)
   float* part_l;  // [B][Hq][max_parts]
@@ -188,6 +192,11 @@ struct DecodeArgs {
   int32_t max_parts;
   float scale_log2;   // scale * log2(e): scores are kept in the log2 domain
 };
+
+// Number of leading table entries of sequence b to read through the caches (wave-uniform).
+__device__ __forceinline__ int cached_blocks(const DecodeArgs& a, int b) {
+  return a.cached ? uniform(a.cached[b]) : 0;
+}
 
 __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int b) {
   int n = a.lens[b];
@@ -225,13 +234,15 @@ struct Valu {
     for (int i = 0; i < VEC; ++i) s.o[i] = 0.f;
   }
 
-  // kb / vb: pool base plus this lane's (KV head, column) offset.
+  // kb / vb: pool base plus this lane's (KV head, column) offset.  cached: read this chunk
+  // through the caches (wave-uniform).
   __device__ static void chunk(const DecodeArgs& a, const int32_t* tbl, const char* kb,
                                const char* vb, size_t blk_bytes, int row, int cs, int t1,
-                               const uint4& qv, State& st) {
+                               bool cached, const uint4& qv, State& st) {
     bool need_mask = cs + CT > t1;  // wave-uniform
     uint4 kr[J], vr[J];
     bool ok[J];
+    size_t off[J];
     if constexpr (UNIFORM) {
       int ids[NBC];
 #pragma unroll
@@ -246,9 +257,7 @@ struct Valu {
         const int tok = cs + j * TPL + row;
         const bool valid = (unsigned)id < (unsigned)a.num_blocks;
         ok[j] = valid && tok < t1;
-        const size_t off = size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * ES;
-        kr[j] = load_stream(kb + off);
-        vr[j] = load_stream(vb + off);
+        off[j] = size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * ES;
       }
     } else {
       need_mask = true;  // per-lane block ids: always mask (generic path)
@@ -258,9 +267,20 @@ struct Valu {
         const int id = tok < t1 ? tbl[tok / BS] : -1;
         const bool valid = (unsigned)id < (unsigned)a.num_blocks;
         ok[j] = valid && tok < t1;
-        const size_t off = size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * ES;
-        kr[j] = load_stream(kb + off);
-        vr[j] = load_stream(vb + off);
+        off[j] = size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * ES;
+      }
+    }
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        kr[j] = load_cached(kb + off[j]);
+        vr[j] = load_cached(vb + off[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        kr[j] = load_stream(kb + off[j]);
+        vr[j] = load_stream(vb + off[j]);
       }
     }
     float s[J];
@@ -332,11 +352,14 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
   const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * V::ES;
   const uint4 qv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
                                                     (out_row + size_t(col) * V::VEC) * V::ES);
+  const int ncached = cached_blocks(a, b);
   typename V::State st;
   V::init(st);
   const int nchunks = (t1 - t0 + V::CT - 1) / V::CT;
-  for (int c = wave; c < nchunks; c += NW)
-    V::chunk(a, tbl, kb, vb, blk_bytes, row, t0 + c * V::CT, t1, qv, st);
+  for (int c = wave; c < nchunks; c += NW) {
+    const int cs = t0 + c * V::CT;
+    V::chunk(a, tbl, kb, vb, blk_bytes, row, cs, t1, cs / BS < ncached, qv, st);
+  }
 
   const int si = wave * V::TPL + row;
 #pragma unroll
@@ -429,10 +452,11 @@ struct Mfma {
     else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
   }
 
-  // kb / vb: pool base plus this KV head's offset.  cs: a multiple of 16.
+  // kb / vb: pool base plus this KV head's offset.  cs: a multiple of 16.  cached: read this
+  // chunk through the caches (wave-uniform).
   __device__ static void chunk(const DecodeArgs& a, const int32_t* tbl, const char* kb,
-                               const char* vb, size_t blk_bytes, int cs, int t1, int lane,
-                               const vec8 (&qop)[KK], State& st) {
+                               const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
+                               int lane, const vec8 (&qop)[KK], State& st) {
     const int n16 = lane & 15, g4 = lane >> 4;
     bool need_mask = cs + kMfmaChunk > t1;  // wave-uniform
     int ids[2][NBH];
@@ -444,38 +468,62 @@ struct Mfma {
         ids[hf][k] = uniform(first < t1 ? tbl[first / BS] : -1);
         need_mask |= (unsigned)ids[hf][k] >= (unsigned)a.num_blocks;
       }
-    // K rows cs + 16hf + n16, 8 elements per k-step.
-    uint4 kr[2][KK];
+    // K rows cs + 16hf + n16 (8 elements per k-step); V rows cs + 16hf + 4g4 + i, elements
+    // [E*n16, E*n16 + E).
+    const char* kp[2];
+    const char* vp[2][4];
+    bool vok[2][4];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int tok = cs + 16 * hf + n16;
       const int id = ids[hf][NBH > 1 ? n16 / BS : 0];
       const bool valid = (unsigned)id < (unsigned)a.num_blocks;
-      const char* p = kb + size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * 2;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kr[hf][kk] = load_stream(p + (32 * kk + 8 * g4) * 2);
-    }
-    // V rows cs + 16hf + 4g4 + i, elements [E*n16, E*n16 + E).
-    uint32_t vr[2][4][E / 2];
-    bool vok[2][4];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+      kp[hf] = kb + size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * 2 + 8 * g4 * 2;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * hf + 4 * g4 + i;
-        const int tok = cs + r;
-        const int id = ids[hf][NBH > 1 ? (4 * g4 + i) / BS : 0];
-        const bool valid = (unsigned)id < (unsigned)a.num_blocks;
-        vok[hf][i] = valid && tok < t1;
-        const char* p = vb + size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * 2 + E * n16 * 2;
-        if constexpr (E == 8) {
-          const uint4 w = load_stream(p);
-          vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
-        } else {
-          const uint2 w = load_stream8(p);
-          vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
+        const int tv = cs + r;
+        const int idv = ids[hf][NBH > 1 ? (4 * g4 + i) / BS : 0];
+        const bool vv = (unsigned)idv < (unsigned)a.num_blocks;
+        vok[hf][i] = vv && tv < t1;
+        vp[hf][i] = vb + size_t(vv ? idv : 0) * blk_bytes + size_t(tv % BS) * D * 2 + E * n16 * 2;
+      }
+    }
+    uint4 kr[2][KK];
+    uint32_t vr[2][4][E / 2];
+    if (cached) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kr[hf][kk] = load_cached(kp[hf] + 32 * kk * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (E == 8) {
+            const uint4 w = load_cached(vp[hf][i]);
+            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
+          } else {
+            const uint2 w = load_cached8(vp[hf][i]);
+            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
+          }
         }
       }
+    } else {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kr[hf][kk] = load_stream(kp[hf] + 32 * kk * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (E == 8) {
+            const uint4 w = load_stream(vp[hf][i]);
+            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
+          } else {
+            const uint2 w = load_stream8(vp[hf][i]);
+            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
+          }
+        }
+      }
+    }
     // S = K . Q^T for both halves.
     float4_t s[2];
 #pragma unroll
@@ -577,10 +625,14 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
   typename M::vec8 qop[M::KK];
   M::load_q(a, q_row0, nh, lane, qop);
+  const int ncached = cached_blocks(a, b);
   typename M::State st;
   M::init(st);
   const int nchunks = (t1 - t0 + kMfmaChunk - 1) / kMfmaChunk;
-  for (int c = wave; c < nchunks; c += NW) M::chunk(a, tbl, kb, vb, blk_bytes, t0 + c * kMfmaChunk, t1, lane, qop, st);
+  for (int c = wave; c < nchunks; c += NW) {
+    const int cs = t0 + c * kMfmaChunk;
+    M::chunk(a, tbl, kb, vb, blk_bytes, cs, t1, cs / BS < ncached, lane, qop, st);
+  }
   st.l = xor_sum_16_32(st.l);  // m already agrees across the four lane groups
 
   float* mo = smem;                       // [NW][16][D]
@@ -876,7 +928,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
 
 pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* block_tables,
-                                      const int32_t* context_lens, int32_t num_seqs,
+                                      const int32_t* context_lens, const int32_t* cached_blocks,
+                                      int32_t num_seqs,
                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                       int32_t block_size, int32_t num_blocks,
                                       int32_t max_blocks_per_seq, int32_t max_context_len,
@@ -919,6 +972,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
   a.v_cache = v_cache;
   a.tables = block_tables;
   a.lens = context_lens;
+  a.cached = cached_blocks;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = group;

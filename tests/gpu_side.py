@@ -103,7 +103,11 @@ class GpuState:
         t, l = self.alloc.pkv_get_block_tables(seqs, max_blocks)
         return t, l
 
-    def decode(self, step=0, partition_size=-1, q=None, tables=None, lens=None, max_ctx=None):
+    def shared_prefix_blocks(self):
+        return self.alloc.pkv_shared_prefix_blocks(list(range(self.w.batch)))
+
+    def decode(self, step=0, partition_size=-1, q=None, tables=None, lens=None, max_ctx=None,
+               cached=None):
         c = self.w.cfg
         if tables is None:
             tables, lens = self.tables()
@@ -115,8 +119,11 @@ class GpuState:
         nbytes = pkv.pkv_decode_workspace_bytes(q.shape[0], q.shape[1], c.num_kv_heads, c.head_dim,
                                                 c.block_size, max(mc, 1), c.dtype, partition_size)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=self.device) if nbytes else None
+        cb = None
+        if cached is not None:
+            cb = torch.from_numpy(np.ascontiguousarray(cached, dtype=np.int32)).to(self.device)
         pkv.pkv_paged_attention_decode(out, q, self.k_cache, self.v_cache, t, l, mc, c.scale,
-                                       partition_size, ws)
+                                       partition_size, ws, cb)
         return out
 
 

@@ -48,13 +48,13 @@ MIS = ctypes.c_void_p(0x100008)    # misaligned
 
 
 def decode(**kw):
-    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, lens=FAKE, nseq=2, hq=4, hkv=4,
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, lens=FAKE, cached=None, nseq=2, hq=4, hkv=4,
                 d=128, bs=16, nblocks=100, maxb=8, maxctx=128, scale=0.1, dtype=1, part=-1,
                 ws=None, wsb=0, stream=None)
     args.update(kw)
     a = args
     return lib().pkv_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["tables"],
-                                            a["lens"], a["nseq"], a["hq"], a["hkv"], a["d"],
+                                            a["lens"], a["cached"], a["nseq"], a["hq"], a["hkv"], a["d"],
                                             a["bs"], a["nblocks"], a["maxb"], a["maxctx"],
                                             a["scale"], a["dtype"], a["part"], a["ws"],
                                             a["wsb"], a["stream"])

@@ -62,6 +62,14 @@ def same_state(o, c):
         tc, lc = c.pkv_get_block_tables(seqs, mb)
         to, lo = o.block_tables(seqs, mb)
         assert tc.tolist() == to and lc.tolist() == lo
+        # Leading table entries that another sequence also references (the decode hint).
+        shared = []
+        for s in seqs:
+            k = 0
+            while k < len(o.tables[s]) and o.ref[o.tables[s][k]] > 1:
+                k += 1
+            shared.append(k)
+        assert c.pkv_shared_prefix_blocks(seqs).tolist() == shared
     assert c.pkv_usage() == o.usage()
 
 

@@ -147,6 +147,29 @@ def test_shared_blocks_equal_duplicated_blocks():
     assert torch.equal(shared, dup)
 
 
+@pytest.mark.parametrize("name,overrides", [
+    ("shared_prefix_bs16_cow", dict(batch=5, num_blocks=512)),
+    ("shared_prefix_bs8", dict(batch=4, num_blocks=1024)),
+    ("gqa_long", dict(batch=2, lengths=("fixed", (3000, 777)), num_blocks=300)),
+    ("llama7b", dict(batch=5, num_blocks=700)),
+])
+def test_cache_hint_does_not_change_results(name, overrides):
+    """Reading some blocks through the caches is a policy hint only: bit-identical output."""
+    cfg = W.get_config(name, **overrides)
+    w = W.make_workload(cfg, device="cuda")
+    g = gpu_side.build(w)
+    shared = g.shared_prefix_blocks()
+    if cfg.prefix_len:
+        assert shared.min() >= (cfg.prefix_len - cfg.block_size) // cfg.block_size
+    rng = np.random.default_rng(1)
+    hints = [shared, np.full(w.batch, 1 << 20, np.int32),
+             rng.integers(-3, 40, size=w.batch).astype(np.int32)]
+    for p in (-1, 0, 64):
+        ref = g.decode(partition_size=p)
+        for hint in hints:
+            assert torch.equal(g.decode(partition_size=p, cached=hint), ref), (p, hint)
+
+
 def test_empty_context_and_invalid_table_entries():
     cfg = W.get_config("llama7b", batch=4, num_blocks=600, num_q_heads=8, num_kv_heads=8)
     w, g, o = both("llama7b", batch=4, num_blocks=600, num_q_heads=8, num_kv_heads=8)
