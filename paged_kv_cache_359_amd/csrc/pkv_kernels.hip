@@ -44,11 +44,16 @@ constexpr int elt_size(int dt) { return dt == DT_F32 ? 4 : 2; }
 
 // ---- work geometry shared by host and device ---------------------------------------------
 // VALU inner loop: a lane holds 16 bytes of a token row, LPT lanes hold one row, a wave-wide
-// load covers TPL rows, and one chunk is CT = TPL * J tokens (J loads per lane).
+// load covers TPL rows, and one chunk is CT = TPL * J >= kValuMinChunk tokens (J loads per
+// lane for K and for V).  kValuWaves waves share one (sequence, head, partition).
+constexpr int kValuWaves = 16;
+constexpr int kValuMinChunk = 16;
 constexpr int valu_vec(int dt) { return 16 / elt_size(dt); }
 constexpr int valu_lpt(int dt, int d) { return d / valu_vec(dt); }
 constexpr int valu_tpl(int dt, int d) { return 64 / valu_lpt(dt, d); }
-constexpr int valu_j(int dt, int d) { return valu_tpl(dt, d) >= 16 ? 1 : 16 / valu_tpl(dt, d); }
+constexpr int valu_j(int dt, int d) {
+  return valu_tpl(dt, d) >= kValuMinChunk ? 1 : kValuMinChunk / valu_tpl(dt, d);
+}
 constexpr int valu_chunk_tokens(int dt, int d) { return valu_tpl(dt, d) * valu_j(dt, d); }
 // MFMA inner loop: 32 tokens per chunk (two 16-token S tiles), up to 16 query heads.
 constexpr int kMfmaChunk = 32;
@@ -169,6 +174,7 @@ __device__ __forceinline__ float xor_sum_16_32(float x) {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 
 // ---- launch parameters -------------------------------------------------------------------
 struct DecodeArgs {
@@ -311,18 +317,35 @@ struct Valu {
     }
   }
 
+  // Merges the TPL row states of a wave through cross-lane exchanges; afterwards every lane
+  // holds the wave's (m, l) and the output columns col * VEC .. + VEC of the merged state.
+  __device__ static void merge_wave(State& st) {
+    float M = st.m;
+#pragma unroll
+    for (int s = LPT; s < 64; s <<= 1) M = fmaxf(M, __shfl_xor(M, s, 64));
+    const float w = st.m == kNegInf ? 0.f : exp2_hw(st.m - M);
+    st.m = M;
+    st.l *= w;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) st.o[i] *= w;
+#pragma unroll
+    for (int s = LPT; s < 64; s <<= 1) {
+      st.l += __shfl_xor(st.l, s, 64);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) st.o[i] += __shfl_xor(st.o[i], s, 64);
+    }
+  }
 };
 
-// VALU decode: one workgroup of NW waves per (sequence, query head, partition);
-// the waves take the partition's chunks in turn and merge their NW * TPL row states through
-// LDS at the end.
+// VALU decode: one workgroup of NW waves per (sequence, query head, partition); the waves
+// take the partition's chunks in turn, merge their row states within the wave, and then the
+// NW wave states through LDS.
 template <int DT, int D, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
   using V = Valu<DT, D, BS>;
-  constexpr int NS = NW * V::TPL;  // row states per workgroup
-  __shared__ float s_o[NS][D];
-  __shared__ float s_m[NS];
-  __shared__ float s_l[NS];
+  __shared__ float s_o[NW][D];
+  __shared__ float s_m[NW];
+  __shared__ float s_l[NW];
 
   const int h = blockIdx.x;
   const int part = blockIdx.y;
@@ -361,20 +384,24 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
     V::chunk(a, tbl, kb, vb, blk_bytes, row, cs, t1, cs / BS < ncached, qv, st);
   }
 
-  const int si = wave * V::TPL + row;
+  V::merge_wave(st);
+  if (row == 0) {
 #pragma unroll
-  for (int i = 0; i < V::VEC; ++i) s_o[si][col * V::VEC + i] = st.o[i];
-  if (col == 0) {
-    s_m[si] = st.m;
-    s_l[si] = st.l;
+    for (int i = 0; i < V::VEC; ++i) s_o[wave][col * V::VEC + i] = st.o[i];
+    if (col == 0) {
+      s_m[wave] = st.m;
+      s_l[wave] = st.l;
+    }
   }
   __syncthreads();
   for (int d = tid; d < D; d += NW * 64) {
     float M = kNegInf;
-    for (int r = 0; r < NS; ++r) M = fmaxf(M, s_m[r]);
+#pragma unroll
+    for (int r = 0; r < NW; ++r) M = fmaxf(M, s_m[r]);
     float L = 0.f, O = 0.f;
     if (M != kNegInf) {
-      for (int r = 0; r < NS; ++r) {
+#pragma unroll
+      for (int r = 0; r < NW; ++r) {
         const float w = exp2_hw(s_m[r] - M);
         L += s_l[r] * w;
         O += s_o[r][d] * w;
@@ -785,10 +812,10 @@ typedef void (*kernel_fn)(DecodeArgs);
 template <int DT, int D>
 kernel_fn pick_valu_bs(int bs) {
   switch (bs) {
-    case 4: return decode_valu<DT, D, 4, 4>;
-    case 8: return decode_valu<DT, D, 8, 4>;
-    case 16: return decode_valu<DT, D, 16, 4>;
-    case 32: return decode_valu<DT, D, 32, 4>;
+    case 4: return decode_valu<DT, D, 4, kValuWaves>;
+    case 8: return decode_valu<DT, D, 8, kValuWaves>;
+    case 16: return decode_valu<DT, D, 16, kValuWaves>;
+    case 32: return decode_valu<DT, D, 32, kValuWaves>;
   }
   return nullptr;
 }
@@ -997,7 +1024,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
   const dim3 grid{unsigned(rows), unsigned(max_parts), unsigned(num_seqs)};
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k, grid, dim3(mfma ? 256 : 64 * kValuWaves), 0, st, a);
   if (launch_status("paged_attention_decode") != PKV_OK) return PKV_ERR_HIP;
   if (max_parts > 1) {
     hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(128), 0, st, a);
