@@ -50,8 +50,9 @@ def test_full_size_sampled(name):
         assert torch.equal(g.k_cache[blk, :, t % bs, :], k[0])
         assert torch.equal(g.v_cache[blk, :, t % bs, :], v[0])
 
-    out = g.decode(partition_size=-1)
-    assert bool(torch.isfinite(out).all())
+    # The automatic split the benchmark times; the long-context GQA workload also in the
+    # 512-token partitions its description names.
+    outs = {p: g.decode(partition_size=p) for p in ([-1, 512] if name == "gqa_long" else [-1])}
     order = np.argsort(w.lengths)
     picks = {(int(order[0]), 0), (int(order[-1]), cfg.num_q_heads - 1)}
     while len(picks) < 24:
@@ -65,6 +66,8 @@ def test_full_size_sampled(name):
         kk = oracle.to_f64(oracle.bits_of(k[:, g_].cpu(), dt), dt)
         vv = oracle.to_f64(oracle.bits_of(v[:, g_].cpu(), dt), dt)
         ref = oracle.attention_contiguous(q[b, h], kk, vv, cfg.scale)
-        err = check(out[b, h].double().cpu().numpy(), ref, dt, f"b={b} h={h} ctx={n}")
-        worst = max(worst, err)
+        for p, out in outs.items():
+            assert bool(torch.isfinite(out[b, h]).all())
+            err = check(out[b, h].double().cpu().numpy(), ref, dt, f"p={p} b={b} h={h} ctx={n}")
+            worst = max(worst, err)
     print(f"  worst sampled max abs err {worst:.3g}", flush=True)

@@ -57,7 +57,7 @@ REDUCED = [
     ("tiny", {}, [-1, 0, 16]),
     ("llama7b", dict(batch=6, num_blocks=1024), [-1, 0, 256]),
     ("llama13b", dict(batch=8, num_blocks=2048, steps=1), [-1, 0, 128]),
-    ("gqa_long", dict(batch=2, lengths=("fixed", (4100, 999)), num_blocks=400), [-1, 0, 1024]),
+    ("gqa_long", dict(batch=2, lengths=("fixed", (4100, 999)), num_blocks=400), [-1, 0, 512, 1024]),
     ("shared_prefix_bs8_cow", dict(batch=5, num_blocks=1024), [-1, 0, 64]),
     ("shared_prefix_bs16_cow", dict(batch=5, num_blocks=512), [-1, 32]),
     ("shared_prefix_bs32_cow", dict(batch=5, num_blocks=256), [-1, 0, 32]),
