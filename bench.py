@@ -6,6 +6,10 @@ One step = one pass of the whole paged decode path over the batch:
   GPU:  copy-on-write block copies (when any), reshape_and_cache of the new K/V, paged
         decode attention, partition merge.
 Inputs (queries, the new tokens' K/V, the existing cache) are resident in HBM before timing.
+Steps are pipelined the way an engine would run them: step s's uploads, copies and cache
+write run on a second stream while step s - 1 decodes (--serial turns this off).  --check
+saves every step's output and afterwards re-decodes each step from the final tables on one
+stream, requiring bit-identical results.
 
 Prints one JSON line.  ``value`` is the whole step's logical KV throughput (bytes of K and V
 that the batch attends to, per second); ``roofline`` rates the decode kernels alone, timed
@@ -61,6 +65,11 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cache-hint", action="store_true",
                     help="stream every block (no cached_blocks hint for shared prefixes)")
+    ap.add_argument("--serial", action="store_true",
+                    help="run every step's uploads and cache write on the decode stream "
+                         "(no overlap with the previous step's decode)")
+    ap.add_argument("--check", action="store_true",
+                    help="verify every timed step's output against a serial re-decode")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (scales HBM counters)")
     return ap.parse_args()
@@ -205,41 +214,58 @@ def main():
                   done=torch.cuda.Event()) for _ in range(2)]
     for st in stage:
         st["done"].record()
-    slots_d = torch.empty(B, dtype=torch.int64, device=dev)
-    pairs_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
-    tables_d = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
-    lens_d = torch.empty(B, dtype=torch.int32, device=dev)
-    cached_d = None if args.no_cache_hint else torch.empty(B, dtype=torch.int32, device=dev)
+    # Double-buffered device copies of the same: step s fills set s % 2 on a side stream
+    # (uploads, copy-on-write copies, cache write) while the decode of step s - 1 still reads
+    # the other set.  Step s's writes touch only its new slots and fresh copy-on-write blocks,
+    # none of which the decode of step s - 1 reads.
+    dset = [dict(slots=torch.empty(B, dtype=torch.int64, device=dev),
+                 pairs=torch.empty((B, 2), dtype=torch.int32, device=dev),
+                 tables=torch.empty((B, max_blocks), dtype=torch.int32, device=dev),
+                 lens=torch.empty(B, dtype=torch.int32, device=dev),
+                 cached=None if args.no_cache_hint else torch.empty(B, dtype=torch.int32, device=dev),
+                 read=torch.cuda.Event(), ready=torch.cuda.Event()) for _ in range(2)]
     stream = torch.cuda.current_stream(dev)
+    side = stream if args.serial else torch.cuda.Stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(total_steps)]
     kv_per_token = 2 * c.num_kv_heads * c.head_dim * c.dsize
     step_bytes = [kv_per_token * int(np.sum(w.lengths + s)) for s in range(total_steps)]
+    host_s = [0.0]
+    saved = [] if args.check else None
 
     def step(s):
-        st = stage[s % 2]
-        st["done"].synchronize()  # the copies that last read this staging set are finished
+        st, ds = stage[s % 2], dset[s % 2]
+        st["done"].synchronize()  # the uploads that last read this staging set are finished
+        h0 = time.perf_counter()
         sl, pr = st["slots"].numpy(), st["pairs"].numpy()
         ncow = alloc.pkv_seq_append_into(ids, sl, pr)                         # a1
         alloc.pkv_get_block_tables(ids, max_blocks, st["tables"].numpy(), st["lens"].numpy())
-        if cached_d is not None:  # leading blocks shared with other sequences: read cached
+        if ds["cached"] is not None:  # leading blocks shared with other sequences: read cached
             alloc.pkv_shared_prefix_blocks(ids, st["cached"].numpy())
-        slots_d.copy_(st["slots"], non_blocking=True)                         # a2
-        tables_d.copy_(st["tables"], non_blocking=True)
-        lens_d.copy_(st["lens"], non_blocking=True)
-        if cached_d is not None:
-            cached_d.copy_(st["cached"], non_blocking=True)
-        if ncow:                                                              # a3
-            pairs_d.view(-1)[: 2 * ncow].copy_(st["pairs"][: 2 * ncow], non_blocking=True)
-        st["done"].record(stream)
-        if ncow:
-            pkv.pkv_copy_blocks(k_cache, v_cache, pairs_d[:ncow])
-        pkv.pkv_reshape_and_cache(k_new[s], v_new[s], slots_d, k_cache, v_cache)  # a4
+        host_s[0] += time.perf_counter() - h0
+        with torch.cuda.stream(side):
+            side.wait_event(ds["read"])  # the decode that last read this device set is done
+            ds["slots"].copy_(st["slots"], non_blocking=True)                 # a2
+            ds["tables"].copy_(st["tables"], non_blocking=True)
+            ds["lens"].copy_(st["lens"], non_blocking=True)
+            if ds["cached"] is not None:
+                ds["cached"].copy_(st["cached"], non_blocking=True)
+            if ncow:
+                ds["pairs"].view(-1)[: 2 * ncow].copy_(st["pairs"][: 2 * ncow], non_blocking=True)
+            st["done"].record(side)
+            if ncow:                                                          # a3
+                pkv.pkv_copy_blocks(k_cache, v_cache, ds["pairs"][:ncow])
+            pkv.pkv_reshape_and_cache(k_new[s], v_new[s], ds["slots"], k_cache, v_cache)  # a4
+            ds["ready"].record(side)
+        stream.wait_event(ds["ready"])
         ev[s][0].record(stream)
-        pkv.pkv_paged_attention_decode(out, q[s], k_cache, v_cache, tables_d, lens_d,  # a5, a6
+        pkv.pkv_paged_attention_decode(out, q[s], k_cache, v_cache, ds["tables"], ds["lens"],  # a5, a6
                                        max_len_final, c.scale, args.partition, workspace,
-                                       cached_d)
+                                       ds["cached"])
         ev[s][1].record(stream)
+        ds["read"].record(stream)
+        if saved is not None:
+            saved.append(out.clone())
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -251,12 +277,26 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
+    host_s[0] = 0.0
     t0 = time.perf_counter()
     for s in range(args.warmup, total_steps):
         step(s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
+    if saved is not None:
+        # During the timed steps tables only grow, so the final tables with each step's
+        # lengths reproduce that step's inputs exactly.
+        final = dset[(total_steps - 1) % 2]["tables"]
+        again = torch.empty_like(out)
+        for s in range(total_steps):
+            lens_s = torch.from_numpy((w.lengths + s).astype(np.int32)).to(dev)
+            pkv.pkv_paged_attention_decode(again, q[s], k_cache, v_cache, final, lens_s,
+                                           max_len_final, c.scale, args.partition, workspace)
+            if not torch.equal(again, saved[s]):
+                raise SystemExit(f"[bench] check failed at step {s}")
+        print(f"[bench] check: all {total_steps} steps bit-identical to a serial re-decode",
+              file=sys.stderr, flush=True)
 
     K = args.steps
     ms_per_step = (t1 - t0) * 1e3 / K
@@ -286,6 +326,9 @@ def main():
         "decode_kernel_tokens_per_s": round(B / (kern_avg_ms * 1e-3), 1),
         "partition_size": args.partition,
         "cache_hint": not args.no_cache_hint,
+        "step_overlap": not args.serial,
+        "checked": bool(args.check),
+        "host_ms_per_step": round(host_s[0] * 1e3 / K, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
