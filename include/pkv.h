@@ -125,8 +125,10 @@ pkv_status pkv_get_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int3
                                 int32_t max_blocks, int32_t* tables_out, int32_t* lens_out);
 
 /* For each of the n sequences seq_ids (host): the number of leading block-table entries
- * whose block is also referenced by another sequence (a shared prefix), into out (host, n
- * int32).  Meant as the cached_blocks hint of pkv_paged_attention_decode. */
+ * whose block is also referenced by another sequence, into out (host, n int32).  Requests
+ * that share a system prompt point at the same physical blocks ("PagedAttention 与 vLLM
+ * 推理加速", §3.2 (3)); this counts that shared run.  Meant as the cached_blocks hint of
+ * pkv_paged_attention_decode.  UNKNOWN_SEQ if an id is missing (out untouched). */
 pkv_status pkv_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
                                     int32_t* out);
 

@@ -1,0 +1,123 @@
+// Randomised operation sequences against the host block allocator through its C ABI, for a
+// build with AddressSanitizer and UndefinedBehaviorSanitizer (host code only).  After every
+// call it checks the allocator's invariants from the outside: free + referenced blocks =
+// pool size, reference counts equal the number of tables holding each block, and a failed
+// call changes nothing.  Exit status 0 = all checks passed.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <vector>
+
+#include "pkv.h"
+
+namespace {
+
+uint64_t rng_state = 0x9E3779B97F4A7C15ull;
+uint32_t next_u32() {  // xorshift64*
+  rng_state ^= rng_state >> 12;
+  rng_state ^= rng_state << 25;
+  rng_state ^= rng_state >> 27;
+  return uint32_t((rng_state * 0x2545F4914F6CDD1Dull) >> 32);
+}
+uint32_t below(uint32_t n) { return next_u32() % n; }
+
+int fail(const char* what, int iter) {
+  std::fprintf(stderr, "invariant violated at op %d: %s\n", iter, what);
+  return 1;
+}
+
+struct Snapshot {
+  int32_t free_blocks;
+  std::vector<int32_t> refs;
+  std::map<int64_t, std::vector<int32_t>> tables;
+  std::map<int64_t, int32_t> lens;
+};
+
+Snapshot snap(const pkv_alloc* a, int32_t nblocks, const std::vector<int64_t>& ids) {
+  Snapshot s;
+  s.free_blocks = pkv_num_free_blocks(a);
+  for (int32_t b = 0; b < nblocks; ++b) s.refs.push_back(pkv_block_refcount(a, b));
+  for (int64_t id : ids) {
+    int32_t len = 0;
+    if (pkv_seq_length(a, id, &len) != PKV_OK) continue;
+    std::vector<int32_t> row(size_t(nblocks) + 1);
+    if (pkv_get_block_tables(a, &id, 1, nblocks + 1, row.data(), nullptr) != PKV_OK) continue;
+    while (!row.empty() && row.back() == -1) row.pop_back();
+    s.tables[id] = row;
+    s.lens[id] = len;
+  }
+  return s;
+}
+
+bool same(const Snapshot& x, const Snapshot& y) {
+  return x.free_blocks == y.free_blocks && x.refs == y.refs && x.tables == y.tables && x.lens == y.lens;
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  const int iters = argc > 1 ? std::atoi(argv[1]) : 20000;
+  const std::vector<int64_t> ids = {0, 1, 2, 3, 4, 5, 6, 7};
+  for (int round = 0; round < 40; ++round) {
+    const int32_t nblocks = 1 + int32_t(below(24));
+    const int32_t bs = 1 << below(5);
+    std::vector<int32_t> order(nblocks);
+    for (int32_t i = 0; i < nblocks; ++i) order[i] = i;
+    for (int32_t i = nblocks - 1; i > 0; --i) std::swap(order[i], order[below(uint32_t(i) + 1)]);
+    pkv_alloc* a = nullptr;
+    if (pkv_alloc_create(nblocks, bs, round % 2 ? order.data() : nullptr, &a) != PKV_OK) return fail("create", -1);
+    for (int it = 0; it < iters / 40; ++it) {
+      const Snapshot before = snap(a, nblocks, ids);
+      const uint32_t op = below(5);
+      pkv_status st = PKV_OK;
+      if (op == 0) {
+        const int32_t n = int32_t(below(uint32_t(3 * bs + 2)));
+        std::vector<int64_t> slots(size_t(n) + 1);
+        st = pkv_seq_add(a, ids[below(8)], n, slots.data());
+      } else if (op == 1) {
+        st = pkv_seq_fork(a, ids[below(8)], ids[below(8)]);
+      } else if (op == 2) {
+        st = pkv_seq_free(a, ids[below(8)]);
+      } else {
+        const int32_t n = 1 + int32_t(below(4));
+        std::vector<int64_t> seqs(n);
+        for (auto& s : seqs) s = ids[below(8)];
+        std::vector<int64_t> slots(n);
+        std::vector<int32_t> pairs(2 * size_t(n));
+        int32_t ncow = -1;
+        st = pkv_seq_append(a, seqs.data(), n, slots.data(), pairs.data(), &ncow);
+        if (st == PKV_OK && (ncow < 0 || ncow > n)) return fail("cow count", it);
+      }
+      const Snapshot after = snap(a, nblocks, ids);
+      if (st != PKV_OK && !same(before, after)) return fail("failed call changed state", it);
+      // Invariants of the state after the call.
+      std::vector<int32_t> count(nblocks, 0);
+      for (const auto& kv : after.tables) {
+        const int64_t need = (after.lens.at(kv.first) + bs - 1) / bs;
+        if (int64_t(kv.second.size()) != need) return fail("table length", it);
+        for (int32_t b : kv.second) {
+          if (b < 0 || b >= nblocks) return fail("block id range", it);
+          ++count[b];
+        }
+      }
+      int32_t referenced = 0;
+      for (int32_t b = 0; b < nblocks; ++b) {
+        if (count[b] != after.refs[b]) return fail("reference count", it);
+        referenced += count[b] > 0;
+      }
+      if (referenced + after.free_blocks != nblocks) return fail("free + referenced", it);
+      int32_t shared = -1;
+      for (const auto& kv : after.tables) {
+        int64_t id = kv.first;
+        if (pkv_shared_prefix_blocks(a, &id, 1, &shared) != PKV_OK) return fail("shared query", it);
+        int32_t k = 0;
+        while (k < int32_t(kv.second.size()) && after.refs[kv.second[k]] > 1) ++k;
+        if (shared != k) return fail("shared prefix count", it);
+      }
+    }
+    pkv_alloc_destroy(a);
+  }
+  std::printf("ok\n");
+  return 0;
+}
