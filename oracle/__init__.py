@@ -10,17 +10,17 @@ Modules:
   allocator  block pool, per-sequence block tables, reference counts, copy-on-write,
              slot mapping (pure Python lists and dicts)
   cache      cache write, block copy and gather on raw bit patterns (NumPy)
-  attention  decode attention in float64 by its plain definition (NumPy)
+  attention  decode and causal prefill attention in float64 by their plain definition (NumPy)
   calc       the pages' closed forms: KV-cache size, block size, utilisation
 """
 from .allocator import (OracleAllocator, OracleError, OutOfBlocks, UnknownSeq, DuplicateSeq,
                         InvalidArg)
 from .cache import new_pool, cache_write, copy_blocks, gather, to_f64, bits_of
-from .attention import decode, attention_contiguous, softmax_weights
+from .attention import decode, prefill, attention_contiguous, softmax_weights
 from . import calc
 
 __all__ = [
     "OracleAllocator", "OracleError", "OutOfBlocks", "UnknownSeq", "DuplicateSeq", "InvalidArg",
     "new_pool", "cache_write", "copy_blocks", "gather", "to_f64", "bits_of",
-    "decode", "attention_contiguous", "softmax_weights", "calc",
+    "decode", "prefill", "attention_contiguous", "softmax_weights", "calc",
 ]

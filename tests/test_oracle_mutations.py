@@ -156,3 +156,33 @@ def test_reversed_initial_order_is_caught(monkeypatch):
 def pins_golden():
     import os
     return os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _prefill_mutant(shift_self=False, positions_from_zero=False):
+    def f(q_bits, k_pool, v_pool, tables, ctx_lens, query_start, scale, dtype, num_kv_heads=None):
+        q = ocache.to_f64(q_bits, dtype)
+        total, hq, d = q.shape
+        hkv = k_pool.shape[1]
+        out = np.zeros((total, hq, d))
+        for b in range(len(ctx_lens)):
+            r0, r1 = int(query_start[b]), int(query_start[b + 1])
+            n, ctx = r1 - r0, int(ctx_lens[b])
+            for g in range(hkv):
+                k = ocache.to_f64(ocache.gather(k_pool, tables[b], ctx, g), dtype)
+                v = ocache.to_f64(ocache.gather(v_pool, tables[b], ctx, g), dtype)
+                for h in range(g * (hq // hkv), (g + 1) * (hq // hkv)):
+                    for i in range(n):
+                        pos = i if positions_from_zero else ctx - n + i
+                        end = pos if shift_self else pos + 1
+                        out[r0 + i, h] = oatt.attention_contiguous(q[r0 + i, h], k[:end], v[:end], scale)
+        return out
+    return f
+
+
+@pytest.mark.parametrize("kw", [dict(shift_self=True), dict(positions_from_zero=True)])
+def test_prefill_mistakes_are_caught(monkeypatch, kw):
+    monkeypatch.setattr(oracle, "prefill", _prefill_mutant(**kw))
+    with pytest.raises(FAIL):
+        pins.test_prefill_on_cached_context_equals_masked_sdpa()
+    with pytest.raises(FAIL):
+        pins.test_prefill_brute_force_tiny()

@@ -418,3 +418,110 @@ def test_block_larger_than_context_is_contiguous():
                                               k[:, h].astype(np.float64),
                                               v[:, h].astype(np.float64), 0.4)
             assert np.array_equal(out[b, h], ref)
+
+
+# --------------------------------------------------------------------------------------
+# Prefill: several new tokens per sequence, each attending causally to the cache
+# --------------------------------------------------------------------------------------
+def paged_prefill(q, kv, n_new, bs, nblocks, order, scale):
+    """q [sum(n_new), Hq, D] f32; kv[b] = (k, v) [ctx_b, Hkv, D] f32, the whole cache of
+    sequence b after the write; its newest n_new[b] tokens are the queries."""
+    a = oracle.OracleAllocator(nblocks, bs, order)
+    hkv, d = kv[0][0].shape[1:]
+    kp = oracle.new_pool(nblocks, hkv, bs, d, "f32")
+    vp = oracle.new_pool(nblocks, hkv, bs, d, "f32")
+    for b, (k, v) in enumerate(kv):
+        slots = a.add(b, k.shape[0])
+        oracle.cache_write(kp, k.view(np.uint32), slots)
+        oracle.cache_write(vp, v.view(np.uint32), slots)
+    mb = max(len(t) for t in a.tables.values()) or 1
+    tables, lens = a.block_tables(range(len(kv)), mb)
+    qs = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int64)
+    return oracle.prefill(q.view(np.uint32), kp, vp, tables, lens, qs, scale, "f32"), qs
+
+
+def sdpa_masked_f64(q, k, v, scale, mask=None, causal=False, gqa=False):
+    """torch SDPA in float64 on the CPU: q [n, Hq, D], k/v [ctx, Hkv, D] -> [n, Hq, D]."""
+    qq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kk = torch.from_numpy(k).permute(1, 0, 2)[None].contiguous()
+    vv = torch.from_numpy(v).permute(1, 0, 2)[None].contiguous()
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=m, is_causal=causal,
+                                                         scale=scale, enable_gqa=gqa)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def prefill_case(seed, ctx_list, n_list, hq, hkv, d):
+    rng = np.random.default_rng(seed)
+    kv = [(rng.standard_normal((c, hkv, d)).astype(np.float32),
+           rng.standard_normal((c, hkv, d)).astype(np.float32)) for c in ctx_list]
+    q = rng.standard_normal((sum(n_list), hq, d)).astype(np.float32)
+    return q, kv
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (8, 2)])
+def test_prefill_of_a_fresh_prompt_equals_causal_sdpa(hq, hkv):
+    """A prompt with no earlier context: row i sees tokens 0..i, torch's is_causal."""
+    ctx = [13, 1, 40]
+    q, kv = prefill_case(3, ctx, ctx, hq, hkv, 16)
+    out, qs = paged_prefill(q, kv, ctx, 4, 40, np.random.default_rng(5).permutation(40), 0.3)
+    for b, (k, v) in enumerate(kv):
+        ref = sdpa_masked_f64(q[qs[b]:qs[b + 1]].astype(np.float64), k.astype(np.float64),
+                              v.astype(np.float64), 0.3, causal=True, gqa=hq != hkv)
+        np.testing.assert_allclose(out[qs[b]:qs[b + 1]], ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_on_cached_context_equals_masked_sdpa():
+    """New tokens on top of cached context: row i of n sits at ctx - n + i (explicit mask)."""
+    ctx, n_new = [37, 9, 64], [5, 9, 16]
+    q, kv = prefill_case(4, ctx, n_new, 6, 3, 8)
+    out, qs = paged_prefill(q, kv, n_new, 8, 20, None, 0.5)
+    for b, (k, v) in enumerate(kv):
+        c, n = ctx[b], n_new[b]
+        mask = np.arange(c)[None, :] <= (c - n + np.arange(n))[:, None]
+        ref = sdpa_masked_f64(q[qs[b]:qs[b + 1]].astype(np.float64), k.astype(np.float64),
+                              v.astype(np.float64), 0.5, mask=mask, gqa=True)
+        np.testing.assert_allclose(out[qs[b]:qs[b + 1]], ref, rtol=0, atol=1e-12)
+
+
+def test_chunked_prefill_equals_one_shot():
+    """Splitting a sequence's new tokens into chunks processed one after another (each chunk
+    seeing the cache as it stands after its own write) gives the same rows."""
+    ctx, n = 50, 30
+    q, kv = prefill_case(6, [ctx], [n], 4, 4, 8)
+    whole, _ = paged_prefill(q, kv, [n], 4, 16, None, 0.35)
+    k, v = kv[0]
+    rows = []
+    for lo, hi in ((0, 7), (7, 23), (23, 30)):
+        c = ctx - n + hi  # cache length after this chunk's write
+        part, _ = paged_prefill(q[lo:hi], [(k[:c].copy(), v[:c].copy())], [hi - lo], 4, 16, None, 0.35)
+        rows.append(part)
+    assert np.array_equal(np.concatenate(rows), whole)
+
+
+def test_prefill_brute_force_tiny():
+    """Python loops and math.exp, token by token, one head."""
+    rng = np.random.default_rng(8)
+    ctx, n, d = 6, 3, 4
+    k = rng.standard_normal((ctx, 1, d)).astype(np.float32)
+    v = rng.standard_normal((ctx, 1, d)).astype(np.float32)
+    q = rng.standard_normal((n, 1, d)).astype(np.float32)
+    out, _ = paged_prefill(q, [(k, v)], [n], 2, 4, [3, 0, 2, 1], 0.7)
+    for i in range(n):
+        pos = ctx - n + i
+        s = [0.7 * sum(float(q[i, 0, e]) * float(k[t, 0, e]) for e in range(d)) for t in range(pos + 1)]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        ref = [sum(w[t] * float(v[t, 0, e]) for t in range(pos + 1)) / sum(w) for e in range(d)]
+        np.testing.assert_allclose(out[i, 0], ref, rtol=0, atol=1e-12)
+
+
+def test_last_prefill_row_equals_decode():
+    """The newest row of a prefill is the decode of that sequence at the same length."""
+    ctx = [21, 8]
+    q, kv = prefill_case(9, ctx, [5, 8], 4, 2, 16)
+    out, qs = paged_prefill(q, kv, [5, 8], 4, 20, None, 0.25)
+    last = np.stack([q[qs[b + 1] - 1] for b in range(2)])
+    dec = paged(last, kv, 4, 20, None, 0.25)
+    for b in range(2):
+        np.testing.assert_array_equal(out[qs[b + 1] - 1], dec[b])
