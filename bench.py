@@ -28,6 +28,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_359_amd", "csrc", "pkv_kernels.hip")
 
@@ -139,6 +140,126 @@ def cpu_baseline(w, budget_s):
                       f"{c.num_q_heads} heads), median of {len(times)} runs"}
 
 
+def prefill_flops(cfg, lengths, n_new):
+    """Causal attention flops of one prefill step: q.k and p.v, 2*D each, per (row, key) pair
+    and query head; new token i of n sees ctx - n + i + 1 keys."""
+    pairs = sum(int(n) * (int(c) - int(n)) + int(n) * (int(n) + 1) // 2 for c, n in zip(lengths, n_new))
+    return 4.0 * cfg.head_dim * cfg.num_q_heads * pairs
+
+
+def main_prefill(args, cfg):
+    """One step = the whole prefill path for the batch's chunk: fork each sequence's cached
+    context (a template sequence), extend the fork by its new tokens (C++ allocator: new
+    blocks, copy-on-write of a partly filled shared last block), upload tables/lengths/
+    slots, copy blocks, write the chunk's K/V, causal paged prefill, free the forks."""
+    import torch
+    import workloads as W
+    import paged_kv_cache_359_amd as pkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    c = cfg
+    print(f"[bench] building {c.name}: {c.batch} sequences", file=sys.stderr, flush=True)
+    w = W.make_workload(c, device=dev)
+    B, bs = w.batch, c.block_size
+    alloc = pkv.PkvAlloc(c.num_blocks, bs, w.free_order)
+    shape = (c.num_blocks, c.num_kv_heads, bs, c.head_dim)
+    k_cache = torch.zeros(shape, dtype=c.torch_dtype, device=dev)
+    v_cache = torch.zeros(shape, dtype=c.torch_dtype, device=dev)
+    # Templates 0..B-1 hold each sequence's cached context; forks B..2B-1 are prefilled.
+    for b in range(B):
+        n0 = int(w.lengths[b] - w.n_new[b])
+        slots = alloc.pkv_seq_add(b, n0)
+        if n0:
+            k, v = w.token_kv(b, 0, n0)
+            pkv.pkv_reshape_and_cache(k.contiguous(), v.contiguous(), torch.from_numpy(slots).to(dev),
+                                      k_cache, v_cache)
+    qs = w.query_start
+    T = int(qs[-1])
+    rows = np.concatenate([np.arange(int(w.lengths[b] - w.n_new[b]), int(w.lengths[b])) for b in range(B)])
+    idx = torch.from_numpy(np.concatenate([w.tok_offsets[b] + np.arange(int(w.lengths[b] - w.n_new[b]), int(w.lengths[b]))
+                                           for b in range(B)])).to(dev)
+    k_new = w.k_tok.index_select(0, idx).contiguous()
+    v_new = w.v_tok.index_select(0, idx).contiguous()
+    del rows
+    max_blocks = -(-int(w.lengths.max()) // bs)
+    out = torch.empty_like(w.q)
+    forks = np.arange(B, 2 * B, dtype=np.int64)
+    h_slots = torch.empty(T, dtype=torch.int64, pin_memory=True)
+    h_pairs = torch.empty(2 * B, dtype=torch.int32, pin_memory=True)
+    h_tables = torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True)
+    h_lens = torch.empty(B, dtype=torch.int32, pin_memory=True)
+    d_slots = torch.empty(T, dtype=torch.int64, device=dev)
+    d_pairs = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    d_tables = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
+    d_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    d_qs = torch.from_numpy(qs.astype(np.int32)).to(dev)
+    max_q = int(w.n_new.max())
+    max_ctx = int(w.lengths.max())
+    stream = torch.cuda.current_stream(dev)
+    total_steps = args.warmup + args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(total_steps)]
+
+    def step(s):
+        sl, pr = h_slots.numpy(), h_pairs.numpy()
+        ncow = 0
+        for b in range(B):
+            alloc.pkv_seq_fork(b, B + b)
+            sb, pb = alloc.pkv_seq_extend(B + b, int(w.n_new[b]))
+            sl[qs[b]:qs[b + 1]] = sb
+            pr[2 * ncow: 2 * ncow + pb.size] = pb.reshape(-1)
+            ncow += pb.shape[0]
+        alloc.pkv_get_block_tables(forks, max_blocks, h_tables.numpy(), h_lens.numpy())
+        d_slots.copy_(h_slots, non_blocking=True)
+        d_tables.copy_(h_tables, non_blocking=True)
+        d_lens.copy_(h_lens, non_blocking=True)
+        if ncow:
+            d_pairs.view(-1)[: 2 * ncow].copy_(h_pairs[: 2 * ncow], non_blocking=True)
+            pkv.pkv_copy_blocks(k_cache, v_cache, d_pairs[:ncow])
+        pkv.pkv_reshape_and_cache(k_new, v_new, d_slots, k_cache, v_cache)
+        ev[s][0].record(stream)
+        pkv.pkv_paged_attention_prefill(out, w.q, k_cache, v_cache, d_tables, d_lens, d_qs,
+                                        max_q, max_ctx, c.scale)
+        ev[s][1].record(stream)
+        stream.synchronize()  # the staging buffers and the forks are reused next step
+        for b in range(B):
+            alloc.pkv_seq_free(B + b)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total_steps):
+        step(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    K = args.steps
+    ms_per_step = (t1 - t0) * 1e3 / K
+    kern_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, total_steps)]))
+    flops = prefill_flops(c, w.lengths, w.n_new)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[c.dtype]
+    res = {
+        "metric": "paged causal prefill attention TFLOP/s, 1 GPU",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"paged prefill, {c.name}: B={B}, Hq={c.num_q_heads}, "
+                               f"Hkv={c.num_kv_heads}, D={c.head_dim}, block={bs}, {c.dtype} KV, "
+                               f"{T} new tokens, contexts {int(w.lengths.min())}..{max_ctx}",
+                   "batch": B, "new_tokens": T, "context_tokens": int(w.lengths.sum())},
+        "prefill_kernel_ms": round(kern_ms, 5),
+        "new_tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": None,
+                     "kernel": "paged_attention_prefill", "flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -150,6 +271,8 @@ def main():
     import workloads as W
     import paged_kv_cache_359_amd as pkv
 
+    if W.get_config(args.config).new_tokens is not None:
+        return main_prefill(args, W.get_config(args.config))
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     total_steps = args.warmup + args.steps

@@ -114,6 +114,14 @@ pkv_status pkv_seq_fork(pkv_alloc* a, int64_t parent_id, int64_t child_id);
 pkv_status pkv_seq_append(pkv_alloc* a, const int64_t* seq_ids, int32_t n, int64_t* slots_out,
                           int32_t* cow_pairs_out, int32_t* n_cow_out);
 
+/* Append n >= 0 tokens to one sequence (a prefill chunk): the same as n calls of
+ * pkv_seq_append with seq_id alone.  slots_out (host, n int64): the new tokens' slots in
+ * order.  cow_pairs_out (host, 2 int32): at most one (src, dst) copy-on-write pair, for the
+ * first token when the last block is shared and partly filled; *n_cow_out = 0 or 1.
+ * All-or-nothing: OUT_OF_BLOCKS leaves everything unchanged. */
+pkv_status pkv_seq_extend(pkv_alloc* a, int64_t seq_id, int32_t n, int64_t* slots_out,
+                          int32_t* cow_pairs_out, int32_t* n_cow_out);
+
 /* End a sequence: each of its blocks loses a reference; blocks with none left return to
  * the pool in logical order (so its last block is the next one handed out). */
 pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id);
@@ -218,6 +226,31 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
                                       int32_t max_blocks_per_seq, int32_t max_context_len,
                                       float scale, pkv_dtype dtype, int32_t partition_size,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Paged causal prefill attention (a prompt, or one chunk of it, for several sequences at
+ * once).  Each new token attends to every earlier token of its sequence and to itself
+ * ("PagedAttention 与 vLLM 推理加速", §1: every new token sees all previous tokens), read
+ * through the block table as in decode.  Sequence b's new tokens are the rows
+ * query_start[b] .. query_start[b+1] - 1 of q and out ([num_tokens][num_q_heads][head_dim],
+ * the cache's element type); their K/V must already be in the cache (reshape_and_cache),
+ * so that context_lens[b] counts them: new token j of n_b sits at position
+ * context_lens[b] - n_b + j and
+ *     out[row][h] = sum_{t <= pos} softmax_t(scale * <q[row][h], K_t>) V_t,
+ * KV head h / (num_q_heads / num_kv_heads), fp32 accumulation, rounded to nearest even.
+ * query_start (device, num_seqs + 1 int32, non-decreasing, query_start[num_seqs] <=
+ * num_tokens): rows outside [0, num_tokens) are neither read nor written.
+ * max_query_len: an upper bound of the n_b (sizes the launch); max_context_len as for
+ * decode.  A token whose position would be negative (n_b > context_lens[b]) gets zeros.
+ * Supported: fp16 and bf16, head_dim 64 or 128, block_size 8, 16 or 32 (matrix cores);
+ * other shapes return PKV_ERR_UNSUPPORTED.  Enqueued on stream; no workspace. */
+pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, const int32_t* query_start,
+                                       int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_query_len, int32_t max_context_len, float scale,
+                                       pkv_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

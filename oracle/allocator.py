@@ -25,6 +25,8 @@ Readings where the pages leave a choice open (each also listed in the design not
     and gives up one reference to the old block; a sequence that finds count == 1 writes in
     place.  The slot of the appended token is ``table[-1] * block_size + length %
     block_size``.
+  * ``extend`` (several new tokens of one sequence, as a prefill chunk brings) is defined as
+    that many single-token appends in a row.
   * Every call either succeeds completely or changes nothing.
 """
 from __future__ import annotations
@@ -137,6 +139,25 @@ class OracleAllocator:
                     pairs.append((old, new))
                 slots.append(self._slot(s))
                 self.lens[s] += 1
+        except OutOfBlocks:
+            self._restore(snap)
+            raise
+        return slots, pairs
+
+    def extend(self, seq, n: int):
+        """``n`` new tokens for one sequence (a prefill chunk): the same as ``n`` calls of
+        ``append([seq])`` in a row, all or nothing.  Returns (slots, cow_pairs)."""
+        if seq not in self.tables:
+            raise UnknownSeq(seq)
+        if n < 0:
+            raise InvalidArg("n must be >= 0")
+        snap = self._snapshot()
+        slots, pairs = [], []
+        try:
+            for _ in range(n):
+                s, p = self.append([seq])
+                slots += s
+                pairs += p
         except OutOfBlocks:
             self._restore(snap)
             raise

@@ -20,6 +20,7 @@ SIGNATURES = {
     "pkv_seq_add": (c_i32, [c_vp, c_i64, c_i32, P_i64]),
     "pkv_seq_fork": (c_i32, [c_vp, c_i64, c_i64]),
     "pkv_seq_append": (c_i32, [c_vp, P_i64, c_i32, P_i64, P_i32, P_i32]),
+    "pkv_seq_extend": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, P_i32]),
     "pkv_seq_free": (c_i32, [c_vp, c_i64]),
     "pkv_get_block_tables": (c_i32, [c_vp, P_i64, c_i32, c_i32, P_i32, P_i32]),
     "pkv_seq_length": (c_i32, [c_vp, c_i64, P_i32]),
@@ -34,6 +35,9 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,
                                            c_i32, c_i32, c_vp, c_sz, c_vp]),
+    "pkv_paged_attention_prefill": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
+                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                            c_i32, c_f32, c_i32, c_vp]),
 }
 
 _lib = None

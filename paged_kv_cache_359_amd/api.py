@@ -107,6 +107,15 @@ class PkvAlloc:
                                         ctypes.byref(ncow)), "pkv_seq_append")
         return ncow.value
 
+    def pkv_seq_extend(self, seq_id: int, n: int):
+        slots = np.empty(max(int(n), 1), dtype=np.int64)
+        pairs = np.empty(2, dtype=np.int32)
+        ncow = ctypes.c_int32(0)
+        _check(self._lib.pkv_seq_extend(self._h, int(seq_id), int(n), _ptr(slots, ctypes.c_int64),
+                                        _ptr(pairs, ctypes.c_int32), ctypes.byref(ncow)),
+               "pkv_seq_extend")
+        return slots[: int(n)], pairs[: 2 * ncow.value].reshape(-1, 2)
+
     def pkv_seq_free(self, seq_id: int):
         _check(self._lib.pkv_seq_free(self._h, int(seq_id)), "pkv_seq_free")
 
@@ -249,4 +258,31 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
         cached_ptr, nb, hq, hkv, d, bs, n, block_tables.shape[1], int(max_context_len),
         float(scale), _dtype_code(k_cache), int(partition_size), ws_ptr, ws_bytes, _stream(q)),
         "pkv_paged_attention_decode")
+    return out
+
+
+def pkv_paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                                max_query_len: int, max_context_len: int, scale: float):
+    """out/q [T, Hq, D]; caches [N, Hkv, bs, D]; block_tables [B, max_blocks] int32;
+    context_lens [B] int32 (new tokens included); query_start [B + 1] int32."""
+    import torch
+    t, hq, d = q.shape
+    n, hkv, bs, d2 = k_cache.shape
+    nb = context_lens.shape[0]
+    if d2 != d or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == out.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    for x in (block_tables, context_lens, query_start):
+        if x.dtype != torch.int32:
+            raise TypeError("block_tables, context_lens and query_start must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != nb or query_start.shape != (nb + 1,):
+        raise ValueError("table shape")
+    if nb == 0 or t == 0:
+        return out
+    _check(_lib.load().pkv_paged_attention_prefill(
+        _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
+        _dev(query_start), nb, t, hq, hkv, d, bs, n, block_tables.shape[1], int(max_query_len),
+        int(max_context_len), float(scale), _dtype_code(k_cache), _stream(q)),
+        "pkv_paged_attention_prefill")
     return out

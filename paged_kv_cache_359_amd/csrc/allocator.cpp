@@ -165,6 +165,38 @@ pkv_status pkv_seq_append(pkv_alloc* a, const int64_t* seq_ids, int32_t n, int64
   return PKV_OK;
 }
 
+pkv_status pkv_seq_extend(pkv_alloc* a, int64_t seq_id, int32_t n, int64_t* slots_out,
+                          int32_t* cow_pairs_out, int32_t* n_cow_out) {
+  if (!a || n < 0 || !n_cow_out) return PKV_ERR_INVALID_ARG;
+  if (n > 0 && (!slots_out || !cow_pairs_out)) return PKV_ERR_INVALID_ARG;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+  Sequence& s = it->second;
+  // Only the first token can meet a shared, partly filled last block; every later one lands
+  // in a private block.
+  const bool cow = n > 0 && s.len % a->block_size != 0 && a->ref[s.table.back()] > 1;
+  const int64_t blocks_after = (int64_t(s.len) + n + a->block_size - 1) / a->block_size;
+  const int64_t need = blocks_after - int64_t(s.table.size()) + (cow ? 1 : 0);
+  if (need > int64_t(a->free_stack.size())) return PKV_ERR_OUT_OF_BLOCKS;
+  int32_t ncow = 0;
+  if (cow) {
+    const int32_t old = s.table.back();
+    const int32_t fresh = a->pop();
+    --a->ref[old];
+    s.table.back() = fresh;
+    cow_pairs_out[0] = old;
+    cow_pairs_out[1] = fresh;
+    ncow = 1;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (s.len % a->block_size == 0) s.table.push_back(a->pop());
+    slots_out[i] = a->slot_of(s);
+    ++s.len;
+  }
+  *n_cow_out = ncow;
+  return PKV_OK;
+}
+
 pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id) {
   if (!a) return PKV_ERR_INVALID_ARG;
   auto it = a->seqs.find(seq_id);

@@ -12,6 +12,9 @@
 //    Two inner loops: VALU (any head layout; DPP row reductions) and MFMA (grouped-query
 //    heads sharing one K/V tile form the columns of small matrix products).  One workgroup
 //    per (sequence, head or head group, partition); reduce_partitions merges partitions.
+//  * prefill: several new tokens of each sequence attend causally to its cached K/V (each
+//    new token sees all earlier tokens and itself, "PagedAttention 与 vLLM 推理加速", §1);
+//    the MFMA inner loop with 16 consecutive query tokens of one head as the columns.
 //
 // Pool layout: [num_blocks][num_kv_heads][block_size][head_dim] for K and for V.  One
 // (block, head) tile is block_size * head_dim contiguous elements (4 KiB for 16 tokens of
@@ -105,6 +108,31 @@ __device__ __forceinline__ void store_elt(void* base, size_t idx, float x) {
   else static_cast<__bf16*>(base)[idx] = __bf16(x);
 }
 
+// Stores N consecutive outputs (N * element size a multiple of 16 bytes, idx aligned).
+template <int DT, int N>
+__device__ __forceinline__ void store_row(void* base, size_t idx, const float (&v)[N]) {
+  constexpr int ES = elt_size(DT);
+  static_assert((N * ES) % 16 == 0, "whole 16-byte stores");
+  uint4* p = reinterpret_cast<uint4*>(static_cast<char*>(base) + idx * ES);
+#pragma unroll
+  for (int s = 0; s < N * ES / 16; ++s) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (DT == DT_F32) {
+        w[k] = __builtin_bit_cast(uint32_t, v[s * 4 + k]);
+      } else if constexpr (DT == DT_F16) {
+        const half2_t h = {_Float16(v[s * 8 + 2 * k]), _Float16(v[s * 8 + 2 * k + 1])};
+        w[k] = __builtin_bit_cast(uint32_t, h);
+      } else {
+        const bf162_t h = {__bf16(v[s * 8 + 2 * k]), __bf16(v[s * 8 + 2 * k + 1])};
+        w[k] = __builtin_bit_cast(uint32_t, h);
+      }
+    }
+    p[s] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // 16-byte dot product accumulated in fp32.  fp16/bf16 products are exact in fp32.
 template <int DT>
 __device__ __forceinline__ float dot16(const uint4& k, const uint4& q, float acc) {
@@ -185,6 +213,8 @@ struct DecodeArgs {
   const int32_t* tables;
   const int32_t* lens;
   const int32_t* cached;  // nullable: leading table entries per sequence read through the caches
+  const int32_t* query_start;  // prefill: [B + 1] first q/out row of each sequence
+  int32_t num_tokens;          // prefill: rows of q and out
   float* part_o;  // [B][Hq][max_parts][D]
   float* part_m;  // [B][Hq][max_parts]   (log2 domain)
   float* part_l;  // [B][Hq][max_parts]
@@ -480,12 +510,16 @@ struct Mfma {
   }
 
   // kb / vb: pool base plus this KV head's offset.  cs: a multiple of 16.  cached: read this
-  // chunk through the caches (wave-uniform).
+  // chunk through the caches (wave-uniform).  CAUSAL: the lane's column may only see keys at
+  // positions <= lim; lim_min is the smallest lim of the wave (wave-uniform).
+  template <bool CAUSAL = false>
   __device__ static void chunk(const DecodeArgs& a, const int32_t* tbl, const char* kb,
                                const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
-                               int lane, const vec8 (&qop)[KK], State& st) {
+                               int lane, const vec8 (&qop)[KK], State& st, int lim = 0,
+                               int lim_min = 0) {
     const int n16 = lane & 15, g4 = lane >> 4;
     bool need_mask = cs + kMfmaChunk > t1;  // wave-uniform
+    if constexpr (CAUSAL) need_mask |= cs + kMfmaChunk - 1 > lim_min;
     int ids[2][NBH];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
@@ -570,6 +604,9 @@ struct Mfma {
             sv[hf][i] = kNegInf;
 #pragma unroll
             for (int q = 0; q < E / 2; ++q) vr[hf][i][q] = 0u;  // unused slots may hold anything
+          }
+          if constexpr (CAUSAL) {
+            if (cs + 16 * hf + 4 * g4 + i > lim) sv[hf][i] = kNegInf;  // a later token
           }
         }
       }
@@ -698,6 +735,69 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
         a.part_l[pi] = L;
       }
     }
+  }
+}
+
+// =========================================================================================
+// Prefill: one workgroup of 4 waves per (query head, 64 consecutive new tokens, sequence);
+// wave w takes new tokens 16w .. 16w + 15 of the tile as the 16 columns of the MFMA inner
+// loop.  Sequence b's new tokens are q rows query_start[b] .. query_start[b+1]; with ctx_b
+// tokens cached (the new ones included), new token j sits at position ctx_b - n_b + j and
+// sees keys 0 .. that position.  Neighbouring tiles and the query heads of a group read the
+// same K/V, so K/V goes through the caches.
+// =========================================================================================
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
+  using M = Mfma<DT, D, BS>;
+  const int h = blockIdx.x;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int r0 = a.query_start[b];
+  const int n = a.query_start[b + 1] - r0;
+  const int j0 = blockIdx.y * 64 + wave * 16;  // first new token of this wave
+  if (r0 < 0 || n <= 0 || j0 >= n || r0 + j0 >= a.num_tokens) return;
+  const int nq = min(min(16, n - j0), a.num_tokens - r0 - j0);  // columns with a row
+  const int ctx = clamp_ctx(a, b);
+  const int first = ctx - n;                 // position of new token 0
+  const int j = j0 + n16;
+  const bool col = n16 < nq;
+  const int lim = col ? first + j : -1;      // last key position this column sees
+  const int lim_min = first + j0;
+  const int t1 = min(ctx, first + j0 + nq);  // keys 0 .. t1 - 1
+  const size_t row = size_t(r0 + (col ? j : j0));
+  const size_t out_idx = (row * a.num_q_heads + h) * D;
+
+  typename M::State st;
+  M::init(st);
+  if (t1 > 0) {
+    typename M::vec8 qop[M::KK];
+    const char* qp = static_cast<const char*>(a.q) + out_idx * 2;
+#pragma unroll
+    for (int kk = 0; kk < M::KK; ++kk) {
+      const uint4 w = col ? *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2) : make_uint4(0, 0, 0, 0);
+      qop[kk] = __builtin_bit_cast(typename M::vec8, w);
+    }
+    const int kvh = h / a.group;
+    const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
+    const size_t head_off = size_t(kvh) * BS * D * 2;
+    const char* kb = static_cast<const char*>(a.k_cache) + head_off;
+    const char* vb = static_cast<const char*>(a.v_cache) + head_off;
+    const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
+    const int nchunks = (t1 + kMfmaChunk - 1) / kMfmaChunk;
+    for (int c = 0; c < nchunks; ++c)
+      M::template chunk<true>(a, tbl, kb, vb, blk_bytes, c * kMfmaChunk, t1, true, lane, qop, st, lim, lim_min);
+  }
+  st.l = xor_sum_16_32(st.l);
+  if (col) {
+    float v[4 * M::E];
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+#pragma unroll
+    for (int r = 0; r < M::E; ++r)
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) v[vv * M::E + r] = st.acc[r][vv] * inv;
+    store_row<DT, 4 * M::E>(a.out, out_idx + 4 * M::E * g4, v);
   }
 }
 
@@ -846,6 +946,23 @@ kernel_fn pick_mfma(int d, int bs) {
     case 64: return pick_mfma_bs<DT, 64>(bs);
     case 128: return pick_mfma_bs<DT, 128>(bs);
   }
+  return nullptr;
+}
+
+template <int DT, int D>
+kernel_fn pick_prefill_bs(int bs) {
+  switch (bs) {
+    case 8: return prefill_mfma<DT, D, 8>;
+    case 16: return prefill_mfma<DT, D, 16>;
+    case 32: return prefill_mfma<DT, D, 32>;
+  }
+  return nullptr;
+}
+
+kernel_fn pick_prefill(pkv_dtype dt, int d, int bs) {
+  if (dt == PKV_F32) return nullptr;
+  if (d == 64) return dt == PKV_F16 ? pick_prefill_bs<DT_F16, 64>(bs) : pick_prefill_bs<DT_BF16, 64>(bs);
+  if (d == 128) return dt == PKV_F16 ? pick_prefill_bs<DT_F16, 128>(bs) : pick_prefill_bs<DT_BF16, 128>(bs);
   return nullptr;
 }
 
@@ -1031,6 +1148,51 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
     return launch_status("reduce_partitions");
   }
   return PKV_OK;
+}
+
+pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, const int32_t* query_start,
+                                       int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int32_t num_blocks, int32_t max_blocks_per_seq,
+                                       int32_t max_query_len, int32_t max_context_len, float scale,
+                                       pkv_dtype dtype, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0 || max_context_len < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return PKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
+  kernel_fn k = pick_prefill(dtype, head_dim, block_size);
+  if (!k) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
+  if (num_seqs > 65535 || (int64_t(max_query_len) + 63) / 64 > 65535) return PKV_ERR_UNSUPPORTED;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t cap = int64_t(max_blocks_per_seq) * block_size;
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.query_start = query_start;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.ctx_limit = int32_t(max_context_len < cap ? max_context_len : cap);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const dim3 grid{unsigned(num_q_heads), unsigned((max_query_len + 63) / 64), unsigned(num_seqs)};
+  clear_stale_error();
+  hipLaunchKernelGGL(k, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  return launch_status("paged_attention_prefill");
 }
 
 }  // extern "C"

@@ -79,6 +79,20 @@ class GpuState:
                 del self.lens[op[1]]
                 if log:
                     self.log.append((op, [], []))
+            elif kind == "extend":
+                flush()
+                _, seq, n = op
+                pos = self.lens[seq]
+                slots, pairs = self.alloc.pkv_seq_extend(seq, n)
+                if pairs.size:
+                    pkv.pkv_copy_blocks(self.k_cache, self.v_cache,
+                                        torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device))
+                if n:
+                    k, v = w.token_kv(seq, pos, pos + n)
+                    self._write(k, v, slots)
+                self.lens[seq] += n
+                if log:
+                    self.log.append((op, slots.tolist(), pairs.tolist()))
             else:
                 flush()
                 seqs = op[1]
@@ -127,6 +141,22 @@ class GpuState:
         return out
 
 
+    def prefill(self, q=None, query_start=None, lens=None, max_query_len=None):
+        c = self.w.cfg
+        tables, l = self.tables()
+        lens = l if lens is None else lens
+        qs = self.w.query_start if query_start is None else query_start
+        q = self.w.q if q is None else q
+        out = torch.empty_like(q)
+        t = torch.from_numpy(np.ascontiguousarray(tables)).to(self.device)
+        ld = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to(self.device)
+        qsd = torch.from_numpy(np.ascontiguousarray(qs, dtype=np.int32)).to(self.device)
+        mq = int(np.max(np.diff(qs))) if max_query_len is None else max_query_len
+        pkv.pkv_paged_attention_prefill(out, q, self.k_cache, self.v_cache, t, ld, qsd, mq,
+                                        int(np.max(lens)), c.scale)
+        return out
+
+
 def build(w: W.Workload, **kw) -> GpuState:
     st = GpuState(w, **kw)
     st.run(W.setup_ops(w))
@@ -137,4 +167,4 @@ def build(w: W.Workload, **kw) -> GpuState:
 def to_cpu(w: W.Workload) -> W.Workload:
     f = lambda t: None if t is None else t.cpu()
     return W.Workload(w.cfg, w.lengths, w.free_order, f(w.q), f(w.k_tok), f(w.v_tok),
-                      w.tok_offsets, f(w.k_prefix), f(w.v_prefix))
+                      w.tok_offsets, f(w.k_prefix), f(w.v_prefix), w.n_new)

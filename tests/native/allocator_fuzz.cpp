@@ -69,7 +69,7 @@ int main(int argc, char** argv) {
     if (pkv_alloc_create(nblocks, bs, round % 2 ? order.data() : nullptr, &a) != PKV_OK) return fail("create", -1);
     for (int it = 0; it < iters / 40; ++it) {
       const Snapshot before = snap(a, nblocks, ids);
-      const uint32_t op = below(5);
+      const uint32_t op = below(6);
       pkv_status st = PKV_OK;
       if (op == 0) {
         const int32_t n = int32_t(below(uint32_t(3 * bs + 2)));
@@ -79,6 +79,12 @@ int main(int argc, char** argv) {
         st = pkv_seq_fork(a, ids[below(8)], ids[below(8)]);
       } else if (op == 2) {
         st = pkv_seq_free(a, ids[below(8)]);
+      } else if (op == 5) {
+        const int32_t n = int32_t(below(uint32_t(2 * bs + 3)));
+        std::vector<int64_t> slots(size_t(n) + 1);
+        int32_t pairs[2] = {-1, -1}, ncow = -1;
+        st = pkv_seq_extend(a, ids[below(8)], n, slots.data(), pairs, &ncow);
+        if (st == PKV_OK && (ncow < 0 || ncow > 1)) return fail("extend cow count", it);
       } else {
         const int32_t n = 1 + int32_t(below(4));
         std::vector<int64_t> seqs(n);

@@ -47,6 +47,15 @@ class OracleState:
             elif kind == "free":
                 self.alloc.free_seq(op[1])
                 self.log.append((op, [], []))
+            elif kind == "extend":
+                _, seq, n = op
+                pos = self.alloc.lens[seq]
+                slots, pairs = self.alloc.extend(seq, n)
+                if self.cache:
+                    oracle.copy_blocks(self.k_pool, pairs)
+                    oracle.copy_blocks(self.v_pool, pairs)
+                self._write(seq, pos, pos + n, slots)
+                self.log.append((op, slots, pairs))
             elif kind == "append":
                 seqs = op[1]
                 pos = [self.alloc.lens[s] for s in seqs]
@@ -73,6 +82,14 @@ class OracleState:
         if q_bits is None:
             q_bits = oracle.bits_of(self.w.q[step], c.dtype)
         return oracle.decode(q_bits, self.k_pool, self.v_pool, tables, lens, c.scale, c.dtype)
+
+
+    def prefill(self):
+        c = self.w.cfg
+        tables, lens = self.tables()
+        q_bits = oracle.bits_of(self.w.q, c.dtype)
+        return oracle.prefill(q_bits, self.k_pool, self.v_pool, tables, lens,
+                              self.w.query_start, c.scale, c.dtype)
 
 
 def build(w: W.Workload, **kw) -> OracleState:

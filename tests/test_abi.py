@@ -167,3 +167,34 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root,
                          check=True).stdout.split()
     assert out == ["1", "1"], out
+
+
+def prefill(**kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, lens=FAKE, qs=FAKE, nseq=2, ntok=10,
+                hq=4, hkv=4, d=128, bs=16, nblocks=100, maxb=8, maxq=8, maxctx=128, scale=0.1,
+                dtype=1, stream=None)
+    args.update(kw)
+    a = args
+    return lib().pkv_paged_attention_prefill(a["out"], a["q"], a["k"], a["v"], a["tables"],
+                                             a["lens"], a["qs"], a["nseq"], a["ntok"], a["hq"],
+                                             a["hkv"], a["d"], a["bs"], a["nblocks"], a["maxb"],
+                                             a["maxq"], a["maxctx"], a["scale"], a["dtype"],
+                                             a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), 5),               # fp32: no matrix-core prefill
+    (dict(d=8), 5),
+    (dict(bs=4), 5),
+    (dict(hq=6, hkv=4), 1),
+    (dict(dtype=9), 1),
+    (dict(ntok=-1), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(qs=None), 1),
+    (dict(out=MIS), 1),
+    (dict(nseq=70000), 5),
+    (dict(ntok=0, out=None), 0),       # nothing to do
+    (dict(maxq=0, q=None), 0),
+])
+def test_prefill_validation(kw, status):
+    assert prefill(**kw) == status

@@ -30,6 +30,9 @@ def run_both(o, c, kind, *args):
         elif kind == "free":
             o.free_seq(*args)
             ro = ("ok", None)
+        elif kind == "extend":
+            s, p = o.extend(*args)
+            ro = ("ok", (list(s), [list(x) for x in p]))
         else:
             s, p = o.append(*args)
             ro = ("ok", (list(s), [list(x) for x in p]))
@@ -44,6 +47,9 @@ def run_both(o, c, kind, *args):
         elif kind == "free":
             c.pkv_seq_free(*args)
             rc = ("ok", None)
+        elif kind == "extend":
+            s, p = c.pkv_seq_extend(*args)
+            rc = ("ok", (s.tolist(), p.tolist()))
         else:
             s, p = c.pkv_seq_append(*args)
             rc = ("ok", (s.tolist(), p.tolist()))
@@ -73,7 +79,7 @@ def same_state(o, c):
     assert c.pkv_usage() == o.usage()
 
 
-ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "append", "free"]),
+ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "append", "free", "extend"]),
                          st.integers(0, 6), st.integers(0, 6), st.integers(0, 11)),
                min_size=1, max_size=80)
 
@@ -92,6 +98,8 @@ def test_random_operation_sequences(ops, bs, nblocks, seed, use_order):
             args = (x, y)
         elif kind == "free":
             args = (x,)
+        elif kind == "extend":
+            args = (x, n)
         else:
             # Mostly distinct ids; sometimes a repeated id (an error on both sides).
             ids = [x, y, (x + n) % 7] if n % 5 else [x, x]

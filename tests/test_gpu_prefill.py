@@ -1,0 +1,122 @@
+"""Paged causal prefill on the GPU against the CPU oracle, on identical seeded inputs.
+
+Bars: block tables, slots and pools bit-exact; outputs within the attention bar of
+tests/tolerance.py (5e-3 for fp16/bf16 K/V, widened only where the output type's own
+rounding exceeds it).  Pools start filled with a quiet-NaN pattern, so a masked or unused
+slot that leaked into an output would show up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_side, oracle_side
+from tests.tolerance import check
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def both(name, **overrides):
+    cfg = W.get_config(name, **overrides)
+    print(f"[case] {cfg.name} {overrides}", flush=True)
+    w = W.make_workload(cfg, device="cuda")
+    g = gpu_side.build(w)
+    o = oracle_side.build(gpu_side.to_cpu(w), fill=gpu_side.SENTINEL_BITS[cfg.dtype])
+    return w, g, o
+
+
+def check_all(w, g, o):
+    assert [(op, s, [list(p) for p in pr]) for op, s, pr in g.log] == \
+        [(op, list(s), [list(p) for p in pr]) for op, s, pr in o.log]
+    tg, lg = g.tables()
+    to, lo = o.tables()
+    assert np.array_equal(tg, to) and np.array_equal(lg, lo)
+    dt = w.cfg.dtype
+    assert np.array_equal(oracle.bits_of(g.k_cache.cpu(), dt), o.k_pool)
+    assert np.array_equal(oracle.bits_of(g.v_cache.cpu(), dt), o.v_pool)
+    out = g.prefill().double().cpu().numpy()
+    err = check(out, o.prefill(), dt, w.cfg.name)
+    print(f"  max abs err {err:.3g}", flush=True)
+
+
+REDUCED = [
+    ("prefill_llama7b", dict(batch=4, lengths=("fixed", (1, 17, 100, 300)), num_blocks=64)),
+    ("prefill_chunked_gqa", dict(batch=2, lengths=("fixed", (700, 1500)), num_blocks=160)),
+    ("prefill_chunked_gqa", dict(batch=3, lengths=("fixed", (40, 513, 600)),
+                                 new_tokens=("fixed", 33), num_blocks=160)),
+]
+
+
+@pytest.mark.parametrize("name,overrides", REDUCED, ids=["fresh", "chunk512", "chunk33"])
+def test_prefill_parity(name, overrides):
+    check_all(*both(name, **overrides))
+
+
+SHAPES = []
+for dtype in ("f16", "bf16"):
+    for d in (64, 128):
+        for bs in (8, 16, 32):
+            for hq, hkv in ((4, 4), (8, 2), (16, 1)):
+                SHAPES.append((dtype, d, bs, hq, hkv))
+
+
+@pytest.mark.parametrize("dtype,d,bs,hq,hkv", SHAPES)
+def test_prefill_shape_sweep(dtype, d, bs, hq, hkv):
+    # Ragged new-token counts around the 16-token column tiles and 64-token workgroup tiles,
+    # fresh prompts and chunks on top of cached context.
+    lengths = (1, 15, 16, 17, 64, 65, 130, 200)
+    for new in (("all",), ("fixed", 47)):
+        cfg = dict(dtype=dtype, head_dim=d, block_size=bs, num_q_heads=hq, num_kv_heads=hkv,
+                   batch=len(lengths), lengths=("fixed", lengths), new_tokens=new,
+                   num_blocks=(sum(lengths) // bs + 16) * 2)
+        check_all(*both("prefill_llama7b", **cfg))
+
+
+def test_prefill_matches_decode_kernel_on_the_last_row():
+    """The newest row of a prefill and a decode of that sequence read the same keys."""
+    w, g, o = both("prefill_chunked_gqa", batch=2, lengths=("fixed", (300, 77)), num_blocks=80)
+    out = g.prefill()
+    qs = w.query_start
+    last = torch.stack([w.q[int(qs[b + 1]) - 1] for b in range(w.batch)])
+    dec = g.decode(q=last.contiguous(), partition_size=0)
+    for b in range(w.batch):
+        check(out[int(qs[b + 1]) - 1].double().cpu().numpy(), dec[b].double().cpu().numpy(),
+              w.cfg.dtype, f"b={b}")
+
+
+@pytest.mark.parametrize("name", ["prefill_llama7b", "prefill_chunked_gqa"])
+def test_prefill_full_size_sampled(name):
+    cfg = W.get_config(name)
+    print(f"[case] full-size {name}", flush=True)
+    w = W.make_workload(cfg, device="cuda")
+    g = gpu_side.build(w)
+    o = oracle_side.OracleState(w, cache=False)
+    o.run(W.setup_ops(w))
+    o.run(W.step_ops(w))
+    for (op_g, s_g, p_g), (op_o, s_o, p_o) in zip(g.log, o.log):
+        assert op_g == op_o and s_g == list(s_o) and p_g == [list(p) for p in p_o]
+    tg, lg = g.tables()
+    to, lo = o.tables()
+    assert np.array_equal(tg, to) and np.array_equal(lg, lo)
+    out = g.prefill()
+    dt = cfg.dtype
+    q = oracle.to_f64(oracle.bits_of(w.q.cpu(), dt), dt)
+    qs = w.query_start
+    rng = np.random.default_rng(0)
+    worst = 0.0
+    for _ in range(24):
+        b = int(rng.integers(w.batch))
+        n, ctx = int(w.n_new[b]), int(w.lengths[b])
+        i = int(rng.choice([0, n - 1, int(rng.integers(n))]))
+        h = int(rng.integers(cfg.num_q_heads))
+        pos = ctx - n + i
+        k, v = w.token_kv(b, 0, pos + 1)
+        g_ = h // cfg.group
+        kk = oracle.to_f64(oracle.bits_of(k[:, g_].cpu(), dt), dt)
+        vv = oracle.to_f64(oracle.bits_of(v[:, g_].cpu(), dt), dt)
+        ref = oracle.attention_contiguous(q[qs[b] + i, h], kk, vv, cfg.scale)
+        err = check(out[qs[b] + i, h].double().cpu().numpy(), ref, dt, f"b={b} i={i} h={h}")
+        worst = max(worst, err)
+    print(f"  worst sampled max abs err {worst:.3g}", flush=True)

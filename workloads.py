@@ -54,6 +54,10 @@ class DecodeConfig:
     prefix_len: int = 0
     partition_size: int = 512
     steps: int = 1
+    # Prefill workloads: how many of each sequence's ``lengths`` tokens are new (processed
+    # as one chunk and attending causally); None for decode.  ("all",) = a fresh prompt,
+    # ("fixed", n) = a chunk of n tokens on top of cached context.
+    new_tokens: Optional[tuple] = None
 
     @property
     def group(self) -> int:
@@ -90,6 +94,14 @@ CONFIGS = {
     # LLaMA-7B attention shape: 32 heads x 128, bf16 KV, contexts uniform in [128, 2048].
     "llama7b": DecodeConfig("llama7b", 2, "bf16", 32, 32, 128, 16, 16384, 64,
                             ("uniform", 128, 2048)),
+    # Prefill (chunked prefill) workloads on the same cache layout.  LLaMA-7B attention shape,
+    # 8 fresh prompts of 256..2048 tokens.
+    "prefill_llama7b": DecodeConfig("prefill_llama7b", 6, "bf16", 32, 32, 128, 16, 2048, 8,
+                                    ("uniform", 256, 2048), new_tokens=("all",)),
+    # Grouped-query heads, a 512-token chunk of each of 4 prompts on top of 1024..4096
+    # cached tokens.
+    "prefill_chunked_gqa": DecodeConfig("prefill_chunked_gqa", 7, "bf16", 64, 8, 128, 16, 2048, 4,
+                                        ("uniform", 1536, 4608), new_tokens=("fixed", 512)),
     # LLaMA-13B attention shape: 40 heads x 128, fp16 KV, continuous-batching length mix.
     "llama13b": DecodeConfig("llama13b", 3, "f16", 40, 40, 128, 16, 16384, 256,
                              ("lognormal", 512, 1.0, 16, 4096), steps=64),
@@ -140,6 +152,18 @@ def draw_lengths(cfg: DecodeConfig) -> np.ndarray:
     return np.asarray(full[: cfg.batch], dtype=np.int64)
 
 
+def new_token_counts(cfg: DecodeConfig, lengths: np.ndarray) -> Optional[np.ndarray]:
+    """Tokens of each sequence processed by the prefill step (None for decode workloads)."""
+    if cfg.new_tokens is None:
+        return None
+    kind = cfg.new_tokens[0]
+    if kind == "all":
+        return lengths.copy()
+    if kind == "fixed":
+        return np.minimum(lengths, cfg.new_tokens[1]).astype(np.int64)
+    raise ValueError(kind)
+
+
 def draw_free_order(cfg: DecodeConfig) -> np.ndarray:
     """Seeded random permutation of the physical blocks: the order the pool hands them out."""
     rng = np.random.Generator(np.random.PCG64(seed_streams(cfg.cfg_id)[1]))
@@ -169,7 +193,9 @@ class Workload:
     ``tok_offsets[b]:tok_offsets[b+1]`` of ``k_tok``/``v_tok``; with a shared prefix those come
     after the ``prefix_len`` tokens of ``k_prefix``/``v_prefix``.  At decode step ``s`` sequence
     ``b`` appends its token number ``lengths[b] - 1 + s`` (counting the prefix) and attends to
-    ``lengths[b] + s`` tokens with query ``q[s, b]``.
+    ``lengths[b] + s`` tokens with query ``q[s, b]``.  Prefill workloads instead process the
+    newest ``n_new[b]`` of sequence b's ``lengths[b]`` tokens in one step, with queries
+    ``q[query_start[b]:query_start[b + 1]]`` ([sum(n_new), Hq, D]).
     """
 
     cfg: DecodeConfig
@@ -181,6 +207,11 @@ class Workload:
     tok_offsets: np.ndarray
     k_prefix: Optional[torch.Tensor]
     v_prefix: Optional[torch.Tensor]
+    n_new: Optional[np.ndarray] = None
+
+    @property
+    def query_start(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.n_new)]).astype(np.int64)
 
     @property
     def batch(self) -> int:
@@ -217,10 +248,14 @@ def make_workload(cfg: DecodeConfig, device="cpu") -> Workload:
     total = int(offs[-1])
     kall = draw_normal((cfg.prefix_len + total, hkv, d), ss[3], dt, device)
     vall = draw_normal((cfg.prefix_len + total, hkv, d), ss[4], dt, device)
-    q = draw_normal((cfg.steps, cfg.batch, cfg.num_q_heads, d), ss[2], dt, device)
+    n_new = new_token_counts(cfg, lengths)
+    if n_new is None:
+        q = draw_normal((cfg.steps, cfg.batch, cfg.num_q_heads, d), ss[2], dt, device)
+    else:
+        q = draw_normal((int(n_new.sum()), cfg.num_q_heads, d), ss[2], dt, device)
     p = cfg.prefix_len
     return Workload(cfg, lengths, free_order, q, kall[p:], vall[p:], offs,
-                    kall[:p] if p else None, vall[:p] if p else None)
+                    kall[:p] if p else None, vall[:p] if p else None, n_new)
 
 
 # ---------------------------------------------------------------------------------------
@@ -228,7 +263,8 @@ def make_workload(cfg: DecodeConfig, device="cpu") -> Workload:
 # then to decode: a list of request-level operations that each side replays with its own
 # allocator and cache.  Tokens written by an operation are the sequence's next tokens in
 # logical order.  ("add", seq, n): a new sequence with n tokens; ("fork", parent, child);
-# ("free", seq); ("append", [seq, ...]): one new token for each listed sequence.
+# ("free", seq); ("append", [seq, ...]): one new token for each listed sequence;
+# ("extend", seq, n): n new tokens of one sequence (a prefill chunk).
 # ---------------------------------------------------------------------------------------
 PARENT = -1  # id of the sequence that holds a shared prefix before it is forked
 
@@ -244,6 +280,9 @@ def setup_ops(w: Workload):
         own = w.lengths - cfg.prefix_len - 1
         for r in range(int(own.max()) if nb else 0):
             ops.append(("append", [b for b in range(nb) if own[b] > r]))
+    elif w.n_new is not None:
+        for b in range(nb):
+            ops.append(("add", b, int(w.lengths[b] - w.n_new[b])))
     else:
         for b in range(nb):
             ops.append(("add", b, int(w.lengths[b]) - 1))
@@ -251,5 +290,7 @@ def setup_ops(w: Workload):
 
 
 def step_ops(w: Workload):
-    """One decode step: every sequence appends the token it decodes."""
+    """One step: every sequence appends the token it decodes, or (prefill) its new chunk."""
+    if w.n_new is not None:
+        return [("extend", b, int(w.n_new[b])) for b in range(w.batch)]
     return [("append", list(range(w.batch)))]
