@@ -6,8 +6,11 @@ One step = one pass of the whole paged decode path over the batch:
   GPU:  copy-on-write block copies (when any), reshape_and_cache of the new K/V, paged
         decode attention, partition merge.
 Inputs (queries, the new tokens' K/V, the existing cache) are resident in HBM before timing.
-Steps are pipelined the way an engine would run them: step s's uploads, copies and cache
-write run on a second stream while step s - 1 decodes (--serial turns this off).  --check
+Each step runs on one stream; the device keeps the block tables and lengths, and a step
+uploads only one small packed buffer (the new slots, the positions they extend and the
+shared-prefix hint) that pkv_update_block_tables applies.  --overlap instead uploads whole
+tables on a second stream during the previous decode (four buffer sets); on some MI355X
+boxes the cross-stream waits stall for milliseconds, so it is not the default.  --check
 saves every step's output and afterwards re-decodes each step from the final tables on one
 stream, requiring bit-identical results.
 
@@ -66,9 +69,9 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cache-hint", action="store_true",
                     help="stream every block (no cached_blocks hint for shared prefixes)")
-    ap.add_argument("--serial", action="store_true",
-                    help="run every step's uploads and cache write on the decode stream "
-                         "(no overlap with the previous step's decode)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run each step's uploads and cache write on a second stream during the "
+                         "previous step's decode (whole tables uploaded per step)")
     ap.add_argument("--check", action="store_true",
                     help="verify every timed step's output against a serial re-decode")
     ap.add_argument("--calib-copy", action="store_true",
@@ -260,6 +263,69 @@ def main_prefill(args, cfg):
     print(json.dumps(res), flush=True)
 
 
+def overlapped_steps(args, alloc, ids, B, max_blocks, NBUF, k_cache, v_cache, k_new, v_new, q,
+                     out, workspace, max_len_final, c, stream, ev, host_s, saved, use_hint, dev):
+    """The --overlap step: step s's uploads, copy-on-write copies and cache write run on a
+    second stream into device set s % NBUF while step s - 1 decodes from another set.  Step
+    s's writes touch only its new slots and fresh copy-on-write blocks, none of which the
+    decode of step s - 1 reads."""
+    import torch
+    import paged_kv_cache_359_amd as pkv
+    stage = [dict(slots=torch.empty(B, dtype=torch.int64, pin_memory=True),
+                  pairs=torch.empty(2 * B, dtype=torch.int32, pin_memory=True),
+                  tables=torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True),
+                  lens=torch.empty(B, dtype=torch.int32, pin_memory=True),
+                  cached=torch.empty(B, dtype=torch.int32, pin_memory=True),
+                  done=torch.cuda.Event()) for _ in range(NBUF)]
+    for st in stage:
+        st["done"].record()
+    dset = [dict(slots=torch.empty(B, dtype=torch.int64, device=dev),
+                 pairs=torch.empty((B, 2), dtype=torch.int32, device=dev),
+                 tables=torch.empty((B, max_blocks), dtype=torch.int32, device=dev),
+                 lens=torch.empty(B, dtype=torch.int32, device=dev),
+                 cached=torch.empty(B, dtype=torch.int32, device=dev) if use_hint else None,
+                 read=torch.cuda.Event(), ready=torch.cuda.Event()) for _ in range(NBUF)]
+    side = torch.cuda.Stream(dev)
+    last = [None]
+
+    def step(s):
+        st, ds = stage[s % NBUF], dset[s % NBUF]
+        st["done"].synchronize()  # the uploads that last read this staging set are finished
+        h0 = time.perf_counter()
+        sl, pr = st["slots"].numpy(), st["pairs"].numpy()
+        ncow = alloc.pkv_seq_append_into(ids, sl, pr)
+        alloc.pkv_get_block_tables(ids, max_blocks, st["tables"].numpy(), st["lens"].numpy())
+        if ds["cached"] is not None:
+            alloc.pkv_shared_prefix_blocks(ids, st["cached"].numpy())
+        host_s[0] += time.perf_counter() - h0
+        with torch.cuda.stream(side):
+            side.wait_event(ds["read"])  # the decode that last read this device set is done
+            ds["slots"].copy_(st["slots"], non_blocking=True)
+            ds["tables"].copy_(st["tables"], non_blocking=True)
+            ds["lens"].copy_(st["lens"], non_blocking=True)
+            if ds["cached"] is not None:
+                ds["cached"].copy_(st["cached"], non_blocking=True)
+            if ncow:
+                ds["pairs"].view(-1)[: 2 * ncow].copy_(st["pairs"][: 2 * ncow], non_blocking=True)
+            st["done"].record(side)
+            if ncow:
+                pkv.pkv_copy_blocks(k_cache, v_cache, ds["pairs"][:ncow])
+            pkv.pkv_reshape_and_cache(k_new[s], v_new[s], ds["slots"], k_cache, v_cache)
+            ds["ready"].record(side)
+        stream.wait_event(ds["ready"])
+        ev[s][0].record(stream)
+        pkv.pkv_paged_attention_decode(out, q[s], k_cache, v_cache, ds["tables"], ds["lens"],
+                                       max_len_final, c.scale, args.partition, workspace,
+                                       ds["cached"])
+        ev[s][1].record(stream)
+        ds["read"].record(stream)
+        last[0] = ds["tables"]
+        if saved is not None:
+            saved.append(out.clone())
+
+    return step, (lambda: last[0])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -328,67 +394,70 @@ def main():
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, c.num_q_heads, c.head_dim), dtype=c.torch_dtype, device=dev)
     ids = np.arange(B, dtype=np.int64)
-    # Double-buffered pinned staging for what the host produces each step.
-    stage = [dict(slots=torch.empty(B, dtype=torch.int64, pin_memory=True),
-                  pairs=torch.empty(2 * B, dtype=torch.int32, pin_memory=True),
-                  tables=torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True),
-                  lens=torch.empty(B, dtype=torch.int32, pin_memory=True),
-                  cached=torch.empty(B, dtype=torch.int32, pin_memory=True),
-                  done=torch.cuda.Event()) for _ in range(2)]
-    for st in stage:
-        st["done"].record()
-    # Double-buffered device copies of the same: step s fills set s % 2 on a side stream
-    # (uploads, copy-on-write copies, cache write) while the decode of step s - 1 still reads
-    # the other set.  Step s's writes touch only its new slots and fresh copy-on-write blocks,
-    # none of which the decode of step s - 1 reads.
-    dset = [dict(slots=torch.empty(B, dtype=torch.int64, device=dev),
-                 pairs=torch.empty((B, 2), dtype=torch.int32, device=dev),
-                 tables=torch.empty((B, max_blocks), dtype=torch.int32, device=dev),
-                 lens=torch.empty(B, dtype=torch.int32, device=dev),
-                 cached=None if args.no_cache_hint else torch.empty(B, dtype=torch.int32, device=dev),
-                 read=torch.cuda.Event(), ready=torch.cuda.Event()) for _ in range(2)]
     stream = torch.cuda.current_stream(dev)
-    side = stream if args.serial else torch.cuda.Stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(total_steps)]
     kv_per_token = 2 * c.num_kv_heads * c.head_dim * c.dsize
     step_bytes = [kv_per_token * int(np.sum(w.lengths + s)) for s in range(total_steps)]
     host_s = [0.0]
     saved = [] if args.check else None
+    use_hint = not args.no_cache_hint
+    NBUF = 4 if args.overlap else 2
 
-    def step(s):
-        st, ds = stage[s % 2], dset[s % 2]
-        st["done"].synchronize()  # the uploads that last read this staging set are finished
-        h0 = time.perf_counter()
-        sl, pr = st["slots"].numpy(), st["pairs"].numpy()
-        ncow = alloc.pkv_seq_append_into(ids, sl, pr)                         # a1
-        alloc.pkv_get_block_tables(ids, max_blocks, st["tables"].numpy(), st["lens"].numpy())
-        if ds["cached"] is not None:  # leading blocks shared with other sequences: read cached
-            alloc.pkv_shared_prefix_blocks(ids, st["cached"].numpy())
-        host_s[0] += time.perf_counter() - h0
-        with torch.cuda.stream(side):
-            side.wait_event(ds["read"])  # the decode that last read this device set is done
-            ds["slots"].copy_(st["slots"], non_blocking=True)                 # a2
-            ds["tables"].copy_(st["tables"], non_blocking=True)
-            ds["lens"].copy_(st["lens"], non_blocking=True)
-            if ds["cached"] is not None:
-                ds["cached"].copy_(st["cached"], non_blocking=True)
-            if ncow:
-                ds["pairs"].view(-1)[: 2 * ncow].copy_(st["pairs"][: 2 * ncow], non_blocking=True)
-            st["done"].record(side)
+    if args.overlap:
+        step, final_tables = overlapped_steps(args, alloc, ids, B, max_blocks, NBUF, k_cache, v_cache,
+                                              k_new, v_new, q, out, workspace, max_len_final, c,
+                                              stream, ev, host_s, saved, use_hint, dev)
+    else:
+        # One stream.  The device keeps the block tables and lengths: each step uploads one
+        # small packed buffer (the slots, the positions they extend and the hint) and
+        # pkv_update_block_tables applies them, instead of re-sending whole tables.
+        t_host, l_host = alloc.pkv_get_block_tables(ids, max_blocks)
+        tables_d = torch.from_numpy(t_host).to(dev)
+        lens_d = torch.from_numpy(l_host).to(dev)
+        lens_h = l_host.astype(np.int32).copy()
+        rows_d = torch.arange(B, dtype=torch.int32, device=dev)
+        nbytes = 8 * B + 4 * B + 4 * B + 8 * B  # slots | positions | hint | cow pairs
+        pk_h = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(NBUF)]
+        pk_done = [torch.cuda.Event() for _ in range(NBUF)]
+        for e in pk_done:
+            e.record(stream)
+        pk_d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        slots_d = pk_d[: 8 * B].view(torch.int64)
+        pos_d = pk_d[8 * B: 12 * B].view(torch.int32)
+        hint_d = pk_d[12 * B: 16 * B].view(torch.int32)
+        pairs_d = pk_d[16 * B:].view(torch.int32).view(B, 2)
+
+        def step(s):
+            i = s % NBUF
+            pk_done[i].synchronize()  # the upload that last read this staging buffer is done
+            h0 = time.perf_counter()
+            buf = pk_h[i].numpy()
+            sl = buf[: 8 * B].view(np.int64)
+            ps = buf[8 * B: 12 * B].view(np.int32)
+            hint = buf[12 * B: 16 * B].view(np.int32)
+            pr = buf[16 * B:].view(np.int32)
+            ps[:] = lens_h                                                    # positions
+            ncow = alloc.pkv_seq_append_into(ids, sl, pr)                     # a1
+            lens_h[:] += 1
+            if use_hint:  # leading blocks shared with other sequences: read cached
+                alloc.pkv_shared_prefix_blocks(ids, hint)
+            host_s[0] += time.perf_counter() - h0
+            pk_d.copy_(pk_h[i], non_blocking=True)                            # a2
+            pk_done[i].record(stream)
             if ncow:                                                          # a3
-                pkv.pkv_copy_blocks(k_cache, v_cache, ds["pairs"][:ncow])
-            pkv.pkv_reshape_and_cache(k_new[s], v_new[s], ds["slots"], k_cache, v_cache)  # a4
-            ds["ready"].record(side)
-        stream.wait_event(ds["ready"])
-        ev[s][0].record(stream)
-        pkv.pkv_paged_attention_decode(out, q[s], k_cache, v_cache, ds["tables"], ds["lens"],  # a5, a6
-                                       max_len_final, c.scale, args.partition, workspace,
-                                       ds["cached"])
-        ev[s][1].record(stream)
-        ds["read"].record(stream)
-        if saved is not None:
-            saved.append(out.clone())
+                pkv.pkv_copy_blocks(k_cache, v_cache, pairs_d[:ncow])
+            pkv.pkv_update_block_tables(tables_d, lens_d, rows_d, pos_d, slots_d, bs, c.num_blocks)
+            pkv.pkv_reshape_and_cache(k_new[s], v_new[s], slots_d, k_cache, v_cache)  # a4
+            ev[s][0].record(stream)
+            pkv.pkv_paged_attention_decode(out, q[s], k_cache, v_cache, tables_d, lens_d,  # a5, a6
+                                           max_len_final, c.scale, args.partition, workspace,
+                                           hint_d if use_hint else None)
+            ev[s][1].record(stream)
+            if saved is not None:
+                saved.append(out.clone())
+
+        final_tables = lambda: tables_d
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -410,7 +479,7 @@ def main():
     if saved is not None:
         # During the timed steps tables only grow, so the final tables with each step's
         # lengths reproduce that step's inputs exactly.
-        final = dset[(total_steps - 1) % 2]["tables"]
+        final = final_tables()
         again = torch.empty_like(out)
         for s in range(total_steps):
             lens_s = torch.from_numpy((w.lengths + s).astype(np.int32)).to(dev)
@@ -449,7 +518,7 @@ def main():
         "decode_kernel_tokens_per_s": round(B / (kern_avg_ms * 1e-3), 1),
         "partition_size": args.partition,
         "cache_hint": not args.no_cache_hint,
-        "step_overlap": not args.serial,
+        "step_overlap": bool(args.overlap),
         "checked": bool(args.check),
         "host_ms_per_step": round(host_s[0] * 1e3 / K, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,

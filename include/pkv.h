@@ -177,6 +177,23 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t num_blocks, pkv_dtype dtype, void* stream);
 
+/* Device-side upkeep of block tables and lengths after appends, so that a decode loop
+ * uploads only the step's slots instead of whole tables ("vLLM + PagedAttention", step 2
+ * under "它是怎么工作的？": each request's page table records where token n lives).  For
+ * each i < n with rows[i] in [0, num_rows), positions[i] >= 0 and slot s = slot_mapping[i]
+ * in [0, num_blocks * block_size): block_tables[rows[i]][positions[i] / block_size] =
+ * s / block_size (if that column is below max_blocks_per_seq) and context_lens[rows[i]] =
+ * positions[i] + 1; other entries are skipped.  rows (device, n int32, distinct),
+ * positions (device, n int32: the token's position = the row's length before the append),
+ * slot_mapping (device, n int64, as returned by pkv_seq_append).  After pkv_seq_append the
+ * result equals the tables pkv_get_block_tables returns, copy-on-write included (the new
+ * token always lands in the row's last block, whose id the slot carries). */
+pkv_status pkv_update_block_tables(int32_t* block_tables, int32_t* context_lens,
+                                   const int32_t* rows, const int32_t* positions,
+                                   const int64_t* slot_mapping, int32_t n, int32_t num_rows,
+                                   int32_t max_blocks_per_seq, int32_t block_size,
+                                   int32_t num_blocks, void* stream);
+
 /* Bytes of workspace pkv_paged_attention_decode needs for this shape, max_context_len and
  * partition_size (same meanings as for the decode call): num_seqs * num_q_heads * P *
  * (head_dim + 2) floats when contexts are split into P > 1 partitions, else 0. */

@@ -11,10 +11,10 @@ _load()
 
 from .api import (PkvAlloc, PkvError, pkv_copy_blocks, pkv_decode_workspace_bytes,  # noqa: E402
                   pkv_paged_attention_decode, pkv_paged_attention_prefill,
-                  pkv_reshape_and_cache, pkv_status_str, pkv_version, DTYPE_CODES,
-                  STATUS_NAMES)
+                  pkv_reshape_and_cache, pkv_status_str, pkv_update_block_tables,
+                  pkv_version, DTYPE_CODES, STATUS_NAMES)
 
 __all__ = ["PkvAlloc", "PkvError", "pkv_copy_blocks", "pkv_decode_workspace_bytes",
            "pkv_paged_attention_decode", "pkv_paged_attention_prefill",
-           "pkv_reshape_and_cache", "pkv_status_str",
+           "pkv_reshape_and_cache", "pkv_status_str", "pkv_update_block_tables",
            "pkv_version", "DTYPE_CODES", "STATUS_NAMES"]

@@ -31,6 +31,8 @@ SIGNATURES = {
     "pkv_reshape_and_cache": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                       c_i32, c_i32, c_vp]),
     "pkv_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pkv_update_block_tables": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                        c_i32, c_vp]),
     "pkv_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_attention_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,

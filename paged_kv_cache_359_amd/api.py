@@ -216,6 +216,26 @@ def pkv_copy_blocks(k_cache, v_cache, pairs):
                                        _dtype_code(k_cache), _stream(k_cache)), "pkv_copy_blocks")
 
 
+def pkv_update_block_tables(block_tables, context_lens, rows, positions, slot_mapping,
+                            block_size: int, num_blocks: int):
+    """block_tables [B, max_blocks] int32 and context_lens [B] int32 (device, updated in
+    place); rows/positions [n] int32 and slot_mapping [n] int64 (device)."""
+    import torch
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if rows.dtype != torch.int32 or positions.dtype != torch.int32 or slot_mapping.dtype != torch.int64:
+        raise TypeError("rows/positions int32, slot_mapping int64")
+    n = rows.numel()
+    if positions.numel() != n or slot_mapping.numel() != n:
+        raise ValueError("rows, positions and slot_mapping differ in length")
+    if n == 0:
+        return
+    _check(_lib.load().pkv_update_block_tables(
+        _dev(block_tables), _dev(context_lens), _dev(rows), _dev(positions), _dev(slot_mapping),
+        n, block_tables.shape[0], block_tables.shape[1], int(block_size), int(num_blocks),
+        _stream(block_tables)), "pkv_update_block_tables")
+
+
 def pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                max_context_len, dtype, partition_size=-1) -> int:
     """dtype: "f32" | "f16" | "bf16" or a torch dtype."""

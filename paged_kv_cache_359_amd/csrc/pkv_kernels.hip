@@ -509,17 +509,23 @@ struct Mfma {
     else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
   }
 
+  // The K/V of one 32-token chunk as this lane holds it: K rows cs + 16hf + lane%16 (8
+  // elements per k-step) and V rows cs + 16hf + 4*(lane/16) + i, elements
+  // [E*(lane%16), E*(lane%16) + E).  compute() zeroes the V rows of tokens that do not exist.
+  struct Chunk {
+    uint4 kr[2][KK];
+    uint32_t vr[2][4][E / 2];
+    bool vok[2][4];
+    bool need_mask;  // wave-uniform: some row of this chunk does not exist
+  };
+
   // kb / vb: pool base plus this KV head's offset.  cs: a multiple of 16.  cached: read this
-  // chunk through the caches (wave-uniform).  CAUSAL: the lane's column may only see keys at
-  // positions <= lim; lim_min is the smallest lim of the wave (wave-uniform).
-  template <bool CAUSAL = false>
-  __device__ static void chunk(const DecodeArgs& a, const int32_t* tbl, const char* kb,
-                               const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
-                               int lane, const vec8 (&qop)[KK], State& st, int lim = 0,
-                               int lim_min = 0) {
+  // chunk through the caches (wave-uniform).
+  __device__ static void load(const DecodeArgs& a, const int32_t* tbl, const char* kb,
+                              const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
+                              int lane, Chunk& ck) {
     const int n16 = lane & 15, g4 = lane >> 4;
     bool need_mask = cs + kMfmaChunk > t1;  // wave-uniform
-    if constexpr (CAUSAL) need_mask |= cs + kMfmaChunk - 1 > lim_min;
     int ids[2][NBH];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
@@ -529,11 +535,8 @@ struct Mfma {
         ids[hf][k] = uniform(first < t1 ? tbl[first / BS] : -1);
         need_mask |= (unsigned)ids[hf][k] >= (unsigned)a.num_blocks;
       }
-    // K rows cs + 16hf + n16 (8 elements per k-step); V rows cs + 16hf + 4g4 + i, elements
-    // [E*n16, E*n16 + E).
     const char* kp[2];
     const char* vp[2][4];
-    bool vok[2][4];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int tok = cs + 16 * hf + n16;
@@ -542,29 +545,26 @@ struct Mfma {
       kp[hf] = kb + size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * 2 + 8 * g4 * 2;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * hf + 4 * g4 + i;
-        const int tv = cs + r;
+        const int tv = cs + 16 * hf + 4 * g4 + i;
         const int idv = ids[hf][NBH > 1 ? (4 * g4 + i) / BS : 0];
         const bool vv = (unsigned)idv < (unsigned)a.num_blocks;
-        vok[hf][i] = vv && tv < t1;
+        ck.vok[hf][i] = vv && tv < t1;
         vp[hf][i] = vb + size_t(vv ? idv : 0) * blk_bytes + size_t(tv % BS) * D * 2 + E * n16 * 2;
       }
     }
-    uint4 kr[2][KK];
-    uint32_t vr[2][4][E / 2];
     if (cached) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kr[hf][kk] = load_cached(kp[hf] + 32 * kk * 2);
+        for (int kk = 0; kk < KK; ++kk) ck.kr[hf][kk] = load_cached(kp[hf] + 32 * kk * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (E == 8) {
             const uint4 w = load_cached(vp[hf][i]);
-            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
+            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y, ck.vr[hf][i][2] = w.z, ck.vr[hf][i][3] = w.w;
           } else {
             const uint2 w = load_cached8(vp[hf][i]);
-            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
+            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y;
           }
         }
       }
@@ -572,26 +572,38 @@ struct Mfma {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kr[hf][kk] = load_stream(kp[hf] + 32 * kk * 2);
+        for (int kk = 0; kk < KK; ++kk) ck.kr[hf][kk] = load_stream(kp[hf] + 32 * kk * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (E == 8) {
             const uint4 w = load_stream(vp[hf][i]);
-            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
+            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y, ck.vr[hf][i][2] = w.z, ck.vr[hf][i][3] = w.w;
           } else {
             const uint2 w = load_stream8(vp[hf][i]);
-            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
+            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y;
           }
         }
       }
     }
+    ck.need_mask = need_mask;
+  }
+
+  // Online-softmax update of one 16-column tile with a loaded chunk starting at token cs.
+  // CAUSAL: the lane's column may only see keys at positions <= lim; lim_min is the smallest
+  // lim of the tile (wave-uniform).
+  template <bool CAUSAL = false>
+  __device__ static void compute(const DecodeArgs& a, Chunk& ck, int cs, int lane,
+                                 const vec8 (&qop)[KK], State& st, int lim = 0, int lim_min = 0) {
+    const int g4 = lane >> 4;
+    bool need_mask = ck.need_mask;
+    if constexpr (CAUSAL) need_mask |= cs + kMfmaChunk - 1 > lim_min;
     // S = K . Q^T for both halves.
     float4_t s[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       s[hf] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) s[hf] = mma(__builtin_bit_cast(vec8, kr[hf][kk]), qop[kk], s[hf]);
+      for (int kk = 0; kk < KK; ++kk) s[hf] = mma(__builtin_bit_cast(vec8, ck.kr[hf][kk]), qop[kk], s[hf]);
     }
     float sv[2][4];
 #pragma unroll
@@ -600,10 +612,10 @@ struct Mfma {
       for (int i = 0; i < 4; ++i) {
         sv[hf][i] = s[hf][i] * a.scale_log2;
         if (need_mask) {
-          if (!vok[hf][i]) {
+          if (!ck.vok[hf][i]) {
             sv[hf][i] = kNegInf;
 #pragma unroll
-            for (int q = 0; q < E / 2; ++q) vr[hf][i][q] = 0u;  // unused slots may hold anything
+            for (int q = 0; q < E / 2; ++q) ck.vr[hf][i][q] = 0u;  // unused slots may hold anything
           }
           if constexpr (CAUSAL) {
             if (cs + 16 * hf + 4 * g4 + i > lim) sv[hf][i] = kNegInf;  // a later token
@@ -635,14 +647,22 @@ struct Mfma {
       uint32_t w[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = vr[(2 * q) >> 2][(2 * q) & 3][r >> 1];
-        const uint32_t hi = vr[(2 * q + 1) >> 2][(2 * q + 1) & 3][r >> 1];
+        const uint32_t lo = ck.vr[(2 * q) >> 2][(2 * q) & 3][r >> 1];
+        const uint32_t hi = ck.vr[(2 * q + 1) >> 2][(2 * q + 1) & 3][r >> 1];
         w[q] = (r & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
       }
       const vec8 vop = __builtin_bit_cast(vec8, make_uint4(w[0], w[1], w[2], w[3]));
       st.acc[r] = mma(vop, phi, st.acc[r]);
       if constexpr (SPLIT_P) st.acc[r] = mma(vop, plo, st.acc[r]);
     }
+  }
+
+  __device__ static void chunk(const DecodeArgs& a, const int32_t* tbl, const char* kb,
+                               const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
+                               int lane, const vec8 (&qop)[KK], State& st) {
+    Chunk ck;
+    load(a, tbl, kb, vb, blk_bytes, cs, t1, cached, lane, ck);
+    compute(a, ck, cs, lane, qop, st);
   }
 
   // Output d of element (r, v) of the lane's accumulators: E * (4 * (lane / 16) + v) + r.
@@ -739,16 +759,20 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 }
 
 // =========================================================================================
-// Prefill: one workgroup of 4 waves per (query head, 64 consecutive new tokens, sequence);
-// wave w takes new tokens 16w .. 16w + 15 of the tile as the 16 columns of the MFMA inner
-// loop.  Sequence b's new tokens are q rows query_start[b] .. query_start[b+1]; with ctx_b
-// tokens cached (the new ones included), new token j sits at position ctx_b - n_b + j and
-// sees keys 0 .. that position.  Neighbouring tiles and the query heads of a group read the
-// same K/V, so K/V goes through the caches.
+// Prefill: one workgroup of 4 waves per (query head, 64 * NT consecutive new tokens,
+// sequence); wave w takes NT tiles of 16 new tokens each as the columns of the MFMA inner
+// loop, so every loaded K/V chunk serves 16 * NT columns.  Sequence b's new tokens are q rows
+// query_start[b] .. query_start[b+1]; with ctx_b tokens cached (the new ones included), new
+// token j sits at position ctx_b - n_b + j and sees keys 0 .. that position.  Neighbouring
+// tiles and the query heads of a group read the same K/V, so K/V goes through the caches.
 // =========================================================================================
+constexpr int kPrefillTiles = 2;  // 16-column tiles per wave
+constexpr int kPrefillRows = 4 * 16 * kPrefillTiles;  // new tokens per workgroup
+
 template <int DT, int D, int BS>
 __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   using M = Mfma<DT, D, BS>;
+  constexpr int NT = kPrefillTiles;
   const int h = blockIdx.x;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -756,29 +780,32 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   const int n16 = lane & 15, g4 = lane >> 4;
   const int r0 = a.query_start[b];
   const int n = a.query_start[b + 1] - r0;
-  const int j0 = blockIdx.y * 64 + wave * 16;  // first new token of this wave
+  const int j0 = blockIdx.y * kPrefillRows + wave * 16 * NT;  // first new token of this wave
   if (r0 < 0 || n <= 0 || j0 >= n || r0 + j0 >= a.num_tokens) return;
-  const int nq = min(min(16, n - j0), a.num_tokens - r0 - j0);  // columns with a row
+  const int nq = min(min(16 * NT, n - j0), a.num_tokens - r0 - j0);  // columns with a row
   const int ctx = clamp_ctx(a, b);
   const int first = ctx - n;                 // position of new token 0
-  const int j = j0 + n16;
-  const bool col = n16 < nq;
-  const int lim = col ? first + j : -1;      // last key position this column sees
-  const int lim_min = first + j0;
   const int t1 = min(ctx, first + j0 + nq);  // keys 0 .. t1 - 1
-  const size_t row = size_t(r0 + (col ? j : j0));
-  const size_t out_idx = (row * a.num_q_heads + h) * D;
 
-  typename M::State st;
-  M::init(st);
-  if (t1 > 0) {
-    typename M::vec8 qop[M::KK];
-    const char* qp = static_cast<const char*>(a.q) + out_idx * 2;
+  typename M::vec8 qop[NT][M::KK];
+  typename M::State st[NT];
+  int lim[NT], lim_min[NT], lim_max[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    M::init(st[t]);
+    const int jt = j0 + 16 * t;
+    const bool col = 16 * t + n16 < nq;
+    lim[t] = col ? first + jt + n16 : -1;
+    lim_min[t] = first + jt;
+    lim_max[t] = first + jt + min(16, max(0, nq - 16 * t)) - 1;  // wave-uniform
+    const char* qp = static_cast<const char*>(a.q) + ((size_t(r0 + (col ? jt + n16 : j0)) * a.num_q_heads + h) * D) * 2;
 #pragma unroll
     for (int kk = 0; kk < M::KK; ++kk) {
       const uint4 w = col ? *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2) : make_uint4(0, 0, 0, 0);
-      qop[kk] = __builtin_bit_cast(typename M::vec8, w);
+      qop[t][kk] = __builtin_bit_cast(typename M::vec8, w);
     }
+  }
+  if (t1 > 0) {
     const int kvh = h / a.group;
     const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
     const size_t head_off = size_t(kvh) * BS * D * 2;
@@ -786,18 +813,28 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
     const char* vb = static_cast<const char*>(a.v_cache) + head_off;
     const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
     const int nchunks = (t1 + kMfmaChunk - 1) / kMfmaChunk;
-    for (int c = 0; c < nchunks; ++c)
-      M::template chunk<true>(a, tbl, kb, vb, blk_bytes, c * kMfmaChunk, t1, true, lane, qop, st, lim, lim_min);
+    for (int c = 0; c < nchunks; ++c) {
+      const int cs = c * kMfmaChunk;
+      typename M::Chunk ck;
+      M::load(a, tbl, kb, vb, blk_bytes, cs, t1, true, lane, ck);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (cs <= lim_max[t])  // a tile whose columns all precede this chunk skips it
+          M::template compute<true>(a, ck, cs, lane, qop[t], st[t], lim[t], lim_min[t]);
+    }
   }
-  st.l = xor_sum_16_32(st.l);
-  if (col) {
-    float v[4 * M::E];
-    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
 #pragma unroll
-    for (int r = 0; r < M::E; ++r)
+  for (int t = 0; t < NT; ++t) {
+    st[t].l = xor_sum_16_32(st[t].l);
+    if (16 * t + n16 < nq) {
+      float v[4 * M::E];
+      const float inv = st[t].l > 0.f ? 1.f / st[t].l : 0.f;
 #pragma unroll
-      for (int vv = 0; vv < 4; ++vv) v[vv * M::E + r] = st.acc[r][vv] * inv;
-    store_row<DT, 4 * M::E>(a.out, out_idx + 4 * M::E * g4, v);
+      for (int r = 0; r < M::E; ++r)
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) v[vv * M::E + r] = st[t].acc[r][vv] * inv;
+      store_row<DT, 4 * M::E>(a.out, (size_t(r0 + j0 + 16 * t + n16) * a.num_q_heads + h) * D + 4 * M::E * g4, v);
+    }
   }
 }
 
@@ -849,6 +886,28 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   const int64_t dst = ((blk * heads + h) * block_size + off) * row_vecs + c;
   k_cache[dst] = key[i];
   v_cache[dst] = value[i];
+}
+
+// Device-side bookkeeping of one append per listed sequence: the token at position pos[i] of
+// row rows[i] sits in slot slots[i], so table entry pos / block_size holds slot / block_size
+// and the row's length becomes pos + 1.
+__global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict__ tables,
+                                                            int32_t* __restrict__ lens,
+                                                            const int32_t* __restrict__ rows,
+                                                            const int32_t* __restrict__ pos,
+                                                            const int64_t* __restrict__ slots,
+                                                            int32_t n, int32_t num_rows,
+                                                            int32_t max_blocks, int32_t block_size,
+                                                            int64_t num_slots) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t r = rows[i], p = pos[i];
+  const int64_t s = slots[i];
+  if ((unsigned)r >= (unsigned)num_rows || p < 0 || s < 0 || s >= num_slots) return;
+  const int32_t col = p / block_size;
+  if (col >= max_blocks) return;
+  tables[int64_t(r) * max_blocks + col] = int32_t(s / block_size);
+  lens[r] = p + 1;
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* k_cache, uint4* v_cache,
@@ -1056,6 +1115,24 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
   return launch_status("copy_blocks");
 }
 
+pkv_status pkv_update_block_tables(int32_t* block_tables, int32_t* context_lens,
+                                   const int32_t* rows, const int32_t* positions,
+                                   const int64_t* slot_mapping, int32_t n, int32_t num_rows,
+                                   int32_t max_blocks_per_seq, int32_t block_size,
+                                   int32_t num_blocks, void* stream) {
+  if (n < 0 || num_rows < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  if (!block_tables || !context_lens || !rows || !positions || !slot_mapping)
+    return PKV_ERR_INVALID_ARG;
+  clear_stale_error();
+  hipLaunchKernelGGL(update_tables_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), block_tables, context_lens, rows, positions,
+                     slot_mapping, n, num_rows, max_blocks_per_seq, block_size,
+                     int64_t(num_blocks) * block_size);
+  return launch_status("update_block_tables");
+}
+
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                   pkv_dtype dtype, int32_t partition_size) {
@@ -1167,7 +1244,8 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   kernel_fn k = pick_prefill(dtype, head_dim, block_size);
   if (!k) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
-  if (num_seqs > 65535 || (int64_t(max_query_len) + 63) / 64 > 65535) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs > 65535 || (int64_t(max_query_len) + kPrefillRows - 1) / kPrefillRows > 65535)
+    return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -1189,7 +1267,8 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   a.max_blocks = max_blocks_per_seq;
   a.ctx_limit = int32_t(max_context_len < cap ? max_context_len : cap);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid{unsigned(num_q_heads), unsigned((max_query_len + 63) / 64), unsigned(num_seqs)};
+  const dim3 grid{unsigned(num_q_heads), unsigned((max_query_len + kPrefillRows - 1) / kPrefillRows),
+                  unsigned(num_seqs)};
   clear_stale_error();
   hipLaunchKernelGGL(k, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
   return launch_status("paged_attention_prefill");

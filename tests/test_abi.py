@@ -198,3 +198,12 @@ def prefill(**kw):
 ])
 def test_prefill_validation(kw, status):
     assert prefill(**kw) == status
+
+
+def test_update_block_tables_validation():
+    l = lib()
+    assert l.pkv_update_block_tables(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 4, 8, 16, 100, None) == 0
+    assert l.pkv_update_block_tables(None, FAKE, FAKE, FAKE, FAKE, 3, 4, 8, 16, 100, None) == 1
+    assert l.pkv_update_block_tables(FAKE, FAKE, FAKE, None, FAKE, 3, 4, 8, 16, 100, None) == 1
+    assert l.pkv_update_block_tables(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 4, 8, 16, 100, None) == 1
+    assert l.pkv_update_block_tables(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 0, 16, 100, None) == 1

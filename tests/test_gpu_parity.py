@@ -197,3 +197,35 @@ def test_empty_context_and_invalid_table_entries():
                 v = oracle.to_f64(oracle.gather(o.v_pool, tables[b], int(lens[b]), h), cfg.dtype)[keep]
                 r = oracle.attention_contiguous(q[b, h], k, v, cfg.scale)
                 check(out[b, h], r, cfg.dtype, f"invalid table entry b={b} h={h} p={p}")
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("shared_prefix_bs16_cow", dict(batch=6, num_blocks=512)),
+    ("llama13b", dict(batch=8, num_blocks=2048)),
+    ("tiny", dict(batch=5, lengths=("fixed", (1, 4, 7, 8, 9)), num_blocks=64)),
+])
+def test_device_table_updates_track_the_allocator(name, overrides):
+    """Tables and lengths kept on the device by pkv_update_block_tables, from each step's
+    slots alone, equal the allocator's tables after every append (copy-on-write included)."""
+    import paged_kv_cache_359_amd as pkv
+    cfg = W.get_config(name, **overrides)
+    w = W.make_workload(cfg, device="cuda")
+    g = gpu_side.GpuState(w)
+    g.run(W.setup_ops(w))
+    B, bs = w.batch, cfg.block_size
+    steps = 2 * bs + 3
+    mb = max(-(-int(g.lens[b] + steps) // bs) for b in range(B))
+    t0, l0 = g.alloc.pkv_get_block_tables(list(range(B)), mb)
+    tables = torch.from_numpy(t0).cuda()
+    lens = torch.from_numpy(l0).cuda()
+    rows = torch.arange(B, dtype=torch.int32, device="cuda")
+    for _ in range(steps):
+        pos = np.array([g.lens[b] for b in range(B)], dtype=np.int32)
+        slots, pairs = g.alloc.pkv_seq_append(list(range(B)))
+        for b in range(B):
+            g.lens[b] += 1
+        pkv.pkv_update_block_tables(tables, lens, rows, torch.from_numpy(pos).cuda(),
+                                    torch.from_numpy(slots).cuda(), bs, cfg.num_blocks)
+        th, lh = g.alloc.pkv_get_block_tables(list(range(B)), mb)
+        assert np.array_equal(tables.cpu().numpy(), th)
+        assert np.array_equal(lens.cpu().numpy(), lh)
