@@ -126,6 +126,23 @@ pkv_status pkv_seq_extend(pkv_alloc* a, int64_t seq_id, int32_t n, int64_t* slot
  * the pool in logical order (so its last block is the next one handed out). */
 pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id);
 
+/* Preemption by swapping ("LLM Systems 24: Efficient LLM Inference with PagedAttention and
+ * vLLM", §3 Conclusion: when the pool runs out a request is preempted, its cache swapped out
+ * to the host, and restored later).  pkv_seq_swap_out writes the sequence's blocks in
+ * logical order to blocks_out (host, capacity max_blocks; INVALID_ARG if too small, nothing
+ * changed) and *n_blocks_out, then gives up its references exactly like pkv_seq_free; the
+ * caller first copies those blocks out (pkv_gather_blocks on the same stream before the
+ * blocks are reused).  The id stays taken (add/fork return DUPLICATE_SEQ) until swap-in.
+ * pkv_seq_swap_in takes that many fresh blocks, handed out in logical order, writes them to
+ * blocks_out and restores the length; the caller then copies the data back
+ * (pkv_scatter_blocks).  The restored sequence owns every block (sharing is not
+ * re-established).  OUT_OF_BLOCKS leaves everything unchanged; UNKNOWN_SEQ if the id is not
+ * resident (swap-out) or not swapped out (swap-in). */
+pkv_status pkv_seq_swap_out(pkv_alloc* a, int64_t seq_id, int32_t max_blocks, int32_t* blocks_out,
+                            int32_t* n_blocks_out);
+pkv_status pkv_seq_swap_in(pkv_alloc* a, int64_t seq_id, int32_t max_blocks, int32_t* blocks_out,
+                           int32_t* n_blocks_out);
+
 /* Copy the block tables of n sequences into tables_out (host, n * max_blocks int32,
  * row-major, padded with -1) and their lengths into lens_out (host, n int32; nullable).
  * INVALID_ARG if a sequence holds more than max_blocks blocks. */
@@ -176,6 +193,22 @@ pkv_status pkv_reshape_and_cache(const void* key, const void* value, const int64
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n_pairs,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t num_blocks, pkv_dtype dtype, void* stream);
+
+/* Whole-block moves for swap preemption (see pkv_seq_swap_out).  pkv_gather_blocks copies
+ * block blocks[i] of the K and V pools (every KV head and slot, blk = num_kv_heads *
+ * block_size * head_dim elements) to k_out + i * blk and v_out + i * blk;
+ * pkv_scatter_blocks copies k_in + i * blk and v_in + i * blk back into block blocks[i].
+ * blocks: device, n_blocks int32 (ids outside [0, num_blocks) are skipped; scatter
+ * destinations must be distinct).  The buffers are device memory (16-byte aligned); to
+ * reach the host, copy them with one asynchronous device-to-host copy on the same stream. */
+pkv_status pkv_gather_blocks(const void* k_cache, const void* v_cache, const int32_t* blocks,
+                             int32_t n_blocks, void* k_out, void* v_out, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             pkv_dtype dtype, void* stream);
+pkv_status pkv_scatter_blocks(const void* k_in, const void* v_in, const int32_t* blocks,
+                              int32_t n_blocks, void* k_cache, void* v_cache, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              pkv_dtype dtype, void* stream);
 
 /* Device-side upkeep of block tables and lengths after appends, so that a decode loop
  * uploads only the step's slots instead of whole tables ("vLLM + PagedAttention", step 2

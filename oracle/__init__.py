@@ -15,12 +15,14 @@ Modules:
 """
 from .allocator import (OracleAllocator, OracleError, OutOfBlocks, UnknownSeq, DuplicateSeq,
                         InvalidArg)
-from .cache import new_pool, cache_write, copy_blocks, gather, to_f64, bits_of
+from .cache import (new_pool, cache_write, copy_blocks, gather, gather_blocks, scatter_blocks,
+                    to_f64, bits_of)
 from .attention import decode, prefill, attention_contiguous, softmax_weights
 from . import calc
 
 __all__ = [
     "OracleAllocator", "OracleError", "OutOfBlocks", "UnknownSeq", "DuplicateSeq", "InvalidArg",
-    "new_pool", "cache_write", "copy_blocks", "gather", "to_f64", "bits_of",
+    "new_pool", "cache_write", "copy_blocks", "gather", "gather_blocks", "scatter_blocks",
+    "to_f64", "bits_of",
     "decode", "prefill", "attention_contiguous", "softmax_weights", "calc",
 ]

@@ -27,6 +27,11 @@ Readings where the pages leave a choice open (each also listed in the design not
     block_size``.
   * ``extend`` (several new tokens of one sequence, as a prefill chunk brings) is defined as
     that many single-token appends in a row.
+  * Preemption by swapping ("LLM Systems 24", §3 Conclusion: when blocks run out a request
+    is preempted and its cache swapped out or recomputed): ``swap_out`` hands the caller the
+    sequence's blocks in logical order, then releases them exactly like ``free_seq``;
+    ``swap_in`` later takes fresh blocks for all of them, popped in logical order, so the
+    restored sequence owns every block (sharing is not re-established).
   * Every call either succeeds completely or changes nothing.
 """
 from __future__ import annotations
@@ -68,6 +73,7 @@ class OracleAllocator:
         self.ref = [0] * num_blocks
         self.tables = {}
         self.lens = {}
+        self.swapped = {}  # seq -> (length, number of blocks) while its cache is on the host
 
     # -- helpers -----------------------------------------------------------------------
     def _pop(self) -> int:
@@ -78,10 +84,11 @@ class OracleAllocator:
         return b
 
     def _snapshot(self):
-        return (list(self.free), list(self.ref), copy.deepcopy(self.tables), dict(self.lens))
+        return (list(self.free), list(self.ref), copy.deepcopy(self.tables), dict(self.lens),
+                dict(self.swapped))
 
     def _restore(self, snap):
-        self.free, self.ref, self.tables, self.lens = snap
+        self.free, self.ref, self.tables, self.lens, self.swapped = snap
 
     def _slot(self, seq) -> int:
         n = self.lens[seq]
@@ -92,7 +99,7 @@ class OracleAllocator:
         """New sequence holding ``num_tokens`` tokens; returns their slots in order."""
         if num_tokens < 0:
             raise InvalidArg("num_tokens must be >= 0")
-        if seq in self.tables:
+        if seq in self.tables or seq in self.swapped:
             raise DuplicateSeq(seq)
         need = -(-num_tokens // self.block_size)
         if need > len(self.free):
@@ -109,7 +116,7 @@ class OracleAllocator:
         """``child`` shares every block of ``parent`` (one more reference each)."""
         if parent not in self.tables:
             raise UnknownSeq(parent)
-        if child in self.tables:
+        if child in self.tables or child in self.swapped:
             raise DuplicateSeq(child)
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
@@ -173,6 +180,31 @@ class OracleAllocator:
                 self.free.append(b)
         del self.tables[seq]
         del self.lens[seq]
+
+    def swap_out(self, seq):
+        """Preempt a sequence to host memory: returns its blocks in logical order (the caller
+        copies them out first), then gives up its references like ``free_seq`` and remembers
+        its length.  Shared blocks stay with their other holders; the host copy is whole."""
+        if seq not in self.tables:
+            raise UnknownSeq(seq)
+        blocks = list(self.tables[seq])
+        length = self.lens[seq]
+        self.free_seq(seq)
+        self.swapped[seq] = (length, len(blocks))
+        return blocks
+
+    def swap_in(self, seq):
+        """Bring a swapped-out sequence back into fresh blocks, popped in logical order (the
+        caller copies its data into them); all or nothing.  Returns the new blocks."""
+        if seq not in self.swapped:
+            raise UnknownSeq(seq)
+        length, nblocks = self.swapped[seq]
+        if nblocks > len(self.free):
+            raise OutOfBlocks(f"need {nblocks} blocks, {len(self.free)} free")
+        self.tables[seq] = [self._pop() for _ in range(nblocks)]
+        self.lens[seq] = length
+        del self.swapped[seq]
+        return list(self.tables[seq])
 
     # -- queries -----------------------------------------------------------------------
     def block_tables(self, seqs, max_blocks: int):

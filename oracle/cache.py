@@ -74,3 +74,15 @@ def gather(pool: np.ndarray, table, ctx: int, kv_head: int) -> np.ndarray:
     t = np.arange(ctx, dtype=np.int64)
     blocks = np.asarray(table, dtype=np.int64)[t // bs]
     return pool[blocks, kv_head, t % bs, :]
+
+
+def gather_blocks(pool: np.ndarray, blocks) -> np.ndarray:
+    """Whole blocks (every head, every slot) in the given order: ``[n, Hkv, bs, D]`` bits.
+    The host copy a swapped-out sequence keeps."""
+    return pool[np.asarray(blocks, dtype=np.int64)].copy()
+
+
+def scatter_blocks(pool: np.ndarray, blocks, data: np.ndarray) -> None:
+    """Inverse of ``gather_blocks``: block ``blocks[i]`` receives ``data[i]``."""
+    for i, b in enumerate(blocks):
+        pool[int(b)] = data[i]

@@ -10,11 +10,13 @@ from ._lib import load as _load
 _load()
 
 from .api import (PkvAlloc, PkvError, pkv_copy_blocks, pkv_decode_workspace_bytes,  # noqa: E402
+                  pkv_gather_blocks, pkv_scatter_blocks,
                   pkv_paged_attention_decode, pkv_paged_attention_prefill,
                   pkv_reshape_and_cache, pkv_status_str, pkv_update_block_tables,
                   pkv_version, DTYPE_CODES, STATUS_NAMES)
 
 __all__ = ["PkvAlloc", "PkvError", "pkv_copy_blocks", "pkv_decode_workspace_bytes",
+           "pkv_gather_blocks", "pkv_scatter_blocks",
            "pkv_paged_attention_decode", "pkv_paged_attention_prefill",
            "pkv_reshape_and_cache", "pkv_status_str", "pkv_update_block_tables",
            "pkv_version", "DTYPE_CODES", "STATUS_NAMES"]

@@ -22,6 +22,8 @@ SIGNATURES = {
     "pkv_seq_append": (c_i32, [c_vp, P_i64, c_i32, P_i64, P_i32, P_i32]),
     "pkv_seq_extend": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, P_i32]),
     "pkv_seq_free": (c_i32, [c_vp, c_i64]),
+    "pkv_seq_swap_out": (c_i32, [c_vp, c_i64, c_i32, P_i32, P_i32]),
+    "pkv_seq_swap_in": (c_i32, [c_vp, c_i64, c_i32, P_i32, P_i32]),
     "pkv_get_block_tables": (c_i32, [c_vp, P_i64, c_i32, c_i32, P_i32, P_i32]),
     "pkv_seq_length": (c_i32, [c_vp, c_i64, P_i32]),
     "pkv_shared_prefix_blocks": (c_i32, [c_vp, P_i64, c_i32, P_i32]),
@@ -31,6 +33,10 @@ SIGNATURES = {
     "pkv_reshape_and_cache": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                       c_i32, c_i32, c_vp]),
     "pkv_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pkv_gather_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                  c_i32, c_vp]),
+    "pkv_scatter_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                   c_i32, c_vp]),
     "pkv_update_block_tables": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                         c_i32, c_vp]),
     "pkv_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),

@@ -116,6 +116,19 @@ class PkvAlloc:
                "pkv_seq_extend")
         return slots[: int(n)], pairs[: 2 * ncow.value].reshape(-1, 2)
 
+    def _swap(self, fn, seq_id, max_blocks):
+        blocks = np.empty(max(int(max_blocks), 1), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, int(seq_id), int(max_blocks), _ptr(blocks, ctypes.c_int32),
+                  ctypes.byref(n)), fn.__name__)
+        return blocks[: n.value]
+
+    def pkv_seq_swap_out(self, seq_id: int, max_blocks: int) -> np.ndarray:
+        return self._swap(self._lib.pkv_seq_swap_out, seq_id, max_blocks)
+
+    def pkv_seq_swap_in(self, seq_id: int, max_blocks: int) -> np.ndarray:
+        return self._swap(self._lib.pkv_seq_swap_in, seq_id, max_blocks)
+
     def pkv_seq_free(self, seq_id: int):
         _check(self._lib.pkv_seq_free(self._h, int(seq_id)), "pkv_seq_free")
 
@@ -214,6 +227,36 @@ def pkv_copy_blocks(k_cache, v_cache, pairs):
     _check(_lib.load().pkv_copy_blocks(_dev(k_cache), _dev(v_cache),
                                        _dev(pairs) if npairs else None, npairs, hkv, d, bs, n,
                                        _dtype_code(k_cache), _stream(k_cache)), "pkv_copy_blocks")
+
+
+def _move_blocks(fn, name, cache_k, cache_v, blocks, buf_k, buf_v):
+    import torch
+    n, hkv, bs, d = cache_k.shape
+    if blocks.dtype != torch.int32:
+        raise TypeError("blocks must be int32")
+    nb = blocks.numel()
+    if buf_k.shape != (nb, hkv, bs, d) or buf_v.shape != buf_k.shape:
+        raise ValueError("buffers must be [n_blocks, Hkv, bs, D]")
+    if not (buf_k.dtype == buf_v.dtype == cache_k.dtype == cache_v.dtype):
+        raise TypeError("dtype mismatch")
+    if nb == 0:
+        return
+    _check(fn(_dev(cache_k), _dev(cache_v), _dev(blocks), nb, _dev(buf_k), _dev(buf_v), hkv, d, bs,
+              n, _dtype_code(cache_k), _stream(cache_k)), name)
+
+
+def pkv_gather_blocks(k_cache, v_cache, blocks, k_out, v_out):
+    """k_out/v_out [n, Hkv, bs, D] (device) receive the blocks ``blocks`` (device int32)."""
+    lib = _lib.load()
+    _move_blocks(lambda kc, vc, bl, n, kb, vb, *r: lib.pkv_gather_blocks(kc, vc, bl, n, kb, vb, *r),
+                 "pkv_gather_blocks", k_cache, v_cache, blocks, k_out, v_out)
+
+
+def pkv_scatter_blocks(k_in, v_in, blocks, k_cache, v_cache):
+    """Blocks ``blocks`` (device int32) of the caches receive k_in/v_in [n, Hkv, bs, D]."""
+    lib = _lib.load()
+    _move_blocks(lambda kc, vc, bl, n, kb, vb, *r: lib.pkv_scatter_blocks(kb, vb, bl, n, kc, vc, *r),
+                 "pkv_scatter_blocks", k_cache, v_cache, blocks, k_in, v_in)
 
 
 def pkv_update_block_tables(block_tables, context_lens, rows, positions, slot_mapping,

@@ -37,6 +37,10 @@ struct pkv_alloc {
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> ref;         // references per physical block
   std::unordered_map<int64_t, Sequence> seqs;
+  // Sequences preempted to the host: length and number of blocks to restore.
+  std::unordered_map<int64_t, std::pair<int32_t, int32_t>> swapped;
+
+  bool taken(int64_t id) const { return seqs.count(id) || swapped.count(id); }
 
   int32_t pop() {
     int32_t b = free_stack.back();
@@ -84,7 +88,7 @@ void pkv_alloc_destroy(pkv_alloc* a) { delete a; }
 
 pkv_status pkv_seq_add(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t* slots_out) {
   if (!a || num_tokens < 0 || (num_tokens > 0 && !slots_out)) return PKV_ERR_INVALID_ARG;
-  if (a->seqs.count(seq_id)) return PKV_ERR_DUPLICATE_SEQ;
+  if (a->taken(seq_id)) return PKV_ERR_DUPLICATE_SEQ;
   const int64_t need = (int64_t(num_tokens) + a->block_size - 1) / a->block_size;
   if (need > int64_t(a->free_stack.size())) return PKV_ERR_OUT_OF_BLOCKS;
   Sequence s;
@@ -102,7 +106,7 @@ pkv_status pkv_seq_fork(pkv_alloc* a, int64_t parent_id, int64_t child_id) {
   if (!a) return PKV_ERR_INVALID_ARG;
   auto it = a->seqs.find(parent_id);
   if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
-  if (a->seqs.count(child_id)) return PKV_ERR_DUPLICATE_SEQ;
+  if (a->taken(child_id)) return PKV_ERR_DUPLICATE_SEQ;
   Sequence child = it->second;  // copy table and length
   for (int32_t b : child.table) ++a->ref[b];
   a->seqs.emplace(child_id, std::move(child));
@@ -204,6 +208,44 @@ pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id) {
   for (int32_t b : it->second.table)
     if (--a->ref[b] == 0) a->free_stack.push_back(b);
   a->seqs.erase(it);
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_swap_out(pkv_alloc* a, int64_t seq_id, int32_t max_blocks, int32_t* blocks_out,
+                            int32_t* n_blocks_out) {
+  if (!a || max_blocks < 0 || !n_blocks_out) return PKV_ERR_INVALID_ARG;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+  const Sequence& s = it->second;
+  const int32_t nb = int32_t(s.table.size());
+  if (nb > max_blocks || (nb > 0 && !blocks_out)) return PKV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < nb; ++i) blocks_out[i] = s.table[i];
+  *n_blocks_out = nb;
+  a->swapped[seq_id] = {s.len, nb};
+  for (int32_t b : s.table)
+    if (--a->ref[b] == 0) a->free_stack.push_back(b);
+  a->seqs.erase(it);
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_swap_in(pkv_alloc* a, int64_t seq_id, int32_t max_blocks, int32_t* blocks_out,
+                           int32_t* n_blocks_out) {
+  if (!a || max_blocks < 0 || !n_blocks_out) return PKV_ERR_INVALID_ARG;
+  auto it = a->swapped.find(seq_id);
+  if (it == a->swapped.end()) return PKV_ERR_UNKNOWN_SEQ;
+  const int32_t len = it->second.first, nb = it->second.second;
+  if (nb > max_blocks || (nb > 0 && !blocks_out)) return PKV_ERR_INVALID_ARG;
+  if (nb > int32_t(a->free_stack.size())) return PKV_ERR_OUT_OF_BLOCKS;
+  Sequence s;
+  s.len = len;
+  s.table.reserve(nb);
+  for (int32_t i = 0; i < nb; ++i) {
+    s.table.push_back(a->pop());
+    blocks_out[i] = s.table.back();
+  }
+  *n_blocks_out = nb;
+  a->swapped.erase(it);
+  a->seqs.emplace(seq_id, std::move(s));
   return PKV_OK;
 }
 

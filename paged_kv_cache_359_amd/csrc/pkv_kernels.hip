@@ -910,6 +910,29 @@ __global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict_
   lens[r] = p + 1;
 }
 
+// Whole-block moves between the pools and a contiguous buffer (swap preemption): with
+// OUT, dst[i] = pool[blocks[i]]; otherwise pool[blocks[i]] = src[i].  Ids outside
+// [0, num_blocks) are skipped.
+template <bool OUT>
+__global__ __launch_bounds__(256) void move_blocks_kernel(uint4* k_cache, uint4* v_cache,
+                                                          uint4* k_buf, uint4* v_buf,
+                                                          const int32_t* __restrict__ blocks,
+                                                          int64_t blk_vecs, int32_t num_blocks) {
+  const int32_t id = blocks[blockIdx.x];
+  if ((unsigned)id >= (unsigned)num_blocks) return;
+  const int64_t po = int64_t(id) * blk_vecs, bo = int64_t(blockIdx.x) * blk_vecs;
+  for (int64_t i = int64_t(blockIdx.y) * blockDim.x + threadIdx.x; i < blk_vecs;
+       i += int64_t(gridDim.y) * blockDim.x) {
+    if constexpr (OUT) {
+      k_buf[bo + i] = k_cache[po + i];
+      v_buf[bo + i] = v_cache[po + i];
+    } else {
+      k_cache[po + i] = k_buf[bo + i];
+      v_cache[po + i] = v_buf[bo + i];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* k_cache, uint4* v_cache,
                                                           const int32_t* __restrict__ pairs,
                                                           int64_t blk_vecs, int32_t num_blocks) {
@@ -1113,6 +1136,48 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
                      static_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
                      static_cast<uint4*>(v_cache), pairs, blk_vecs, num_blocks);
   return launch_status("copy_blocks");
+}
+
+namespace {
+pkv_status move_blocks(bool out, void* k_cache, void* v_cache, void* k_buf, void* v_buf,
+                       const int32_t* blocks, int32_t n, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, pkv_dtype dtype, void* stream) {
+  if (n < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return PKV_ERR_INVALID_ARG;
+  const int64_t blk_bytes = int64_t(num_kv_heads) * block_size * head_dim * dtype_size(dtype);
+  if (blk_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if (n == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_buf || !v_buf || !blocks) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t blk_vecs = blk_bytes / 16;
+  int64_t ychunks = (blk_vecs + 255) / 256;
+  if (ychunks > 64) ychunks = 64;
+  clear_stale_error();
+  auto k = out ? move_blocks_kernel<true> : move_blocks_kernel<false>;
+  hipLaunchKernelGGL(k, dim3(unsigned(n), unsigned(ychunks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), static_cast<uint4*>(k_buf),
+                     static_cast<uint4*>(v_buf), blocks, blk_vecs, num_blocks);
+  return launch_status(out ? "gather_blocks" : "scatter_blocks");
+}
+}  // namespace
+
+pkv_status pkv_gather_blocks(const void* k_cache, const void* v_cache, const int32_t* blocks,
+                             int32_t n_blocks, void* k_out, void* v_out, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             pkv_dtype dtype, void* stream) {
+  return move_blocks(true, const_cast<void*>(k_cache), const_cast<void*>(v_cache), k_out, v_out,
+                     blocks, n_blocks, num_kv_heads, head_dim, block_size, num_blocks, dtype, stream);
+}
+
+pkv_status pkv_scatter_blocks(const void* k_in, const void* v_in, const int32_t* blocks,
+                              int32_t n_blocks, void* k_cache, void* v_cache, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              pkv_dtype dtype, void* stream) {
+  return move_blocks(false, k_cache, v_cache, const_cast<void*>(k_in), const_cast<void*>(v_in),
+                     blocks, n_blocks, num_kv_heads, head_dim, block_size, num_blocks, dtype, stream);
 }
 
 pkv_status pkv_update_block_tables(int32_t* block_tables, int32_t* context_lens,

@@ -31,6 +31,7 @@ class GpuState:
             fill_bits(self.v_cache, c.dtype, SENTINEL_BITS[c.dtype])
         self.log = []
         self.lens = {}
+        self.host = {}  # swapped-out sequence -> (K blocks, V blocks) in host memory
         offs = torch.from_numpy(w.tok_offsets).to(device)
         self._offs = offs
 
@@ -93,6 +94,42 @@ class GpuState:
                 self.lens[seq] += n
                 if log:
                     self.log.append((op, slots.tolist(), pairs.tolist()))
+            elif kind == "swap_out":
+                flush()
+                seq = op[1]
+                blocks = self.alloc.pkv_seq_swap_out(seq, self.w.cfg.num_blocks)
+                c = self.w.cfg
+                shape = (blocks.size, c.num_kv_heads, c.block_size, c.head_dim)
+                kb = torch.empty(shape, dtype=c.torch_dtype, device=self.device)
+                vb = torch.empty_like(kb)
+                bd = torch.from_numpy(np.ascontiguousarray(blocks)).to(self.device)
+                pkv.pkv_gather_blocks(self.k_cache, self.v_cache, bd, kb, vb)
+                self.host[seq] = (kb.cpu(), vb.cpu(), self.lens.pop(seq))
+                if log:
+                    self.log.append((op, blocks.tolist(), []))
+            elif kind == "swap_in":
+                flush()
+                seq = op[1]
+                blocks = self.alloc.pkv_seq_swap_in(seq, self.w.cfg.num_blocks)
+                kb, vb, n = self.host.pop(seq)
+                bd = torch.from_numpy(np.ascontiguousarray(blocks)).to(self.device)
+                pkv.pkv_scatter_blocks(kb.to(self.device), vb.to(self.device), bd,
+                                       self.k_cache, self.v_cache)
+                self.lens[seq] = n
+                if log:
+                    self.log.append((op, blocks.tolist(), []))
+            elif kind == "junk":
+                # A sequence outside the workload whose tokens are all-zero bits.
+                flush()
+                _, seq, n = op
+                slots = self.alloc.pkv_seq_add(seq, n)
+                c = self.w.cfg
+                z = torch.zeros((n, c.num_kv_heads, c.head_dim), dtype=c.torch_dtype,
+                                device=self.device)
+                self._write(z, z, slots)
+                self.lens[seq] = n
+                if log:
+                    self.log.append((op, slots.tolist(), []))
             else:
                 flush()
                 seqs = op[1]

@@ -69,7 +69,7 @@ int main(int argc, char** argv) {
     if (pkv_alloc_create(nblocks, bs, round % 2 ? order.data() : nullptr, &a) != PKV_OK) return fail("create", -1);
     for (int it = 0; it < iters / 40; ++it) {
       const Snapshot before = snap(a, nblocks, ids);
-      const uint32_t op = below(6);
+      const uint32_t op = below(8);
       pkv_status st = PKV_OK;
       if (op == 0) {
         const int32_t n = int32_t(below(uint32_t(3 * bs + 2)));
@@ -79,6 +79,13 @@ int main(int argc, char** argv) {
         st = pkv_seq_fork(a, ids[below(8)], ids[below(8)]);
       } else if (op == 2) {
         st = pkv_seq_free(a, ids[below(8)]);
+      } else if (op == 6 || op == 7) {
+        std::vector<int32_t> blocks(size_t(nblocks) + 1);
+        int32_t nb = -1;
+        const int64_t id = ids[below(8)];
+        st = op == 6 ? pkv_seq_swap_out(a, id, nblocks, blocks.data(), &nb)
+                     : pkv_seq_swap_in(a, id, nblocks, blocks.data(), &nb);
+        if (st == PKV_OK && (nb < 0 || nb > nblocks)) return fail("swap block count", it);
       } else if (op == 5) {
         const int32_t n = int32_t(below(uint32_t(2 * bs + 3)));
         std::vector<int64_t> slots(size_t(n) + 1);

@@ -23,6 +23,7 @@ class OracleState:
             self.v_pool = oracle.new_pool(c.num_blocks, c.num_kv_heads, c.block_size,
                                           c.head_dim, c.dtype, fill)
         self.log = []  # (op, slots, cow_pairs) per operation, for comparisons
+        self.host = {}  # swapped-out sequence -> (K blocks, V blocks)
 
     def _write(self, seq, lo, hi, slots):
         if not self.cache:
@@ -66,6 +67,28 @@ class OracleState:
                 for s, p, sl in zip(seqs, pos, slots):
                     self._write(s, p, p + 1, [sl])
                 self.log.append((op, slots, pairs))
+            elif kind == "swap_out":
+                blocks = self.alloc.swap_out(op[1])
+                if self.cache:
+                    self.host[op[1]] = (oracle.gather_blocks(self.k_pool, blocks),
+                                        oracle.gather_blocks(self.v_pool, blocks))
+                self.log.append((op, blocks, []))
+            elif kind == "swap_in":
+                blocks = self.alloc.swap_in(op[1])
+                if self.cache:
+                    kb, vb = self.host.pop(op[1])
+                    oracle.scatter_blocks(self.k_pool, blocks, kb)
+                    oracle.scatter_blocks(self.v_pool, blocks, vb)
+                self.log.append((op, blocks, []))
+            elif kind == "junk":
+                _, seq, n = op
+                slots = self.alloc.add(seq, n)
+                if self.cache:
+                    c = self.w.cfg
+                    z = np.zeros((n, c.num_kv_heads, c.head_dim), self.k_pool.dtype)
+                    oracle.cache_write(self.k_pool, z, slots)
+                    oracle.cache_write(self.v_pool, z, slots)
+                self.log.append((op, slots, []))
             else:
                 raise ValueError(kind)
 

@@ -207,3 +207,29 @@ def test_update_block_tables_validation():
     assert l.pkv_update_block_tables(FAKE, FAKE, FAKE, None, FAKE, 3, 4, 8, 16, 100, None) == 1
     assert l.pkv_update_block_tables(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 4, 8, 16, 100, None) == 1
     assert l.pkv_update_block_tables(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 0, 16, 100, None) == 1
+
+
+def test_swap_block_move_validation():
+    l = lib()
+    for fn in (l.pkv_gather_blocks, l.pkv_scatter_blocks):
+        assert fn(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 2, 8, 4, 8, 1, None) == 0   # nothing to move
+        assert fn(FAKE, FAKE, None, 3, FAKE, FAKE, 2, 8, 4, 8, 1, None) == 1
+        assert fn(FAKE, FAKE, FAKE, 3, MIS, FAKE, 2, 8, 4, 8, 1, None) == 1
+        assert fn(FAKE, FAKE, FAKE, -1, FAKE, FAKE, 2, 8, 4, 8, 1, None) == 1
+        assert fn(FAKE, FAKE, FAKE, 3, FAKE, FAKE, 1, 6, 1, 8, 1, None) == 5    # 12-byte block
+
+
+def test_swap_capacity_and_unknown_ids():
+    a = pkv.PkvAlloc(8, 4)
+    a.pkv_seq_add(0, 9)
+    with pytest.raises(pkv.PkvError) as e:
+        a.pkv_seq_swap_out(0, 2)  # 3 blocks do not fit
+    assert e.value.name == "PKV_ERR_INVALID_ARG" and a.pkv_num_free_blocks() == 5
+    assert a.pkv_seq_swap_out(0, 8).tolist() == [0, 1, 2]
+    with pytest.raises(pkv.PkvError) as e:
+        a.pkv_seq_add(0, 1)
+    assert e.value.name == "PKV_ERR_DUPLICATE_SEQ"
+    with pytest.raises(pkv.PkvError) as e:
+        a.pkv_seq_swap_in(5, 8)
+    assert e.value.name == "PKV_ERR_UNKNOWN_SEQ"
+    assert a.pkv_seq_swap_in(0, 8).tolist() == [2, 1, 0] and a.pkv_seq_length(0) == 9

@@ -33,6 +33,10 @@ def run_both(o, c, kind, *args):
         elif kind == "extend":
             s, p = o.extend(*args)
             ro = ("ok", (list(s), [list(x) for x in p]))
+        elif kind == "swap_out":
+            ro = ("ok", list(o.swap_out(args[0])))
+        elif kind == "swap_in":
+            ro = ("ok", list(o.swap_in(args[0])))
         else:
             s, p = o.append(*args)
             ro = ("ok", (list(s), [list(x) for x in p]))
@@ -50,6 +54,10 @@ def run_both(o, c, kind, *args):
         elif kind == "extend":
             s, p = c.pkv_seq_extend(*args)
             rc = ("ok", (s.tolist(), p.tolist()))
+        elif kind == "swap_out":
+            rc = ("ok", c.pkv_seq_swap_out(args[0], 64).tolist())
+        elif kind == "swap_in":
+            rc = ("ok", c.pkv_seq_swap_in(args[0], 64).tolist())
         else:
             s, p = c.pkv_seq_append(*args)
             rc = ("ok", (s.tolist(), p.tolist()))
@@ -79,7 +87,8 @@ def same_state(o, c):
     assert c.pkv_usage() == o.usage()
 
 
-ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "append", "free", "extend"]),
+ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "append", "free", "extend", "swap_out",
+                                          "swap_in"]),
                          st.integers(0, 6), st.integers(0, 6), st.integers(0, 11)),
                min_size=1, max_size=80)
 
@@ -100,6 +109,8 @@ def test_random_operation_sequences(ops, bs, nblocks, seed, use_order):
             args = (x,)
         elif kind == "extend":
             args = (x, n)
+        elif kind in ("swap_out", "swap_in"):
+            args = (x,)
         else:
             # Mostly distinct ids; sometimes a repeated id (an error on both sides).
             ids = [x, y, (x + n) % 7] if n % 5 else [x, x]

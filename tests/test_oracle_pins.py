@@ -141,7 +141,7 @@ def check_invariants(a: oracle.OracleAllocator):
 
 
 op_strategy = st.lists(
-    st.tuples(st.sampled_from(["add", "fork", "append", "free"]),
+    st.tuples(st.sampled_from(["add", "fork", "append", "free", "swap_out", "swap_in", "extend"]),
               st.integers(0, 5), st.integers(0, 5), st.integers(0, 9)),
     min_size=1, max_size=60)
 
@@ -154,7 +154,7 @@ def test_allocator_invariants_random_ops(ops, bs, nblocks, seed):
     a = oracle.OracleAllocator(nblocks, bs, order)
     for kind, x, y, n in ops:
         before = (list(a.free), list(a.ref), {k: list(v) for k, v in a.tables.items()},
-                  dict(a.lens))
+                  dict(a.lens), dict(a.swapped))
         try:
             if kind == "add":
                 a.add(x, n)
@@ -162,6 +162,16 @@ def test_allocator_invariants_random_ops(ops, bs, nblocks, seed):
                 a.fork(x, y)
             elif kind == "free":
                 a.free_seq(x)
+            elif kind == "extend":
+                a.extend(x, n)
+            elif kind == "swap_out":
+                length, blocks = a.lens.get(x), list(a.tables.get(x, []))
+                out = a.swap_out(x)
+                assert out == blocks and a.swapped[x] == (length, len(blocks)) and x not in a.tables
+            elif kind == "swap_in":
+                length, nb = a.swapped.get(x, (None, None))
+                new = a.swap_in(x)
+                assert len(new) == nb and a.lens[x] == length and all(a.ref[b] == 1 for b in new)
             else:
                 seqs = sorted({x, y})
                 shared_before = {s: (a.tables[s][-1] if s in a.tables and a.tables[s] else None,
@@ -177,7 +187,7 @@ def test_allocator_invariants_random_ops(ops, bs, nblocks, seed):
                     assert a.ref[new] == 1 and a.ref[old] >= 1
                     assert any(shared_before[s][0] == old for s in seqs)
         except oracle.OracleError:
-            after = (a.free, a.ref, a.tables, a.lens)
+            after = (a.free, a.ref, a.tables, a.lens, a.swapped)
             assert after == before  # failed calls change nothing
         check_invariants(a)
 
@@ -525,3 +535,69 @@ def test_last_prefill_row_equals_decode():
     dec = paged(last, kv, 4, 20, None, 0.25)
     for b in range(2):
         np.testing.assert_array_equal(out[qs[b + 1] - 1], dec[b])
+
+
+
+# --------------------------------------------------------------------------------------
+# Swap preemption: a sequence's cache leaves for the host and comes back in fresh blocks
+# --------------------------------------------------------------------------------------
+def test_swap_round_trip_restores_the_sequence():
+    rng = np.random.default_rng(12)
+    bs, d, hkv = 4, 8, 2
+    a = oracle.OracleAllocator(16, bs, rng.permutation(16))
+    kp = oracle.new_pool(16, hkv, bs, d, "f32", fill=0x7FC00001)
+    vp = oracle.new_pool(16, hkv, bs, d, "f32", fill=0x7FC00001)
+    toks = {}
+    for s, n in ((0, 9), (1, 6), (2, 13)):
+        k = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+        slots = a.add(s, n)
+        oracle.cache_write(kp, k.view(np.uint32), slots)
+        oracle.cache_write(vp, v.view(np.uint32), slots)
+        toks[s] = (k, v)
+    a.fork(1, 3)  # sequence 1's blocks are shared with 3
+    q = rng.standard_normal((4, 2 * hkv, d)).astype(np.float32)
+
+    def dec():
+        mb = max(len(t) for t in a.tables.values())
+        tables, lens = a.block_tables([0, 1, 2, 3], mb)
+        return oracle.decode(q.view(np.uint32), kp, vp, tables, lens, 0.3, "f32")
+
+    ref = dec()
+    host = {}
+    for s in (1, 0):  # 1 shares its blocks with 3: those stay on the device for 3
+        blocks = a.swap_out(s)
+        host[s] = (oracle.gather_blocks(kp, blocks), oracle.gather_blocks(vp, blocks))
+        check_invariants(a)
+    assert 1 not in a.tables and a.swapped[1] == (6, 2)
+    with pytest.raises(oracle.DuplicateSeq):
+        a.add(1, 3)  # the id is still taken while swapped out
+    # Somebody else takes and overwrites the freed blocks meanwhile.
+    junk = a.add(9, 4 * (a.num_free() - 5))
+    oracle.cache_write(kp, np.zeros((len(junk), hkv, d), np.uint32), junk)
+    a.free_seq(9)
+    for s in (0, 1):
+        new = a.swap_in(s)
+        oracle.scatter_blocks(kp, new, host[s][0])
+        oracle.scatter_blocks(vp, new, host[s][1])
+        check_invariants(a)
+    assert a.ref[a.tables[1][0]] == 1  # the restored sequence owns its blocks
+    np.testing.assert_array_equal(dec(), ref)
+    for s in (0, 1):  # the logical cache reads back token for token
+        k, v = toks[s]
+        for g in range(hkv):
+            got = oracle.gather(kp, a.tables[s], a.lens[s], g)
+            assert np.array_equal(got, k[:, g].view(np.uint32))
+
+
+def test_swap_in_without_room_changes_nothing():
+    a = oracle.OracleAllocator(4, 2)
+    a.add(0, 5)  # 3 blocks
+    a.swap_out(0)
+    a.add(1, 4)  # 2 of the 4 blocks
+    before = (list(a.free), list(a.ref), dict(a.tables), dict(a.lens), dict(a.swapped))
+    with pytest.raises(oracle.OutOfBlocks):
+        a.swap_in(0)
+    assert (a.free, a.ref, a.tables, a.lens, a.swapped) == before
+    a.free_seq(1)
+    assert len(a.swap_in(0)) == 3 and a.lens[0] == 5
