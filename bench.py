@@ -33,13 +33,23 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_359_amd", "csrc", "pkv_kernels.hip")
+CSRC = os.path.join(ROOT, "paged_kv_cache_359_amd", "csrc")
+# Sources the decode kernels are built from: counters taken on them stay valid while these
+# files are unchanged.
+DECODE_SOURCES = ["device.h", "mfma_tile.h", "host.h", "decode.hip"]
+
+
+def decode_source_sha():
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
 
 
 def counted_traffic(config_name):
     """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
     of this workload (scaled by a 1 GiB copy's counts), or None when there is none or the
-    kernel source has changed since the counters were taken."""
+    decode sources have changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"paged_decode_{config_name}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -48,8 +58,7 @@ def counted_traffic(config_name):
         if ":" in line and not line.startswith(" "):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("decode_source_sha256") != decode_source_sha() or "traffic_bytes_per_launch" not in fields:
         return None
     return {"bytes_per_launch": int(fields["traffic_bytes_per_launch"]),
             "over_algorithmic": float(fields["traffic_over_algorithmic"]),
@@ -74,6 +83,13 @@ def parse():
                          "previous step's decode (whole tables uploaded per step)")
     ap.add_argument("--check", action="store_true",
                     help="verify every timed step's output against a serial re-decode")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure swap preemption (swap out and back in) instead of decode")
+    ap.add_argument("--swap-every", type=int, default=8,
+                    help="--swap: every n-th sequence of the batch is a victim")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write the profiles/ summaries of --config from rocprofv3 output in DIR "
+                         "(kt_<config>/, pmc_fetch_<config>/, pmc_write_<config>/, kt_<config>.log)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (scales HBM counters)")
     return ap.parse_args()
@@ -263,6 +279,48 @@ def main_prefill(args, cfg):
     print(json.dumps(res), flush=True)
 
 
+def build_resident(w, dev):
+    """The C++ allocator and both pools holding every sequence's existing context, written
+    with the workload's own set-up operations (untimed)."""
+    import torch
+    import workloads as W
+    import paged_kv_cache_359_amd as pkv
+    c = w.cfg
+    bs = c.block_size
+    alloc = pkv.PkvAlloc(c.num_blocks, bs, w.free_order)
+    shape = (c.num_blocks, c.num_kv_heads, bs, c.head_dim)
+    k_cache = torch.zeros(shape, dtype=c.torch_dtype, device=dev)
+    v_cache = torch.zeros(shape, dtype=c.torch_dtype, device=dev)
+    lens_host = {}
+    for op in W.setup_ops(w):
+        if op[0] == "add":
+            _, s, n = op
+            slots = alloc.pkv_seq_add(s, n)
+            lens_host[s] = n
+            if n:
+                k, v = w.token_kv(0 if s == W.PARENT else s, 0, n)
+                pkv.pkv_reshape_and_cache(k.contiguous(), v.contiguous(),
+                                          torch.from_numpy(slots).to(dev), k_cache, v_cache)
+        elif op[0] == "fork":
+            alloc.pkv_seq_fork(op[1], op[2])
+            lens_host[op[2]] = lens_host[op[1]]
+        elif op[0] == "free":
+            alloc.pkv_seq_free(op[1])
+            del lens_host[op[1]]
+        else:
+            seqs = op[1]
+            pos = np.array([lens_host[s] for s in seqs])
+            slots, pairs = alloc.pkv_seq_append(seqs)
+            if pairs.size:
+                pkv.pkv_copy_blocks(k_cache, v_cache, torch.from_numpy(pairs).to(dev))
+            idx = torch.from_numpy(w.tok_offsets[np.asarray(seqs)] + pos - c.prefix_len).to(dev)
+            pkv.pkv_reshape_and_cache(w.k_tok.index_select(0, idx), w.v_tok.index_select(0, idx),
+                                      torch.from_numpy(slots).to(dev), k_cache, v_cache)
+            for s in seqs:
+                lens_host[s] += 1
+    return alloc, k_cache, v_cache
+
+
 def overlapped_steps(args, alloc, ids, B, max_blocks, NBUF, k_cache, v_cache, k_new, v_new, q,
                      out, workspace, max_len_final, c, stream, ev, host_s, saved, use_hint, dev):
     """The --overlap step: step s's uploads, copy-on-write copies and cache write run on a
@@ -326,12 +384,238 @@ def overlapped_steps(args, alloc, ids, B, max_blocks, NBUF, k_cache, v_cache, k_
     return step, (lambda: last[0])
 
 
+def main_swap(args):
+    """One step = one swap cycle of the victims (every --swap-every-th sequence of the batch):
+    swap-out (the allocator releases each victim's blocks; pkv_gather_blocks copies them into
+    a device staging buffer; one DMA copy takes that to pinned host memory), then swap-in (the
+    allocator hands out fresh blocks; one DMA copy back; pkv_scatter_blocks writes them into
+    the pools).  ``value`` counts the K/V bytes moved in both directions per second of the
+    whole cycle (host link included); ``roofline`` rates the gather kernel (each byte read
+    from and written to HBM once).  A decode of the whole batch before the first and after the
+    last cycle must be bit-identical."""
+    import torch
+    import workloads as W
+    import paged_kv_cache_359_amd as pkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    c = W.get_config(args.config, steps=1)
+    print(f"[bench] building {c.name}: {c.batch} sequences (swap)", file=sys.stderr, flush=True)
+    w = W.make_workload(c, device=dev)
+    B, bs = w.batch, c.block_size
+    alloc, k_cache, v_cache = build_resident(w, dev)
+    victims = list(range(0, B, max(1, args.swap_every)))
+    nblk = sum(-(-int(alloc.pkv_seq_length(v)) // bs) for v in victims)
+    shape = (nblk, c.num_kv_heads, bs, c.head_dim)
+    k_stage = torch.empty(shape, dtype=c.torch_dtype, device=dev)
+    v_stage = torch.empty_like(k_stage)
+    k_host = torch.empty(shape, dtype=c.torch_dtype, pin_memory=True)
+    v_host = torch.empty(shape, dtype=c.torch_dtype, pin_memory=True)
+    ids_h = [torch.empty(nblk, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    ids_d = [torch.empty(nblk, dtype=torch.int32, device=dev) for _ in range(2)]
+    moved = 2 * k_stage.numel() * k_stage.element_size()  # K and V bytes, one direction
+    stream = torch.cuda.current_stream(dev)
+
+    max_ctx = int(w.lengths.max())
+    max_blocks = -(-max_ctx // bs)
+    ws = torch.empty(max(16, pkv.pkv_decode_workspace_bytes(B, c.num_q_heads, c.num_kv_heads,
+                                                            c.head_dim, bs, max_ctx, c.dtype, -1)),
+                     dtype=torch.uint8, device=dev)
+
+    def decode():
+        t, l = alloc.pkv_get_block_tables(np.arange(B), max_blocks)
+        o = torch.empty_like(w.q[0])
+        pkv.pkv_paged_attention_decode(o, w.q[0], k_cache, v_cache, torch.from_numpy(t).to(dev),
+                                       torch.from_numpy(l).to(dev), max_ctx, c.scale, -1, ws)
+        return o
+
+    before = decode()
+    total = args.warmup + args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
+    host_s = [0.0]
+
+    def cycle(i):
+        e = ev[i]
+        h0 = time.perf_counter()
+        out_ids, n = ids_h[0].numpy(), 0
+        for v in victims:
+            blk = alloc.pkv_seq_swap_out(v, nblk)
+            out_ids[n:n + blk.size] = blk
+            n += blk.size
+        host_s[0] += time.perf_counter() - h0
+        ids_d[0].copy_(ids_h[0], non_blocking=True)
+        e[0].record(stream)
+        pkv.pkv_gather_blocks(k_cache, v_cache, ids_d[0], k_stage, v_stage)
+        e[1].record(stream)
+        k_host.copy_(k_stage, non_blocking=True)
+        v_host.copy_(v_stage, non_blocking=True)
+        e[2].record(stream)
+        h0 = time.perf_counter()
+        in_ids, n = ids_h[1].numpy(), 0
+        for v in victims:
+            blk = alloc.pkv_seq_swap_in(v, nblk)
+            in_ids[n:n + blk.size] = blk
+            n += blk.size
+        host_s[0] += time.perf_counter() - h0
+        ids_d[1].copy_(ids_h[1], non_blocking=True)
+        k_stage.copy_(k_host, non_blocking=True)
+        v_stage.copy_(v_host, non_blocking=True)
+        e[3].record(stream)
+        pkv.pkv_scatter_blocks(k_stage, v_stage, ids_d[1], k_cache, v_cache)
+        e[4].record(stream)
+        stream.synchronize()  # the pinned id buffers are rewritten next cycle
+
+    for i in range(args.warmup):
+        cycle(i)
+    torch.cuda.synchronize()
+    host_s[0] = 0.0
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        cycle(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    after = decode()
+    if not torch.equal(before, after):
+        raise SystemExit("[bench] swap check failed: decode differs after the swap cycles")
+
+    K = args.steps
+    ms = (t1 - t0) * 1e3 / K
+    timed = range(args.warmup, total)
+    span = lambda a, b: float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in timed]))
+    g_ms, d2h_ms, h2d_ms, s_ms = span(0, 1), span(1, 2), span(2, 3), span(3, 4)
+    gbs = lambda nbytes, t: round(nbytes / (t * 1e-3) / 1e9, 3)
+    res = {
+        "metric": "swap preemption K/V GB/s (out + in, host link included), 1 GPU",
+        "value": gbs(2 * moved, ms), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": f"swap, {c.name}: {len(victims)} of {B} sequences "
+                               f"({nblk} blocks, {moved / 1e6:.1f} MB of K/V) out to pinned host "
+                               f"memory and back, Hkv={c.num_kv_heads}, D={c.head_dim}, block={bs}, "
+                               f"{c.dtype} KV",
+                   "victims": len(victims), "blocks": nblk, "bytes_each_way": moved},
+        "gather_kernel_ms": round(g_ms, 5), "scatter_kernel_ms": round(s_ms, 5),
+        "d2h_ms": round(d2h_ms, 5), "h2d_ms": round(h2d_ms, 5),
+        "d2h_GBs": gbs(moved, d2h_ms), "h2d_GBs": gbs(moved, h2d_ms),
+        "scatter_GBs": gbs(2 * moved, s_ms),
+        "host_ms_per_step": round(host_s[0] * 1e3 / K, 4),
+        "checked": True,
+        "roofline": {"bound": "hbm", "achieved": gbs(2 * moved, g_ms), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(2 * moved / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                     "traffic": None, "kernel": "gather_blocks (swap-out staging)",
+                     "bytes_per_launch": 2 * moved},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def summarize(config, outdir):
+    """Writes profiles/paged_decode_<config>_kernel_trace.txt and _hbm_traffic.txt from the
+    rocprofv3 output of the three runs named in those files (one kernel trace, one
+    FETCH_SIZE run, one WRITE_SIZE run, each of bench.py on this config)."""
+    import csv
+    import workloads as W
+
+    C = config
+    rel = os.path.relpath(outdir, ROOT)
+    sha = decode_source_sha()
+    short = lambda n: (n.replace("void ", "").split("(")[0] if "pkv::" in n else n)[:70]
+    stats = list(csv.DictReader(open(os.path.join(outdir, f"kt_{C}", f"{C}_kernel_stats.csv"))))
+    bj = json.loads([l for l in open(os.path.join(outdir, f"kt_{C}.log")) if l.startswith("{")][-1])
+
+    def counter(run, name):
+        path = os.path.join(outdir, run, f"{C}_counter_collection.csv")
+        return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == name]
+
+    fetch, write = counter(f"pmc_fetch_{C}", "FETCH_SIZE"), counter(f"pmc_write_{C}", "WRITE_SIZE")
+    # The calibration copy (1 GiB read and written) is the largest copyBuffer of each run.
+    cal_f = max(float(r["Counter_Value"]) for r in fetch if "copyBuffer" in r["Kernel_Name"])
+    cal_w = max(float(r["Counter_Value"]) for r in write if "copyBuffer" in r["Kernel_Name"])
+    gib_kib = 1 << 20
+    ff, fw = gib_kib / cal_f, gib_kib / cal_w
+
+    cfg = W.get_config(C, steps=3)
+    lengths = W.draw_lengths(cfg)
+    kvpt = 2 * cfg.num_kv_heads * cfg.head_dim * cfg.dsize
+    alg = [kvpt * int(np.sum(lengths + k)) for k in range(3)]
+
+    def per_kernel(rows):
+        out = {}
+        for r in rows:
+            n = r["Kernel_Name"]
+            if n.startswith("void pkv::decode") or n.startswith("void pkv::reduce"):
+                out.setdefault(short(n), []).append(float(r["Counter_Value"]))
+        return out
+
+    pf, pw = per_kernel(fetch), per_kernel(write)
+    main_k = [k for k in pf if "decode" in k][0]
+    red = [k for k in pf if "reduce" in k]
+    run = "python3 bench.py --config {} --steps 2 --warmup 1 --no-cpu-baseline --calib-copy".format(C)
+    T = [f"HBM traffic of the paged decode kernels, {C} workload, one MI355X (gfx950).", "",
+         "Commands (repository root on the GPU box; one counter per run), then the summary:",
+         f"  rocprofv3 --pmc FETCH_SIZE -f csv -d {rel}/pmc_fetch_{C} -o {C} -- {run}",
+         f"  rocprofv3 --pmc WRITE_SIZE -f csv -d {rel}/pmc_write_{C} -o {C} -- {run}",
+         f"  python3 bench.py --config {C} --summarize {rel}",
+         f"decode_source_sha256: {sha}", "",
+         "Calibration: --calib-copy runs one 1 GiB device-to-device copy (__amd_rocclr_copyBuffer)",
+         "that reads and writes exactly 1048576 KiB.",
+         f"  FETCH_SIZE of the copy: {cal_f:.1f} KiB -> read scale factor {ff:.5f}",
+         f"  WRITE_SIZE of the copy: {cal_w:.1f} KiB -> write scale factor {fw:.5f}", "",
+         "Per dispatch (steps 0, 1, 2 of the run; KiB as counted, then scaled bytes):"]
+    tot = []
+    for i in range(len(pf[main_k])):
+        f_m, w_m = pf[main_k][i], pw[main_k][i]
+        f_r, w_r = (pf[red[0]][i], pw[red[0]][i]) if red else (0.0, 0.0)
+        b = (f_m + f_r) * ff * 1024 + (w_m + w_r) * fw * 1024
+        tot.append(b)
+        T.append(f"  step {i}: {main_k} FETCH {f_m:.1f} WRITE {w_m:.1f}; "
+                 + (f"{red[0]} FETCH {f_r:.1f} WRITE {w_r:.1f}; " if red else "")
+                 + f"scaled total {b / 1e9:.4f} GB; algorithmic K/V bytes {alg[i] / 1e9:.4f} GB; "
+                 f"ratio {b / alg[i]:.4f}")
+    T += ["", f"traffic_bytes_per_launch: {int(round(np.mean(tot)))}",
+          f"algorithmic_bytes_per_launch: {int(round(np.mean(alg)))}",
+          f"traffic_over_algorithmic: {np.mean(tot) / np.mean(alg):.4f}"]
+    open(os.path.join(ROOT, "profiles", f"paged_decode_{C}_hbm_traffic.txt"), "w").write("\n".join(T) + "\n")
+
+    r0 = bj["roofline"]
+    L = [f"Kernel trace of the paged decode benchmark, {C} workload, one MI355X (gfx950).", "",
+         "Command (repository root on the GPU box), then the summary:",
+         f"  rocprofv3 --kernel-trace --stats -f csv -d {rel}/kt_{C} -o {C} -- python3 bench.py "
+         f"--config {C} --steps 16 --warmup 4 --no-cpu-baseline > {rel}/kt_{C}.log",
+         f"  python3 bench.py --config {C} --summarize {rel}",
+         f"decode_source_sha256: {sha}", "",
+         "bench.py line of the same run (HIP events on the launch stream, 16 timed steps):",
+         f"  decode_kernel_ms {bj['decode_kernel_ms']}  roofline.achieved {r0['achieved']} GB/s  "
+         f"frac {r0['frac']}  bytes_per_launch {r0['bytes_per_launch']}  step value {bj['value']} GB/s  "
+         f"ms_per_step {bj['ms_per_step']}", "",
+         "Kernel statistics (all dispatches of the run, including set-up; ns):",
+         f"  {'kernel':72s} {'calls':>6s} {'avg':>11s} {'min':>9s} {'max':>9s} {'share%':>7s}"]
+    for r in stats:
+        L.append(f"  {short(r['Name']):72s} {r['Calls']:>6s} {float(r['AverageNs']):11.1f} "
+                 f"{r['MinNs']:>9s} {r['MaxNs']:>9s} {float(r['Percentage']):7.2f}")
+    dm = [r for r in stats if r["Name"].startswith("void pkv::decode")][0]
+    rr = [r for r in stats if r["Name"].startswith("void pkv::reduce")]
+    avg = float(dm["AverageNs"]) + (float(rr[0]["AverageNs"]) if rr else 0.0)
+    L += ["", f"Decode call = {short(dm['Name'])} ({float(dm['AverageNs']) / 1e3:.2f} us avg)"
+          + (f" + {short(rr[0]['Name'])} ({float(rr[0]['AverageNs']) / 1e3:.2f} us avg)" if rr else "")
+          + f" = {avg / 1e3:.2f} us per launch;",
+          f"bench.py's event-timed decode call: {bj['decode_kernel_ms'] * 1e3:.2f} us (the events "
+          "also cover launch overhead" + (" and the gap between the two kernels)." if rr else ").")]
+    open(os.path.join(ROOT, "profiles", f"paged_decode_{C}_kernel_trace.txt"), "w").write("\n".join(L) + "\n")
+    print("\n".join(L + [""] + T))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the paged decode path here runs on a single GPU).", file=sys.stderr)
         sys.exit(2)
+
+    if args.summarize:
+        return summarize(args.config, args.summarize)
+    if args.swap:
+        return main_swap(args)
 
     import torch
     import workloads as W
@@ -349,37 +633,7 @@ def main():
     B, bs = w.batch, c.block_size
 
     # ---- resident state: allocator + pools holding every sequence's existing context ----
-    alloc = pkv.PkvAlloc(c.num_blocks, bs, w.free_order)
-    shape = (c.num_blocks, c.num_kv_heads, bs, c.head_dim)
-    k_cache = torch.zeros(shape, dtype=c.torch_dtype, device=dev)
-    v_cache = torch.zeros(shape, dtype=c.torch_dtype, device=dev)
-    lens_host = {}
-    for op in W.setup_ops(w):
-        if op[0] == "add":
-            _, s, n = op
-            slots = alloc.pkv_seq_add(s, n)
-            lens_host[s] = n
-            if n:
-                k, v = w.token_kv(0 if s == W.PARENT else s, 0, n)
-                pkv.pkv_reshape_and_cache(k.contiguous(), v.contiguous(),
-                                          torch.from_numpy(slots).to(dev), k_cache, v_cache)
-        elif op[0] == "fork":
-            alloc.pkv_seq_fork(op[1], op[2])
-            lens_host[op[2]] = lens_host[op[1]]
-        elif op[0] == "free":
-            alloc.pkv_seq_free(op[1])
-            del lens_host[op[1]]
-        else:
-            seqs = op[1]
-            pos = np.array([lens_host[s] for s in seqs])
-            slots, pairs = alloc.pkv_seq_append(seqs)
-            if pairs.size:
-                pkv.pkv_copy_blocks(k_cache, v_cache, torch.from_numpy(pairs).to(dev))
-            idx = torch.from_numpy(w.tok_offsets[np.asarray(seqs)] + pos - c.prefix_len).to(dev)
-            pkv.pkv_reshape_and_cache(w.k_tok.index_select(0, idx), w.v_tok.index_select(0, idx),
-                                      torch.from_numpy(slots).to(dev), k_cache, v_cache)
-            for s in seqs:
-                lens_host[s] += 1
+    alloc, k_cache, v_cache = build_resident(w, dev)
 
     # ---- per-step inputs, resident in HBM: the appended token's K/V and the query ----
     base = w.tok_offsets[:B] + (w.lengths - 1 - c.prefix_len)

@@ -4,6 +4,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -13,7 +14,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-SOURCES = ["allocator.cpp", "pkv_kernels.hip"]
+SOURCES = ["allocator.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
 
 # Device code is built without packed-fp32 instructions (compiler-generated v_pk_* fp32 ops
 # are avoided on this target); the host pass only warns that it does not know the feature.
@@ -24,9 +25,9 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 def build(verbose: bool = False, extra_flags=None) -> str:
     hipcc = os.path.join(ROCM, "bin", "hipcc")
-    objs = []
     tmp = LIB + ".tmp"
-    for src in SOURCES:
+
+    def compile_one(src):
         path = os.path.join(CSRC, src)
         obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
@@ -34,7 +35,10 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True, capture_output=not verbose)
-        objs.append(obj)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -1,0 +1,540 @@
+// Paged decode attention for gfx950 (CDNA4): one query token per (sequence, head) attends
+// over its cached K/V, gathered block by block through the block table ("vLLM +
+// PagedAttention：打造高并发LLM推理引擎", step 3 under "它是怎么工作的？"; "PagedAttention 与
+// vLLM 推理加速", §2.3), tiled so that scores are never written to memory and the softmax is
+// computed online ("vLLM 推理加速：PagedAttention、FlashAttention 与动态批处理",
+// FlashAttention section: IO-aware tiling that never materialises the score matrix).
+// Two inner loops: VALU (any head layout; DPP row reductions) and MFMA (grouped-query heads
+// sharing one K/V tile form the columns of small matrix products).  One workgroup per
+// (sequence, head or head group, partition); reduce_partitions merges partitions.
+#include "device.h"
+#include "host.h"
+#include "mfma_tile.h"
+
+namespace pkv {
+
+// =========================================================================================
+// VALU inner loop.  One wave streams the chunk of CT tokens starting at cs (tokens >= t1 are
+// masked): J loads of 16 bytes per lane for K and for V, a fully used 1 KiB per wave-wide load
+// for 128-wide fp16.  Each group of LPT lanes (a "row") keeps its own online-softmax state
+// (running max m, running sum l, unnormalised output o) for the tokens it sees, so the loop
+// needs no communication beyond the DPP sum of the dot product.
+// =========================================================================================
+template <int DT, int D, int BS>
+struct Valu {
+  static constexpr int ES = elt_size(DT);
+  static constexpr int VEC = valu_vec(DT);
+  static constexpr int LPT = valu_lpt(DT, D);
+  static_assert(LPT >= 1 && LPT <= 32 && (LPT & (LPT - 1)) == 0, "unsupported head_dim");
+  static constexpr int TPL = valu_tpl(DT, D);
+  static constexpr int J = valu_j(DT, D);
+  static constexpr int CT = valu_chunk_tokens(DT, D);
+  static constexpr bool UNIFORM = TPL <= BS;  // a wave-wide load stays inside one block
+  static constexpr int NBC = (UNIFORM && BS < CT) ? CT / BS : 1;
+
+  struct State {
+    float m, l, o[VEC];
+  };
+
+  __device__ static void init(State& s) {
+    s.m = kNegInf;
+    s.l = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) s.o[i] = 0.f;
+  }
+
+  // kb / vb: pool base plus this lane's (KV head, column) offset.  cached: read this chunk
+  // through the caches (wave-uniform).
+  __device__ static void chunk(const DecodeArgs& a, const int32_t* tbl, const char* kb,
+                               const char* vb, size_t blk_bytes, int row, int cs, int t1,
+                               bool cached, const uint4& qv, State& st) {
+    bool need_mask = cs + CT > t1;  // wave-uniform
+    uint4 kr[J], vr[J];
+    bool ok[J];
+    size_t off[J];
+    if constexpr (UNIFORM) {
+      int ids[NBC];
+#pragma unroll
+      for (int k = 0; k < NBC; ++k) {
+        const int first = cs + k * BS;  // first token of the k-th block of this chunk
+        ids[k] = uniform(first < t1 ? tbl[first / BS] : -1);
+        need_mask |= (unsigned)ids[k] >= (unsigned)a.num_blocks;
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int id = ids[NBC > 1 ? (j * TPL) / BS : 0];
+        const int tok = cs + j * TPL + row;
+        const bool valid = (unsigned)id < (unsigned)a.num_blocks;
+        ok[j] = valid && tok < t1;
+        off[j] = size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * ES;
+      }
+    } else {
+      need_mask = true;  // per-lane block ids: always mask (generic path)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int tok = cs + j * TPL + row;
+        const int id = tok < t1 ? tbl[tok / BS] : -1;
+        const bool valid = (unsigned)id < (unsigned)a.num_blocks;
+        ok[j] = valid && tok < t1;
+        off[j] = size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * ES;
+      }
+    }
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        kr[j] = load_cached(kb + off[j]);
+        vr[j] = load_cached(vb + off[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        kr[j] = load_stream(kb + off[j]);
+        vr[j] = load_stream(vb + off[j]);
+      }
+    }
+    float s[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) s[j] = group_sum<LPT>(dot16<DT>(kr[j], qv, 0.f)) * a.scale_log2;
+    if (need_mask) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        s[j] = ok[j] ? s[j] : kNegInf;
+        if (!ok[j]) vr[j] = make_uint4(0, 0, 0, 0);  // unused slots may hold anything
+      }
+    }
+    float cm = s[0];
+#pragma unroll
+    for (int j = 1; j < J; ++j) cm = fmaxf(cm, s[j]);
+    const float mn = fmaxf(st.m, cm);
+    const float mu = mn == kNegInf ? 0.f : mn;  // no token seen yet: keep everything at 0
+    const float alpha = exp2_hw(st.m - mu);
+    st.m = mn;
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) st.o[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float pj = exp2_hw(s[j] - mu);
+      st.l += pj;
+      axpy16<DT, VEC>(st.o, pj, vr[j]);
+    }
+  }
+
+  // Merges the TPL row states of a wave through cross-lane exchanges; afterwards every lane
+  // holds the wave's (m, l) and the output columns col * VEC .. + VEC of the merged state.
+  __device__ static void merge_wave(State& st) {
+    float M = st.m;
+#pragma unroll
+    for (int s = LPT; s < 64; s <<= 1) M = fmaxf(M, __shfl_xor(M, s, 64));
+    const float w = st.m == kNegInf ? 0.f : exp2_hw(st.m - M);
+    st.m = M;
+    st.l *= w;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) st.o[i] *= w;
+#pragma unroll
+    for (int s = LPT; s < 64; s <<= 1) {
+      st.l += __shfl_xor(st.l, s, 64);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) st.o[i] += __shfl_xor(st.o[i], s, 64);
+    }
+  }
+};
+
+// VALU decode: one workgroup of NW waves per (sequence, query head, partition); the waves
+// take the partition's chunks in turn, merge their row states within the wave, and then the
+// NW wave states through LDS.
+template <int DT, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
+  using V = Valu<DT, D, BS>;
+  __shared__ float s_o[NW][D];
+  __shared__ float s_m[NW];
+  __shared__ float s_l[NW];
+
+  const int h = blockIdx.x;
+  const int part = blockIdx.y;
+  const int b = blockIdx.z;
+  const int ctx = clamp_ctx(a, b);
+  const int tid = threadIdx.x;
+  const size_t out_row = (size_t(b) * a.num_q_heads + h) * D;
+  if (ctx == 0) {
+    if (part == 0)
+      for (int d = tid; d < D; d += NW * 64) store_elt<DT>(a.out, out_row + d, 0.f);
+    return;
+  }
+  const int t0 = part * a.part_size;
+  if (t0 >= ctx) return;
+  const int t1 = min(ctx, t0 + a.part_size);
+  const int nparts = (ctx + a.part_size - 1) / a.part_size;
+
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int row = lane / V::LPT;
+  const int col = lane % V::LPT;
+  const int kvh = h / a.group;
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
+  const size_t lane_off = (size_t(kvh) * BS * D + size_t(col) * V::VEC) * V::ES;
+  const char* kb = static_cast<const char*>(a.k_cache) + lane_off;
+  const char* vb = static_cast<const char*>(a.v_cache) + lane_off;
+  const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * V::ES;
+  const uint4 qv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                    (out_row + size_t(col) * V::VEC) * V::ES);
+  const int ncached = cached_blocks(a, b);
+  typename V::State st;
+  V::init(st);
+  const int nchunks = (t1 - t0 + V::CT - 1) / V::CT;
+  for (int c = wave; c < nchunks; c += NW) {
+    const int cs = t0 + c * V::CT;
+    V::chunk(a, tbl, kb, vb, blk_bytes, row, cs, t1, cs / BS < ncached, qv, st);
+  }
+
+  V::merge_wave(st);
+  if (row == 0) {
+#pragma unroll
+    for (int i = 0; i < V::VEC; ++i) s_o[wave][col * V::VEC + i] = st.o[i];
+    if (col == 0) {
+      s_m[wave] = st.m;
+      s_l[wave] = st.l;
+    }
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += NW * 64) {
+    float M = kNegInf;
+#pragma unroll
+    for (int r = 0; r < NW; ++r) M = fmaxf(M, s_m[r]);
+    float L = 0.f, O = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int r = 0; r < NW; ++r) {
+        const float w = exp2_hw(s_m[r] - M);
+        L += s_l[r] * w;
+        O += s_o[r][d] * w;
+      }
+    }
+    if (nparts == 1) {
+      store_elt<DT>(a.out, out_row + d, L > 0.f ? O / L : 0.f);
+    } else {
+      const size_t pi = (size_t(b) * a.num_q_heads + h) * a.max_parts + part;
+      a.part_o[pi * D + d] = O;
+      if (d == 0) {
+        a.part_m[pi] = M;
+        a.part_l[pi] = L;
+      }
+    }
+  }
+}
+
+// MFMA decode: one workgroup of 4 waves per (sequence, KV head, partition, group
+// of up to 16 query heads); the waves take the partition's 32-token chunks in turn and merge
+// through LDS at the end.
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
+  using M = Mfma<DT, D, BS>;
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) float smem[NW * 16 * (D + 2)];
+
+  const int nhg = (a.group + 15) / 16;
+  const int kvh = blockIdx.x / nhg;
+  const int hg = blockIdx.x % nhg;
+  const int part = blockIdx.y;
+  const int b = blockIdx.z;
+  const int h0 = kvh * a.group + hg * 16;             // first query head of this workgroup
+  const int nh = min(16, a.group - hg * 16);          // query heads in this workgroup
+  const int ctx = clamp_ctx(a, b);
+  const int tid = threadIdx.x;
+  const size_t q_row0 = size_t(b) * a.num_q_heads + h0;
+  if (ctx == 0) {
+    if (part == 0)
+      for (int i = tid; i < nh * D; i += NW * 64) store_elt<DT>(a.out, q_row0 * D + i, 0.f);
+    return;
+  }
+  const int t0 = part * a.part_size;
+  if (t0 >= ctx) return;
+  const int t1 = min(ctx, t0 + a.part_size);
+  const int nparts = (ctx + a.part_size - 1) / a.part_size;
+
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
+  const size_t head_off = size_t(kvh) * BS * D * 2;
+  const char* kb = static_cast<const char*>(a.k_cache) + head_off;
+  const char* vb = static_cast<const char*>(a.v_cache) + head_off;
+  const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
+
+  typename M::vec8 qop[M::KK];
+  M::load_q(a, q_row0, nh, lane, qop);
+  const int ncached = cached_blocks(a, b);
+  typename M::State st;
+  M::init(st);
+  const int nchunks = (t1 - t0 + kMfmaChunk - 1) / kMfmaChunk;
+  for (int c = wave; c < nchunks; c += NW) {
+    const int cs = t0 + c * kMfmaChunk;
+    M::chunk(a, tbl, kb, vb, blk_bytes, cs, t1, cs / BS < ncached, lane, qop, st);
+  }
+  st.l = xor_sum_16_32(st.l);  // m already agrees across the four lane groups
+
+  float* mo = smem;                       // [NW][16][D]
+  float* mm = mo + NW * 16 * D;           // [NW][16]
+  float* ml = mm + NW * 16;               // [NW][16]
+#pragma unroll
+  for (int r = 0; r < M::E; ++r)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) mo[(wave * 16 + n16) * D + M::out_d(g4, v, r)] = st.acc[r][v];
+  if (g4 == 0) {
+    mm[wave * 16 + n16] = st.m;
+    ml[wave * 16 + n16] = st.l;
+  }
+  __syncthreads();
+  for (int i = tid; i < nh * D; i += NW * 64) {
+    const int hh = i / D, d = i % D;
+    float Mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, mm[w * 16 + hh]);
+    float L = 0.f, O = 0.f;
+    if (Mx != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float sc = exp2_hw(mm[w * 16 + hh] - Mx);
+        L += ml[w * 16 + hh] * sc;
+        O += mo[(w * 16 + hh) * D + d] * sc;
+      }
+    }
+    if (nparts == 1) {
+      store_elt<DT>(a.out, (q_row0 + hh) * D + d, L > 0.f ? O / L : 0.f);
+    } else {
+      const size_t pi = ((size_t(b) * a.num_q_heads + h0 + hh) * a.max_parts + part);
+      a.part_o[pi * D + d] = O;
+      if (d == 0) {
+        a.part_m[pi] = Mx;
+        a.part_l[pi] = L;
+      }
+    }
+  }
+}
+
+// =========================================================================================
+// Partition merge: out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p, for
+// (sequence, head) pairs whose context spans more than one partition.  One workgroup per
+// (head, sequence); one thread per output element.
+// =========================================================================================
+template <int DT, int D>
+__global__ __launch_bounds__(128) void reduce_partitions(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int ctx = clamp_ctx(a, b);
+  const int nparts = (ctx + a.part_size - 1) / a.part_size;
+  if (nparts <= 1) return;
+  const size_t base = (size_t(b) * a.num_q_heads + h) * a.max_parts;
+  float M = kNegInf;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.part_m[base + p]);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float L = 0.f, O = 0.f;
+    if (M != kNegInf) {
+      for (int p = 0; p < nparts; ++p) {
+        const float w = exp2_hw(a.part_m[base + p] - M);
+        L += a.part_l[base + p] * w;
+        O += a.part_o[(base + p) * D + d] * w;
+      }
+    }
+    store_elt<DT>(a.out, (size_t(b) * a.num_q_heads + h) * D + d, L > 0.f ? O / L : 0.f);
+  }
+}
+
+}  // namespace pkv
+
+// =========================================================================================
+// Host side: instance selection and launches.
+// =========================================================================================
+namespace {
+
+using namespace pkv;
+
+bool use_mfma(pkv_dtype dt, int d, int bs, int group) {
+  return dt != PKV_F32 && (d == 64 || d == 128) && bs >= 8 && group > 1;
+}
+
+// Tokens per partition for a shape (a multiple of 16 and of the block size).  0 = the whole
+// context; -1 = automatic: the fewest partitions that give the launch about kAutoWorkgroups
+// workgroups, at most one per kAutoMinPartition tokens of the longest context, their size
+// rounded up to a multiple of kAutoQuantum.  Decided from the shape and max_context_len only.
+int resolve_partition(int32_t partition_size, int32_t ctx_limit, int64_t rows) {
+  const int whole = ctx_limit < 16 ? 16 : (ctx_limit + 15) / 16 * 16;
+  if (partition_size > 0) return partition_size;
+  if (partition_size == 0) return whole;
+  const int64_t want = (kAutoWorkgroups + rows - 1) / rows;
+  const int64_t most = (int64_t(ctx_limit) + kAutoMinPartition - 1) / kAutoMinPartition;
+  const int64_t parts = want < most ? want : most;
+  if (parts <= 1) return whole;
+  const int64_t per = (int64_t(ctx_limit) + parts - 1) / parts;
+  return int((per + kAutoQuantum - 1) / kAutoQuantum * kAutoQuantum);
+}
+
+// Workgroups per (sequence, partition): one per query head (VALU) or per group of up to 16
+// query heads sharing a KV head (MFMA).
+int64_t rows_per_seq(pkv_dtype dt, int hq, int hkv, int d, int bs) {
+  const int group = hq / hkv;
+  return use_mfma(dt, d, bs, group) ? int64_t(hkv) * ((group + 15) / 16) : int64_t(hq);
+}
+
+typedef void (*kernel_fn)(DecodeArgs);
+
+template <int DT, int D>
+kernel_fn pick_valu_bs(int bs) {
+  switch (bs) {
+    case 4: return decode_valu<DT, D, 4, kValuWaves>;
+    case 8: return decode_valu<DT, D, 8, kValuWaves>;
+    case 16: return decode_valu<DT, D, 16, kValuWaves>;
+    case 32: return decode_valu<DT, D, 32, kValuWaves>;
+  }
+  return nullptr;
+}
+
+template <int DT>
+kernel_fn pick_valu(int d, int bs) {
+  switch (d) {
+    case 8: return pick_valu_bs<DT, 8>(bs);
+    case 64: return pick_valu_bs<DT, 64>(bs);
+    case 128: return pick_valu_bs<DT, 128>(bs);
+  }
+  return nullptr;
+}
+
+template <int DT, int D>
+kernel_fn pick_mfma_bs(int bs) {
+  switch (bs) {
+    case 8: return decode_mfma<DT, D, 8>;
+    case 16: return decode_mfma<DT, D, 16>;
+    case 32: return decode_mfma<DT, D, 32>;
+  }
+  return nullptr;
+}
+
+template <int DT>
+kernel_fn pick_mfma(int d, int bs) {
+  switch (d) {
+    case 64: return pick_mfma_bs<DT, 64>(bs);
+    case 128: return pick_mfma_bs<DT, 128>(bs);
+  }
+  return nullptr;
+}
+
+kernel_fn pick_decode(pkv_dtype dt, int d, int bs, bool mfma) {
+  if (mfma) return dt == PKV_F16 ? pick_mfma<DT_F16>(d, bs) : pick_mfma<DT_BF16>(d, bs);
+  return dt == PKV_F32   ? pick_valu<DT_F32>(d, bs)
+         : dt == PKV_F16 ? pick_valu<DT_F16>(d, bs)
+                         : pick_valu<DT_BF16>(d, bs);
+}
+
+template <int DT>
+kernel_fn pick_reduce(int d) {
+  switch (d) {
+    case 8: return reduce_partitions<DT, 8>;
+    case 64: return reduce_partitions<DT, 64>;
+    case 128: return reduce_partitions<DT, 128>;
+  }
+  return nullptr;
+}
+
+kernel_fn pick_reduce(pkv_dtype dt, int d) {
+  return dt == PKV_F32 ? pick_reduce<DT_F32>(d)
+         : dt == PKV_F16 ? pick_reduce<DT_F16>(d) : pick_reduce<DT_BF16>(d);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                  pkv_dtype dtype, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_context_len <= 0 || num_q_heads % num_kv_heads != 0 ||
+      !valid_dtype(dtype) || partition_size < -1)
+    return 0;
+  const int64_t rows = rows_per_seq(dtype, num_q_heads, num_kv_heads, head_dim, block_size);
+  const int p = resolve_partition(partition_size, max_context_len, int64_t(num_seqs) * rows);
+  const int64_t max_parts = (int64_t(max_context_len) + p - 1) / p;
+  if (max_parts <= 1) return 0;
+  return size_t(num_seqs) * num_q_heads * max_parts * (size_t(head_dim) + 2) * sizeof(float);
+}
+
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, const int32_t* cached_blocks,
+                                      int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, pkv_dtype dtype, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return PKV_ERR_INVALID_ARG;
+  if (!(head_dim == 8 || head_dim == 64 || head_dim == 128)) return PKV_ERR_UNSUPPORTED;
+  if (!(block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32))
+    return PKV_ERR_UNSUPPORTED;
+  if (partition_size < -1) return PKV_ERR_INVALID_ARG;
+  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+    return PKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_INVALID_ARG;
+
+  const int64_t cap = int64_t(max_blocks_per_seq) * block_size;
+  const int32_t ctx_limit = int32_t(max_context_len < cap ? max_context_len : cap);
+  const int group = num_q_heads / num_kv_heads;
+  const bool mfma = use_mfma(dtype, head_dim, block_size, group);
+  const int64_t rows = rows_per_seq(dtype, num_q_heads, num_kv_heads, head_dim, block_size);
+  // The partition follows max_context_len exactly as pkv_decode_workspace_bytes does; the
+  // clamp to the table's capacity can only lower the partition count.
+  const int part = resolve_partition(partition_size, max_context_len, int64_t(num_seqs) * rows);
+  const int64_t max_parts64 = ctx_limit > 0 ? (int64_t(ctx_limit) + part - 1) / part : 1;
+  if (max_parts64 > 65535 || num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
+  const int max_parts = int(max_parts64);
+
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.cached = cached_blocks;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.ctx_limit = ctx_limit;
+  a.part_size = part;
+  a.max_parts = max_parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if (max_parts > 1) {
+    const size_t need =
+        size_t(num_seqs) * num_q_heads * max_parts * (size_t(head_dim) + 2) * sizeof(float);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
+    float* w = static_cast<float*>(workspace);
+    a.part_o = w;
+    a.part_m = w + size_t(num_seqs) * num_q_heads * max_parts * head_dim;
+    a.part_l = a.part_m + size_t(num_seqs) * num_q_heads * max_parts;
+  }
+  kernel_fn k = pick_decode(dtype, head_dim, block_size, mfma);
+  kernel_fn r = pick_reduce(dtype, head_dim);
+  if (!k || !r) return PKV_ERR_UNSUPPORTED;
+  const dim3 grid{unsigned(rows), unsigned(max_parts), unsigned(num_seqs)};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  clear_stale_error();
+  hipLaunchKernelGGL(k, grid, dim3(mfma ? 256 : 64 * kValuWaves), 0, st, a);
+  if (launch_status("paged_attention_decode") != PKV_OK) return PKV_ERR_HIP;
+  if (max_parts > 1) {
+    hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(128), 0, st, a);
+    return launch_status("reduce_partitions");
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

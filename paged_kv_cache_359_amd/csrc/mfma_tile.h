@@ -1,0 +1,228 @@
+// The MFMA attention tile shared by decode (grouped-query heads as columns) and prefill
+// (consecutive new tokens of one head as columns).
+#pragma once
+
+#include "device.h"
+
+namespace pkv {
+
+// =========================================================================================
+// MFMA inner loop for grouped-query attention (16-bit K/V, head_dim 64 or 128).  The query
+// heads sharing a KV head (up to 16 per row) are the columns of two small products per
+// 32-token chunk:
+//   S[16 tokens x 16 heads]  = K_half[16 x D] . Q^T[D x 16]       (v_mfma 16x16x32), twice
+//   O^T[D x 16 heads]       += V^T[D x 32 tokens] . P^T[32 x 16]   (v_mfma 16x16x32), E times
+// The S accumulator of lane l holds scores of head l%16 for tokens 4*(l/16)+i of each half;
+// taking those eight tokens, in that order, as the lane's eight contraction indices of the
+// second product puts P^T in its operand layout without moving data.  The V^T operand needs,
+// per lane, the same eight tokens for one output column: each lane loads the 16-byte (E
+// elements) slice [E*c, E*c + E) of those eight token rows, which is already a fully used
+// coalesced load (16 lanes cover a row), and picks element r of each row to form the operand
+// of output tile r, whose column c stands for d = E*c + r.  So V is transposed in registers
+// with one byte-permute per operand word and never goes through LDS.  Lane l ends up holding
+// the outputs of head l%16 for d in [4E*(l/16), 4E*(l/16) + 4E), contiguous.
+// For bf16 the probabilities are split into a bf16 high part and a bf16 remainder (two
+// products), so P keeps ~16 significant bits; fp16 P keeps 11.
+// =========================================================================================
+template <int DT, int D, int BS>
+struct Mfma {
+  static_assert(DT == DT_F16 || DT == DT_BF16, "16-bit only");
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static_assert(BS >= 8, "block_size >= 8");
+  static constexpr int KK = D / 32;   // k-steps of the S product
+  static constexpr int E = D / 16;    // elements per lane per V row = output tiles
+  static constexpr int NBH = BS < 16 ? 16 / BS : 1;  // blocks per 16-token half
+  static constexpr bool SPLIT_P = DT == DT_BF16;
+  using vec8 = typename std::conditional<DT == DT_F16, half8_t, bf168_t>::type;
+  using elt = typename std::conditional<DT == DT_F16, _Float16, __bf16>::type;
+
+  struct State {
+    float4_t acc[E];
+    float m, l;
+  };
+
+  __device__ static void init(State& st) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) st.acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
+    st.m = kNegInf;
+    st.l = 0.f;
+  }
+
+  // Q^T operand: lane holds q[h0 + lane%16][32kk + 8*(lane/16) .. + 8] for each k-step.
+  __device__ static void load_q(const DecodeArgs& a, size_t q_row0, int nh, int lane, vec8 (&qop)[KK]) {
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const bool hv = n16 < nh;
+    const char* qp = static_cast<const char*>(a.q) + ((q_row0 + (hv ? n16 : 0)) * D) * 2;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 w = hv ? *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2) : make_uint4(0, 0, 0, 0);
+      qop[kk] = __builtin_bit_cast(vec8, w);
+    }
+  }
+
+  __device__ static float4_t mma(const vec8& x, const vec8& y, const float4_t& c) {
+    if constexpr (DT == DT_F16) return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, y, c, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+  }
+
+  // The K/V of one 32-token chunk as this lane holds it: K rows cs + 16hf + lane%16 (8
+  // elements per k-step) and V rows cs + 16hf + 4*(lane/16) + i, elements
+  // [E*(lane%16), E*(lane%16) + E).  compute() zeroes the V rows of tokens that do not exist.
+  struct Chunk {
+    uint4 kr[2][KK];
+    uint32_t vr[2][4][E / 2];
+    bool vok[2][4];
+    bool need_mask;  // wave-uniform: some row of this chunk does not exist
+  };
+
+  // kb / vb: pool base plus this KV head's offset.  cs: a multiple of 16.  cached: read this
+  // chunk through the caches (wave-uniform).
+  __device__ static void load(const DecodeArgs& a, const int32_t* tbl, const char* kb,
+                              const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
+                              int lane, Chunk& ck) {
+    const int n16 = lane & 15, g4 = lane >> 4;
+    bool need_mask = cs + kMfmaChunk > t1;  // wave-uniform
+    int ids[2][NBH];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int k = 0; k < NBH; ++k) {
+        const int first = cs + 16 * hf + k * (BS < 16 ? BS : 16);
+        ids[hf][k] = uniform(first < t1 ? tbl[first / BS] : -1);
+        need_mask |= (unsigned)ids[hf][k] >= (unsigned)a.num_blocks;
+      }
+    const char* kp[2];
+    const char* vp[2][4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int tok = cs + 16 * hf + n16;
+      const int id = ids[hf][NBH > 1 ? n16 / BS : 0];
+      const bool valid = (unsigned)id < (unsigned)a.num_blocks;
+      kp[hf] = kb + size_t(valid ? id : 0) * blk_bytes + size_t(tok % BS) * D * 2 + 8 * g4 * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tv = cs + 16 * hf + 4 * g4 + i;
+        const int idv = ids[hf][NBH > 1 ? (4 * g4 + i) / BS : 0];
+        const bool vv = (unsigned)idv < (unsigned)a.num_blocks;
+        ck.vok[hf][i] = vv && tv < t1;
+        vp[hf][i] = vb + size_t(vv ? idv : 0) * blk_bytes + size_t(tv % BS) * D * 2 + E * n16 * 2;
+      }
+    }
+    if (cached) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) ck.kr[hf][kk] = load_cached(kp[hf] + 32 * kk * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (E == 8) {
+            const uint4 w = load_cached(vp[hf][i]);
+            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y, ck.vr[hf][i][2] = w.z, ck.vr[hf][i][3] = w.w;
+          } else {
+            const uint2 w = load_cached8(vp[hf][i]);
+            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) ck.kr[hf][kk] = load_stream(kp[hf] + 32 * kk * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (E == 8) {
+            const uint4 w = load_stream(vp[hf][i]);
+            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y, ck.vr[hf][i][2] = w.z, ck.vr[hf][i][3] = w.w;
+          } else {
+            const uint2 w = load_stream8(vp[hf][i]);
+            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y;
+          }
+        }
+      }
+    }
+    ck.need_mask = need_mask;
+  }
+
+  // Online-softmax update of one 16-column tile with a loaded chunk starting at token cs.
+  // CAUSAL: the lane's column may only see keys at positions <= lim; lim_min is the smallest
+  // lim of the tile (wave-uniform).
+  template <bool CAUSAL = false>
+  __device__ static void compute(const DecodeArgs& a, Chunk& ck, int cs, int lane,
+                                 const vec8 (&qop)[KK], State& st, int lim = 0, int lim_min = 0) {
+    const int g4 = lane >> 4;
+    bool need_mask = ck.need_mask;
+    if constexpr (CAUSAL) need_mask |= cs + kMfmaChunk - 1 > lim_min;
+    // S = K . Q^T for both halves.
+    float4_t s[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      s[hf] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) s[hf] = mma(__builtin_bit_cast(vec8, ck.kr[hf][kk]), qop[kk], s[hf]);
+    }
+    float sv[2][4];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[hf][i] = s[hf][i] * a.scale_log2;
+        if (need_mask) {
+          if (!ck.vok[hf][i]) {
+            sv[hf][i] = kNegInf;
+#pragma unroll
+            for (int q = 0; q < E / 2; ++q) ck.vr[hf][i][q] = 0u;  // unused slots may hold anything
+          }
+          if constexpr (CAUSAL) {
+            if (cs + 16 * hf + 4 * g4 + i > lim) sv[hf][i] = kNegInf;  // a later token
+          }
+        }
+      }
+    float cm = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    cm = xor_max_16_32(cm);
+    const float mn = fmaxf(st.m, cm);
+    const float mu = mn == kNegInf ? 0.f : mn;
+    const float alpha = exp2_hw(st.m - mu);
+    st.m = mn;
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = exp2_hw(sv[j >> 2][j & 3] - mu);
+    st.l = st.l * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+#pragma unroll
+    for (int r = 0; r < E; ++r) st.acc[r] *= alpha;
+    vec8 phi, plo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      phi[j] = elt(p[j]);
+      if constexpr (SPLIT_P) plo[j] = elt(p[j] - float(phi[j]));
+    }
+    // O^T += V^T . P^T, one output tile per element position r of the lane's V slices.
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = ck.vr[(2 * q) >> 2][(2 * q) & 3][r >> 1];
+        const uint32_t hi = ck.vr[(2 * q + 1) >> 2][(2 * q + 1) & 3][r >> 1];
+        w[q] = (r & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      const vec8 vop = __builtin_bit_cast(vec8, make_uint4(w[0], w[1], w[2], w[3]));
+      st.acc[r] = mma(vop, phi, st.acc[r]);
+      if constexpr (SPLIT_P) st.acc[r] = mma(vop, plo, st.acc[r]);
+    }
+  }
+
+  __device__ static void chunk(const DecodeArgs& a, const int32_t* tbl, const char* kb,
+                               const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
+                               int lane, const vec8 (&qop)[KK], State& st) {
+    Chunk ck;
+    load(a, tbl, kb, vb, blk_bytes, cs, t1, cached, lane, ck);
+    compute(a, ck, cs, lane, qop, st);
+  }
+
+  // Output d of element (r, v) of the lane's accumulators: E * (4 * (lane / 16) + v) + r.
+  __device__ static int out_d(int g4, int v, int r) { return E * (4 * g4 + v) + r; }
+};
+
+}  // namespace pkv
