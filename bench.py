@@ -22,6 +22,7 @@ bounded sample of the same batch.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -31,6 +32,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+HOST_LINK_GBS = 64.0  # MI355X host interface, PCIe 5.0 x16: 32 GT/s x 16 lanes per direction
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "paged_kv_cache_359_amd", "csrc")
@@ -44,6 +46,23 @@ def decode_source_sha():
     for f in DECODE_SOURCES:
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
+
+
+def run_timed(fn, first, last, sync):
+    """Runs fn(first) .. fn(last - 1) between two device synchronisations and returns the wall
+    time in seconds.  Python's cyclic garbage collector is run before and kept off inside, so
+    that none of its passes (tens of ms with torch loaded) lands in the timed steps."""
+    gc.collect()
+    gc.disable()
+    try:
+        sync()
+        t0 = time.perf_counter()
+        for i in range(first, last):
+            fn(i)
+        sync()
+        return time.perf_counter() - t0
+    finally:
+        gc.enable()
 
 
 def counted_traffic(config_name):
@@ -85,6 +104,9 @@ def parse():
                     help="verify every timed step's output against a serial re-decode")
     ap.add_argument("--swap", action="store_true",
                     help="measure swap preemption (swap out and back in) instead of decode")
+    ap.add_argument("--swap-mode", choices=["staged", "direct"], default="staged",
+                    help="--swap: staged = gather into HBM then one DMA copy each way; direct = "
+                         "the block-move kernels write and read the pinned host copy themselves")
     ap.add_argument("--swap-every", type=int, default=8,
                     help="--swap: every n-th sequence of the batch is a victim")
     ap.add_argument("--summarize", metavar="DIR",
@@ -248,13 +270,9 @@ def main_prefill(args, cfg):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.warmup, total_steps):
-        step(s)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    elapsed = run_timed(step, args.warmup, total_steps, torch.cuda.synchronize)
     K = args.steps
-    ms_per_step = (t1 - t0) * 1e3 / K
+    ms_per_step = elapsed * 1e3 / K
     kern_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][1]) for s in range(args.warmup, total_steps)]))
     flops = prefill_flops(c, w.lengths, w.n_new)
     achieved = flops / (kern_ms * 1e-3) / 1e12
@@ -385,14 +403,14 @@ def overlapped_steps(args, alloc, ids, B, max_blocks, NBUF, k_cache, v_cache, k_
 
 
 def main_swap(args):
-    """One step = one swap cycle of the victims (every --swap-every-th sequence of the batch):
-    swap-out (the allocator releases each victim's blocks; pkv_gather_blocks copies them into
-    a device staging buffer; one DMA copy takes that to pinned host memory), then swap-in (the
-    allocator hands out fresh blocks; one DMA copy back; pkv_scatter_blocks writes them into
-    the pools).  ``value`` counts the K/V bytes moved in both directions per second of the
-    whole cycle (host link included); ``roofline`` rates the gather kernel (each byte read
-    from and written to HBM once).  A decode of the whole batch before the first and after the
-    last cycle must be bit-identical."""
+    """One step = one swap cycle of the victims (every --swap-every-th sequence of the batch).
+    Swap-out: the allocator releases each victim's blocks and pkv_gather_blocks copies them
+    out.  Swap-in: the allocator hands out fresh blocks and pkv_scatter_blocks writes them
+    back.  --swap-mode staged moves the blocks through an HBM staging buffer and one DMA copy
+    each way; --swap-mode direct lets the two kernels write and read the pinned host copy
+    themselves.  ``value`` counts the K/V bytes moved in both directions per second of the
+    whole cycle (host link included); ``roofline`` rates the gather kernel.  A decode of the
+    whole batch before the first and after the last cycle must be bit-identical."""
     import torch
     import workloads as W
     import paged_kv_cache_359_amd as pkv
@@ -434,6 +452,9 @@ def main_swap(args):
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
     host_s = [0.0]
 
+    direct = args.swap_mode == "direct"
+    k_out, v_out = (k_host, v_host) if direct else (k_stage, v_stage)
+
     def cycle(i):
         e = ev[i]
         h0 = time.perf_counter()
@@ -445,10 +466,11 @@ def main_swap(args):
         host_s[0] += time.perf_counter() - h0
         ids_d[0].copy_(ids_h[0], non_blocking=True)
         e[0].record(stream)
-        pkv.pkv_gather_blocks(k_cache, v_cache, ids_d[0], k_stage, v_stage)
+        pkv.pkv_gather_blocks(k_cache, v_cache, ids_d[0], k_out, v_out)
         e[1].record(stream)
-        k_host.copy_(k_stage, non_blocking=True)
-        v_host.copy_(v_stage, non_blocking=True)
+        if not direct:
+            k_host.copy_(k_stage, non_blocking=True)
+            v_host.copy_(v_stage, non_blocking=True)
         e[2].record(stream)
         h0 = time.perf_counter()
         in_ids, n = ids_h[1].numpy(), 0
@@ -458,10 +480,11 @@ def main_swap(args):
             n += blk.size
         host_s[0] += time.perf_counter() - h0
         ids_d[1].copy_(ids_h[1], non_blocking=True)
-        k_stage.copy_(k_host, non_blocking=True)
-        v_stage.copy_(v_host, non_blocking=True)
+        if not direct:
+            k_stage.copy_(k_host, non_blocking=True)
+            v_stage.copy_(v_host, non_blocking=True)
         e[3].record(stream)
-        pkv.pkv_scatter_blocks(k_stage, v_stage, ids_d[1], k_cache, v_cache)
+        pkv.pkv_scatter_blocks(k_out, v_out, ids_d[1], k_cache, v_cache)
         e[4].record(stream)
         stream.synchronize()  # the pinned id buffers are rewritten next cycle
 
@@ -469,17 +492,13 @@ def main_swap(args):
         cycle(i)
     torch.cuda.synchronize()
     host_s[0] = 0.0
-    t0 = time.perf_counter()
-    for i in range(args.warmup, total):
-        cycle(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    elapsed = run_timed(cycle, args.warmup, total, torch.cuda.synchronize)
     after = decode()
     if not torch.equal(before, after):
         raise SystemExit("[bench] swap check failed: decode differs after the swap cycles")
 
     K = args.steps
-    ms = (t1 - t0) * 1e3 / K
+    ms = elapsed * 1e3 / K
     timed = range(args.warmup, total)
     span = lambda a, b: float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in timed]))
     g_ms, d2h_ms, h2d_ms, s_ms = span(0, 1), span(1, 2), span(2, 3), span(3, 4)
@@ -489,7 +508,8 @@ def main_swap(args):
         "value": gbs(2 * moved, ms), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
-        "config": {"workload": f"swap, {c.name}: {len(victims)} of {B} sequences "
+        "swap_mode": args.swap_mode,
+        "config": {"workload": f"swap ({args.swap_mode}), {c.name}: {len(victims)} of {B} sequences "
                                f"({nblk} blocks, {moved / 1e6:.1f} MB of K/V) out to pinned host "
                                f"memory and back, Hkv={c.num_kv_heads}, D={c.head_dim}, block={bs}, "
                                f"{c.dtype} KV",
@@ -498,12 +518,20 @@ def main_swap(args):
         "d2h_ms": round(d2h_ms, 5), "h2d_ms": round(h2d_ms, 5),
         "d2h_GBs": gbs(moved, d2h_ms), "h2d_GBs": gbs(moved, h2d_ms),
         "scatter_GBs": gbs(2 * moved, s_ms),
+        "host_link": {"peak": HOST_LINK_GBS, "unit": "GB/s",
+                      "out_GBs": gbs(moved, g_ms if direct else d2h_ms),
+                      "in_GBs": gbs(moved, s_ms if direct else h2d_ms)},
         "host_ms_per_step": round(host_s[0] * 1e3 / K, 4),
         "checked": True,
-        "roofline": {"bound": "hbm", "achieved": gbs(2 * moved, g_ms), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(2 * moved / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
-                     "traffic": None, "kernel": "gather_blocks (swap-out staging)",
-                     "bytes_per_launch": 2 * moved},
+        "roofline": ({"bound": "hbm", "achieved": gbs(2 * moved, g_ms), "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": round(2 * moved / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                      "traffic": None, "kernel": "gather_blocks (swap-out staging)",
+                      "bytes_per_launch": 2 * moved} if not direct else
+                     {"bound": "host link", "achieved": gbs(moved, g_ms), "peak": HOST_LINK_GBS,
+                      "unit": "GB/s", "frac": round(moved / (g_ms * 1e-3) / 1e9 / HOST_LINK_GBS, 5),
+                      "traffic": None,
+                      "kernel": "gather_blocks (swap-out straight to pinned host memory)",
+                      "bytes_per_launch": moved}),
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
@@ -724,11 +752,7 @@ def main():
         step(s)
     torch.cuda.synchronize()
     host_s[0] = 0.0
-    t0 = time.perf_counter()
-    for s in range(args.warmup, total_steps):
-        step(s)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    elapsed = run_timed(step, args.warmup, total_steps, torch.cuda.synchronize)
     print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
     if saved is not None:
         # During the timed steps tables only grow, so the final tables with each step's
@@ -745,7 +769,7 @@ def main():
               file=sys.stderr, flush=True)
 
     K = args.steps
-    ms_per_step = (t1 - t0) * 1e3 / K
+    ms_per_step = elapsed * 1e3 / K
     timed = range(args.warmup, total_steps)
     kern_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in timed]
     kern_avg_ms = float(np.mean(kern_ms))

@@ -199,8 +199,12 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, i
  * block_size * head_dim elements) to k_out + i * blk and v_out + i * blk;
  * pkv_scatter_blocks copies k_in + i * blk and v_in + i * blk back into block blocks[i].
  * blocks: device, n_blocks int32 (ids outside [0, num_blocks) are skipped; scatter
- * destinations must be distinct).  The buffers are device memory (16-byte aligned); to
- * reach the host, copy them with one asynchronous device-to-host copy on the same stream. */
+ * destinations must be distinct).  The buffers (16-byte aligned, owned by the caller) are
+ * either device memory, then moved to and from the host by asynchronous copies on the same
+ * stream, or pinned host memory mapped into the device's address space (hipHostMalloc),
+ * passed by its device-side address (hipHostGetDevicePointer): the kernel then reads and
+ * writes the host copy directly over the host link, with no staging buffer and no separate
+ * copy.  Either way the call is asynchronous on `stream`. */
 pkv_status pkv_gather_blocks(const void* k_cache, const void* v_cache, const int32_t* blocks,
                              int32_t n_blocks, void* k_out, void* v_out, int32_t num_kv_heads,
                              int32_t head_dim, int32_t block_size, int32_t num_blocks,

@@ -229,6 +229,32 @@ def pkv_copy_blocks(k_cache, v_cache, pairs):
                                        _dtype_code(k_cache), _stream(k_cache)), "pkv_copy_blocks")
 
 
+_HIP = None
+
+
+def _mapped(t):
+    """Device address of a staging buffer: a GPU tensor's own pointer, or for a pinned host
+    tensor the address the HIP runtime maps it at on the device (an error if it is not
+    mapped)."""
+    global _HIP
+    if t.is_cuda:
+        return _dev(t)
+    if not t.is_pinned():
+        raise ValueError("staging buffers must be GPU tensors or pinned host tensors")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if _HIP is None:
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                                 ctypes.c_uint]
+        _HIP.hipHostGetDevicePointer.restype = ctypes.c_int
+    ptr = ctypes.c_void_p()
+    err = _HIP.hipHostGetDevicePointer(ctypes.byref(ptr), ctypes.c_void_p(t.data_ptr()), 0)
+    if err != 0 or not ptr.value:
+        raise ValueError(f"pinned buffer is not mapped for the device (hip error {err})")
+    return ptr.value
+
+
 def _move_blocks(fn, name, cache_k, cache_v, blocks, buf_k, buf_v):
     import torch
     n, hkv, bs, d = cache_k.shape
@@ -241,19 +267,21 @@ def _move_blocks(fn, name, cache_k, cache_v, blocks, buf_k, buf_v):
         raise TypeError("dtype mismatch")
     if nb == 0:
         return
-    _check(fn(_dev(cache_k), _dev(cache_v), _dev(blocks), nb, _dev(buf_k), _dev(buf_v), hkv, d, bs,
-              n, _dtype_code(cache_k), _stream(cache_k)), name)
+    _check(fn(_dev(cache_k), _dev(cache_v), _dev(blocks), nb, _mapped(buf_k), _mapped(buf_v), hkv,
+              d, bs, n, _dtype_code(cache_k), _stream(cache_k)), name)
 
 
 def pkv_gather_blocks(k_cache, v_cache, blocks, k_out, v_out):
-    """k_out/v_out [n, Hkv, bs, D] (device) receive the blocks ``blocks`` (device int32)."""
+    """k_out/v_out [n, Hkv, bs, D] (GPU or pinned host tensors) receive the blocks ``blocks``
+    (device int32)."""
     lib = _lib.load()
     _move_blocks(lambda kc, vc, bl, n, kb, vb, *r: lib.pkv_gather_blocks(kc, vc, bl, n, kb, vb, *r),
                  "pkv_gather_blocks", k_cache, v_cache, blocks, k_out, v_out)
 
 
 def pkv_scatter_blocks(k_in, v_in, blocks, k_cache, v_cache):
-    """Blocks ``blocks`` (device int32) of the caches receive k_in/v_in [n, Hkv, bs, D]."""
+    """Blocks ``blocks`` (device int32) of the caches receive k_in/v_in [n, Hkv, bs, D] (GPU or
+    pinned host tensors)."""
     lib = _lib.load()
     _move_blocks(lambda kc, vc, bl, n, kb, vb, *r: lib.pkv_scatter_blocks(kb, vb, bl, n, kc, vc, *r),
                  "pkv_scatter_blocks", k_cache, v_cache, blocks, k_in, v_in)
