@@ -99,6 +99,24 @@ void pkv_alloc_destroy(pkv_alloc* a);
  * DUPLICATE_SEQ if seq_id exists; OUT_OF_BLOCKS if the pool is short. */
 pkv_status pkv_seq_add(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t* slots_out);
 
+/* Prefix caching: requests that begin with the same system prompt share the physical blocks
+ * of that prompt ("PagedAttention 与 vLLM 推理加速", §3.2 (3), the three requests that keep
+ * one copy of a six-block prompt), here also when they arrive independently.  Adds seq_id
+ * with the prompt tokens[0..num_tokens) (host, token ids).  A full block of a prompt is
+ * identified by the whole token prefix that ends with it; the sequence shares the cached
+ * blocks of its longest run of leading full blocks found in the cache (each gains one
+ * reference), takes fresh blocks for the rest in logical order, and registers its fresh full
+ * blocks.  slots_out (host, num_tokens): -1 for tokens in shared blocks (their K/V is
+ * already in the pools; pkv_reshape_and_cache skips them), otherwise the slot as
+ * pkv_seq_add gives it.  *n_cached_out = number of shared tokens (a multiple of
+ * block_size).  A cached block stays cached after its last holder ends ("evictable"): it is
+ * reused only when no plain free block is left, in the order such blocks were released, a
+ * sequence's blocks tail first; evictable blocks count as free in pkv_num_free_blocks.
+ * Only prompts given here are cached (tokens added by append/extend carry no ids).
+ * DUPLICATE_SEQ / OUT_OF_BLOCKS (nothing changes) / INVALID_ARG as for pkv_seq_add. */
+pkv_status pkv_seq_add_tokens(pkv_alloc* a, int64_t seq_id, const int32_t* tokens,
+                              int32_t num_tokens, int64_t* slots_out, int32_t* n_cached_out);
+
 /* Create child_id sharing every block of parent_id (each block gains one reference).
  * UNKNOWN_SEQ if the parent is missing; DUPLICATE_SEQ if the child exists. */
 pkv_status pkv_seq_fork(pkv_alloc* a, int64_t parent_id, int64_t child_id);
@@ -160,8 +178,13 @@ pkv_status pkv_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq_ids, 
 /* Length (tokens) of one sequence. */
 pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out);
 
-/* Number of free blocks (-1 for a null handle). */
+/* Number of blocks a call can take: free ones plus evictable cached ones (-1 for a null
+ * handle). */
 int32_t pkv_num_free_blocks(const pkv_alloc* a);
+
+/* Number of blocks registered in the prefix cache and not yet evicted, held or evictable
+ * (-1 for a null handle). */
+int32_t pkv_num_cached_blocks(const pkv_alloc* a);
 
 /* Reference count of a physical block (-1 if out of range or a null handle). */
 int32_t pkv_block_refcount(const pkv_alloc* a, int32_t block);

@@ -32,6 +32,19 @@ Readings where the pages leave a choice open (each also listed in the design not
     sequence's blocks in logical order, then releases them exactly like ``free_seq``;
     ``swap_in`` later takes fresh blocks for all of them, popped in logical order, so the
     restored sequence owns every block (sharing is not re-established).
+  * Prefix caching ("PagedAttention 与 vLLM 推理加速", §3.2 (3): requests that share a system
+    prompt share its physical blocks; "vLLM 推理加速：PagedAttention、FlashAttention 与动态批处理"
+    lists prefix matching, i.e. KV reuse, among a router's signals).  The pages give the
+    effect, not the mechanism; the reading here: ``add_tokens`` names a new sequence's
+    prompt by its token ids, and each full block of the prompt is identified by the whole
+    token prefix that ends with it (the K/V of a position depends on every earlier token).
+    The new sequence shares the longest run of leading full blocks whose prefixes are
+    cached; its other blocks are fresh, and its fresh full blocks enter the cache.  Cached
+    blocks that no sequence holds any more stay cached and "evictable" until their block is
+    needed: plain free blocks are used first, then evictable ones, least recently released
+    first, a sequence's blocks released tail first.  Evicting a block also makes every cached
+    block that extends its prefix unreachable (their content can no longer be found; they
+    are evicted in turn when their place in the order comes).
   * Every call either succeeds completely or changes nothing.
 """
 from __future__ import annotations
@@ -74,21 +87,59 @@ class OracleAllocator:
         self.tables = {}
         self.lens = {}
         self.swapped = {}  # seq -> (length, number of blocks) while its cache is on the host
+        # Prefix cache: token prefix (a tuple ending at a block boundary) -> block, for the
+        # reachable entries; every registered block's prefix (reachable or not); and the
+        # registered blocks no sequence holds, next to be evicted first.
+        self.cache = {}
+        self.cached_key = {}
+        self.evictable = []
 
     # -- helpers -----------------------------------------------------------------------
     def _pop(self) -> int:
-        if not self.free:
+        if self.free:
+            b = self.free.pop()
+        elif self.evictable:
+            b = self.evictable.pop(0)
+            self._evict(b)
+        else:
             raise OutOfBlocks("no free block")
-        b = self.free.pop()
         self.ref[b] = 1
         return b
 
+    def _evict(self, b):
+        """Drop block b's content from the prefix cache.  If b is where its prefix is found,
+        every cached prefix that extends it goes too (those blocks stay registered and
+        evictable, but cannot be found).  If b was already unreachable, a newer block may
+        hold the same prefix by now, and nothing else changes."""
+        key = self.cached_key.pop(b)
+        if self.cache.get(key) != b:
+            return
+        for k in [k for k in self.cache if len(k) >= len(key) and k[:len(key)] == key]:
+            del self.cache[k]
+
+    def _release(self, blocks):
+        """Drop one reference to each block (a table in logical order).  Blocks reaching 0
+        that hold no cached prefix go onto the free stack in logical order; cached ones join
+        the evictable order tail first."""
+        gone = []
+        for b in blocks:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                gone.append(b)
+        for b in gone:
+            if b not in self.cached_key:
+                self.free.append(b)
+        for b in reversed(gone):
+            if b in self.cached_key:
+                self.evictable.append(b)
+
     def _snapshot(self):
         return (list(self.free), list(self.ref), copy.deepcopy(self.tables), dict(self.lens),
-                dict(self.swapped))
+                dict(self.swapped), dict(self.cache), dict(self.cached_key), list(self.evictable))
 
     def _restore(self, snap):
-        self.free, self.ref, self.tables, self.lens, self.swapped = snap
+        (self.free, self.ref, self.tables, self.lens, self.swapped, self.cache,
+         self.cached_key, self.evictable) = snap
 
     def _slot(self, seq) -> int:
         n = self.lens[seq]
@@ -102,8 +153,8 @@ class OracleAllocator:
         if seq in self.tables or seq in self.swapped:
             raise DuplicateSeq(seq)
         need = -(-num_tokens // self.block_size)
-        if need > len(self.free):
-            raise OutOfBlocks(f"need {need} blocks, {len(self.free)} free")
+        if need > self.num_free():
+            raise OutOfBlocks(f"need {need} blocks, {self.num_free()} free")
         self.tables[seq] = [self._pop() for _ in range(need)]
         self.lens[seq] = 0
         slots = []
@@ -111,6 +162,44 @@ class OracleAllocator:
             slots.append(self._slot(seq))
             self.lens[seq] += 1
         return slots
+
+    def add_tokens(self, seq, tokens):
+        """New sequence whose prompt is the token ids ``tokens``, sharing the cached blocks of
+        its longest cached run of leading full-block prefixes.  Returns (slots, n_cached):
+        tokens in shared blocks get slot -1 (their K/V is already in the pools) and
+        ``n_cached`` counts them; the others get slots in fresh blocks as ``add`` gives."""
+        tokens = [int(t) for t in tokens]
+        if seq in self.tables or seq in self.swapped:
+            raise DuplicateSeq(seq)
+        bs = self.block_size
+        n = len(tokens)
+        hits = []
+        for j in range(n // bs):
+            b = self.cache.get(tuple(tokens[: (j + 1) * bs]))
+            if b is None:
+                break
+            hits.append(b)
+        need = -(-n // bs) - len(hits)
+        avail = self.num_free() - sum(1 for b in hits if self.ref[b] == 0)
+        if need > avail:
+            raise OutOfBlocks(f"need {need} blocks, {avail} free")
+        for b in hits:
+            if self.ref[b] == 0:
+                self.evictable.remove(b)
+            self.ref[b] += 1
+        table = list(hits)
+        for j in range(len(hits), -(-n // bs)):
+            b = self._pop()
+            table.append(b)
+            if (j + 1) * bs <= n:
+                key = tuple(tokens[: (j + 1) * bs])
+                self.cache[key] = b
+                self.cached_key[b] = key
+        self.tables[seq] = table
+        self.lens[seq] = n
+        shared = len(hits) * bs
+        slots = [-1 if i < shared else table[i // bs] * bs + i % bs for i in range(n)]
+        return slots, shared
 
     def fork(self, parent, child):
         """``child`` shares every block of ``parent`` (one more reference each)."""
@@ -174,10 +263,7 @@ class OracleAllocator:
         """End a sequence: drop one reference per block; blocks reaching 0 go back."""
         if seq not in self.tables:
             raise UnknownSeq(seq)
-        for b in self.tables[seq]:
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
+        self._release(self.tables[seq])
         del self.tables[seq]
         del self.lens[seq]
 
@@ -199,8 +285,8 @@ class OracleAllocator:
         if seq not in self.swapped:
             raise UnknownSeq(seq)
         length, nblocks = self.swapped[seq]
-        if nblocks > len(self.free):
-            raise OutOfBlocks(f"need {nblocks} blocks, {len(self.free)} free")
+        if nblocks > self.num_free():
+            raise OutOfBlocks(f"need {nblocks} blocks, {self.num_free()} free")
         self.tables[seq] = [self._pop() for _ in range(nblocks)]
         self.lens[seq] = length
         del self.swapped[seq]
@@ -221,7 +307,12 @@ class OracleAllocator:
         return rows, lens
 
     def num_free(self) -> int:
-        return len(self.free)
+        """Blocks that can be handed out: free ones and evictable cached ones."""
+        return len(self.free) + len(self.evictable)
+
+    def num_cached(self) -> int:
+        """Blocks registered in the prefix cache and not evicted (held or evictable)."""
+        return len(self.cached_key)
 
     def refcount(self, block: int) -> int:
         if not 0 <= block < self.num_blocks:

@@ -18,6 +18,7 @@ SIGNATURES = {
     "pkv_alloc_create": (c_i32, [c_i32, c_i32, P_i32, ctypes.POINTER(c_vp)]),
     "pkv_alloc_destroy": (None, [c_vp]),
     "pkv_seq_add": (c_i32, [c_vp, c_i64, c_i32, P_i64]),
+    "pkv_seq_add_tokens": (c_i32, [c_vp, c_i64, P_i32, c_i32, P_i64, P_i32]),
     "pkv_seq_fork": (c_i32, [c_vp, c_i64, c_i64]),
     "pkv_seq_append": (c_i32, [c_vp, P_i64, c_i32, P_i64, P_i32, P_i32]),
     "pkv_seq_extend": (c_i32, [c_vp, c_i64, c_i32, P_i64, P_i32, P_i32]),
@@ -28,6 +29,7 @@ SIGNATURES = {
     "pkv_seq_length": (c_i32, [c_vp, c_i64, P_i32]),
     "pkv_shared_prefix_blocks": (c_i32, [c_vp, P_i64, c_i32, P_i32]),
     "pkv_num_free_blocks": (c_i32, [c_vp]),
+    "pkv_num_cached_blocks": (c_i32, [c_vp]),
     "pkv_block_refcount": (c_i32, [c_vp, c_i32]),
     "pkv_usage": (c_i32, [c_vp, P_i64, P_i64]),
     "pkv_reshape_and_cache": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,

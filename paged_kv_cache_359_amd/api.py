@@ -84,6 +84,17 @@ class PkvAlloc:
                "pkv_seq_add")
         return slots
 
+    def pkv_seq_add_tokens(self, seq_id: int, tokens):
+        """Prefix-cached add: returns (slots int64, n_cached); slots of shared tokens are -1."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        n = toks.size
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        nc = ctypes.c_int32(0)
+        _check(self._lib.pkv_seq_add_tokens(self._h, int(seq_id), _ptr(toks, ctypes.c_int32) if n else None,
+                                            n, _ptr(slots, ctypes.c_int64), ctypes.byref(nc)),
+               "pkv_seq_add_tokens")
+        return slots[:n], int(nc.value)
+
     def pkv_seq_fork(self, parent_id: int, child_id: int):
         _check(self._lib.pkv_seq_fork(self._h, int(parent_id), int(child_id)), "pkv_seq_fork")
 
@@ -160,6 +171,9 @@ class PkvAlloc:
 
     def pkv_num_free_blocks(self) -> int:
         return int(self._lib.pkv_num_free_blocks(self._h))
+
+    def pkv_num_cached_blocks(self) -> int:
+        return int(self._lib.pkv_num_cached_blocks(self._h))
 
     def pkv_block_refcount(self, block: int) -> int:
         return int(self._lib.pkv_block_refcount(self._h, int(block)))
@@ -244,7 +258,9 @@ def _mapped(t):
     if not t.is_contiguous():
         raise ValueError("expected a contiguous tensor")
     if _HIP is None:
-        _HIP = ctypes.CDLL("libamdhip64.so")
+        # Looked up through the library's own handle, so the symbol comes from the HIP runtime
+        # the library (and torch) is linked against, never from a second copy.
+        _HIP = _lib.load()
         _HIP.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
                                                  ctypes.c_uint]
         _HIP.hipHostGetDevicePointer.restype = ctypes.c_int

@@ -10,12 +10,22 @@
 // "LLM Systems 24", §3 Conclusion).  Running out of blocks is reported, never partially
 // applied, so the caller can preempt a sequence and retry (same Conclusion).
 //
+// Prompts that start with the same tokens share the blocks of that prefix even when they
+// arrive independently (prefix caching; "PagedAttention 与 vLLM 推理加速", §3.2 (3): requests
+// with one system prompt keep a single copy of its K/V).  A full prompt block is found by
+// its content: the content id of the block before it plus its own token ids, so a match
+// means the whole token prefix matches.  Cached blocks nobody holds stay cached until their
+// block is needed again, and are then evicted in the order they were released (a
+// sequence's blocks tail first), after the plain free blocks are used up.
+//
 // Per decode step the work is O(number of sequences appended): a length check, at most one
 // stack pop, and one slot computation each.  Plain single-threaded host code, no HIP.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <list>
 #include <new>
+#include <string>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
@@ -40,13 +50,67 @@ struct pkv_alloc {
   // Sequences preempted to the host: length and number of blocks to restore.
   std::unordered_map<int64_t, std::pair<int32_t, int32_t>> swapped;
 
+  // Prefix cache.  key = 8 bytes of the parent block's content id (-1 for the first block)
+  // followed by the block's block_size token ids.  Content ids are never reused, so a key
+  // whose parent was evicted can no longer be formed by a lookup.
+  std::unordered_map<std::string, int32_t> cache;
+  std::vector<std::string> key_of;  // per block, while registered
+  std::vector<int64_t> cid;         // per block: content id, -1 when not registered
+  int64_t next_cid = 0;
+  int32_t n_registered = 0;
+  std::list<int32_t> evictable;  // registered blocks with no holder; front goes first
+  std::vector<std::list<int32_t>::iterator> evict_pos;
+  std::vector<char> in_evictable;
+
   bool taken(int64_t id) const { return seqs.count(id) || swapped.count(id); }
 
+  // Blocks a call may take: free ones, then evictable cached ones.
+  int64_t available() const { return int64_t(free_stack.size()) + int64_t(evictable.size()); }
+
   int32_t pop() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {
+      b = evictable.front();
+      evictable.pop_front();
+      in_evictable[b] = 0;
+      unregister(b);
+    }
     ref[b] = 1;
     return b;
+  }
+  void unregister(int32_t b) {
+    auto it = cache.find(key_of[b]);
+    if (it != cache.end() && it->second == b) cache.erase(it);
+    key_of[b].clear();
+    key_of[b].shrink_to_fit();
+    cid[b] = -1;
+    --n_registered;
+  }
+  std::string make_key(int64_t parent, const int32_t* toks) const {
+    std::string k(sizeof(int64_t) + size_t(block_size) * sizeof(int32_t), '\0');
+    std::memcpy(&k[0], &parent, sizeof(int64_t));
+    std::memcpy(&k[sizeof(int64_t)], toks, size_t(block_size) * sizeof(int32_t));
+    return k;
+  }
+  // One reference less on each block of a table (logical order).  Blocks left with none go
+  // onto the free stack in logical order, or, if they hold a cached prefix, to the back of
+  // the eviction order tail first.
+  void release(const std::vector<int32_t>& table) {
+    std::vector<int32_t> gone;
+    for (int32_t b : table)
+      if (--ref[b] == 0) gone.push_back(b);
+    for (int32_t b : gone)
+      if (cid[b] < 0) free_stack.push_back(b);
+    for (auto it = gone.rbegin(); it != gone.rend(); ++it) {
+      const int32_t b = *it;
+      if (cid[b] < 0) continue;
+      evictable.push_back(b);
+      evict_pos[b] = std::prev(evictable.end());
+      in_evictable[b] = 1;
+    }
   }
   int64_t slot_of(const Sequence& s) const {
     // Token number s.len sits in logical page len / bs at offset len % bs.
@@ -65,6 +129,10 @@ pkv_status pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_
   a->num_blocks = num_blocks;
   a->block_size = block_size;
   a->ref.assign(num_blocks, 0);
+  a->key_of.resize(num_blocks);
+  a->cid.assign(num_blocks, -1);
+  a->evict_pos.resize(num_blocks);
+  a->in_evictable.assign(num_blocks, 0);
   a->free_stack.resize(num_blocks);
   if (free_order) {
     std::vector<char> seen(num_blocks, 0);
@@ -90,7 +158,7 @@ pkv_status pkv_seq_add(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t
   if (!a || num_tokens < 0 || (num_tokens > 0 && !slots_out)) return PKV_ERR_INVALID_ARG;
   if (a->taken(seq_id)) return PKV_ERR_DUPLICATE_SEQ;
   const int64_t need = (int64_t(num_tokens) + a->block_size - 1) / a->block_size;
-  if (need > int64_t(a->free_stack.size())) return PKV_ERR_OUT_OF_BLOCKS;
+  if (need > a->available()) return PKV_ERR_OUT_OF_BLOCKS;
   Sequence s;
   s.table.reserve(need);
   for (int64_t i = 0; i < need; ++i) s.table.push_back(a->pop());
@@ -98,6 +166,58 @@ pkv_status pkv_seq_add(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t
     slots_out[t] = a->slot_of(s);
     ++s.len;
   }
+  a->seqs.emplace(seq_id, std::move(s));
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_add_tokens(pkv_alloc* a, int64_t seq_id, const int32_t* tokens,
+                              int32_t num_tokens, int64_t* slots_out, int32_t* n_cached_out) {
+  if (!a || num_tokens < 0 || !n_cached_out) return PKV_ERR_INVALID_ARG;
+  if (num_tokens > 0 && (!tokens || !slots_out)) return PKV_ERR_INVALID_ARG;
+  if (a->taken(seq_id)) return PKV_ERR_DUPLICATE_SEQ;
+  const int32_t bs = a->block_size;
+  const int32_t full = num_tokens / bs;
+  const int64_t nb = (int64_t(num_tokens) + bs - 1) / bs;
+  // Longest run of leading full blocks whose prefixes are cached.
+  std::vector<int32_t> hits;
+  int64_t parent = -1;
+  int64_t reused_idle = 0;
+  for (int32_t j = 0; j < full; ++j) {
+    auto it = a->cache.find(a->make_key(parent, tokens + int64_t(j) * bs));
+    if (it == a->cache.end()) break;
+    const int32_t b = it->second;
+    hits.push_back(b);
+    if (a->ref[b] == 0) ++reused_idle;
+    parent = a->cid[b];
+  }
+  const int64_t need = nb - int64_t(hits.size());
+  if (need > a->available() - reused_idle) return PKV_ERR_OUT_OF_BLOCKS;
+  for (int32_t b : hits) {
+    if (a->in_evictable[b]) {
+      a->evictable.erase(a->evict_pos[b]);
+      a->in_evictable[b] = 0;
+    }
+    ++a->ref[b];
+  }
+  Sequence s;
+  s.table = hits;
+  s.table.reserve(nb);
+  for (int64_t j = int64_t(hits.size()); j < nb; ++j) {
+    const int32_t b = a->pop();
+    s.table.push_back(b);
+    if ((j + 1) * bs <= num_tokens) {  // a full prompt block: register its content
+      a->cid[b] = a->next_cid++;
+      a->key_of[b] = a->make_key(parent, tokens + j * bs);
+      a->cache[a->key_of[b]] = b;
+      ++a->n_registered;
+      parent = a->cid[b];
+    }
+  }
+  const int64_t shared = int64_t(hits.size()) * bs;
+  for (int32_t t = 0; t < num_tokens; ++t)
+    slots_out[t] = t < shared ? -1 : int64_t(s.table[t / bs]) * bs + t % bs;
+  s.len = num_tokens;
+  *n_cached_out = int32_t(shared);
   a->seqs.emplace(seq_id, std::move(s));
   return PKV_OK;
 }
@@ -145,7 +265,7 @@ pkv_status pkv_seq_append(pkv_alloc* a, const int64_t* seq_ids, int32_t n, int64
       }
     }
   }
-  if (need > int64_t(a->free_stack.size())) return PKV_ERR_OUT_OF_BLOCKS;
+  if (need > a->available()) return PKV_ERR_OUT_OF_BLOCKS;
 
   int32_t ncow = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -181,7 +301,7 @@ pkv_status pkv_seq_extend(pkv_alloc* a, int64_t seq_id, int32_t n, int64_t* slot
   const bool cow = n > 0 && s.len % a->block_size != 0 && a->ref[s.table.back()] > 1;
   const int64_t blocks_after = (int64_t(s.len) + n + a->block_size - 1) / a->block_size;
   const int64_t need = blocks_after - int64_t(s.table.size()) + (cow ? 1 : 0);
-  if (need > int64_t(a->free_stack.size())) return PKV_ERR_OUT_OF_BLOCKS;
+  if (need > a->available()) return PKV_ERR_OUT_OF_BLOCKS;
   int32_t ncow = 0;
   if (cow) {
     const int32_t old = s.table.back();
@@ -205,8 +325,7 @@ pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id) {
   if (!a) return PKV_ERR_INVALID_ARG;
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
-  for (int32_t b : it->second.table)
-    if (--a->ref[b] == 0) a->free_stack.push_back(b);
+  a->release(it->second.table);
   a->seqs.erase(it);
   return PKV_OK;
 }
@@ -222,8 +341,7 @@ pkv_status pkv_seq_swap_out(pkv_alloc* a, int64_t seq_id, int32_t max_blocks, in
   for (int32_t i = 0; i < nb; ++i) blocks_out[i] = s.table[i];
   *n_blocks_out = nb;
   a->swapped[seq_id] = {s.len, nb};
-  for (int32_t b : s.table)
-    if (--a->ref[b] == 0) a->free_stack.push_back(b);
+  a->release(s.table);
   a->seqs.erase(it);
   return PKV_OK;
 }
@@ -235,7 +353,7 @@ pkv_status pkv_seq_swap_in(pkv_alloc* a, int64_t seq_id, int32_t max_blocks, int
   if (it == a->swapped.end()) return PKV_ERR_UNKNOWN_SEQ;
   const int32_t len = it->second.first, nb = it->second.second;
   if (nb > max_blocks || (nb > 0 && !blocks_out)) return PKV_ERR_INVALID_ARG;
-  if (nb > int32_t(a->free_stack.size())) return PKV_ERR_OUT_OF_BLOCKS;
+  if (nb > a->available()) return PKV_ERR_OUT_OF_BLOCKS;
   Sequence s;
   s.len = len;
   s.table.reserve(nb);
@@ -293,8 +411,10 @@ pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out) 
 }
 
 int32_t pkv_num_free_blocks(const pkv_alloc* a) {
-  return a ? int32_t(a->free_stack.size()) : -1;
+  return a ? int32_t(a->available()) : -1;
 }
+
+int32_t pkv_num_cached_blocks(const pkv_alloc* a) { return a ? a->n_registered : -1; }
 
 int32_t pkv_block_refcount(const pkv_alloc* a, int32_t block) {
   if (!a || block < 0 || block >= a->num_blocks) return -1;
@@ -305,7 +425,7 @@ pkv_status pkv_usage(const pkv_alloc* a, int64_t* tokens_stored, int64_t* slots_
   if (!a || !tokens_stored || !slots_allocated) return PKV_ERR_INVALID_ARG;
   int64_t tok = 0;
   for (const auto& kv : a->seqs) tok += kv.second.len;
-  int64_t used = a->num_blocks - int64_t(a->free_stack.size());
+  int64_t used = a->num_blocks - a->available();
   *tokens_stored = tok;
   *slots_allocated = used * a->block_size;
   return PKV_OK;

@@ -29,6 +29,7 @@ int fail(const char* what, int iter) {
 
 struct Snapshot {
   int32_t free_blocks;
+  int32_t cached_blocks;
   std::vector<int32_t> refs;
   std::map<int64_t, std::vector<int32_t>> tables;
   std::map<int64_t, int32_t> lens;
@@ -37,6 +38,7 @@ struct Snapshot {
 Snapshot snap(const pkv_alloc* a, int32_t nblocks, const std::vector<int64_t>& ids) {
   Snapshot s;
   s.free_blocks = pkv_num_free_blocks(a);
+  s.cached_blocks = pkv_num_cached_blocks(a);
   for (int32_t b = 0; b < nblocks; ++b) s.refs.push_back(pkv_block_refcount(a, b));
   for (int64_t id : ids) {
     int32_t len = 0;
@@ -51,7 +53,7 @@ Snapshot snap(const pkv_alloc* a, int32_t nblocks, const std::vector<int64_t>& i
 }
 
 bool same(const Snapshot& x, const Snapshot& y) {
-  return x.free_blocks == y.free_blocks && x.refs == y.refs && x.tables == y.tables && x.lens == y.lens;
+  return x.free_blocks == y.free_blocks && x.cached_blocks == y.cached_blocks && x.refs == y.refs && x.tables == y.tables && x.lens == y.lens;
 }
 
 }  // namespace
@@ -67,9 +69,15 @@ int main(int argc, char** argv) {
     for (int32_t i = nblocks - 1; i > 0; --i) std::swap(order[i], order[below(uint32_t(i) + 1)]);
     pkv_alloc* a = nullptr;
     if (pkv_alloc_create(nblocks, bs, round % 2 ? order.data() : nullptr, &a) != PKV_OK) return fail("create", -1);
+    // A few "system prompts" that prompts start with, so that cached prefixes repeat.
+    std::vector<std::vector<int32_t>> systems(3);
+    for (auto& sp : systems) {
+      sp.resize(below(uint32_t(3 * bs + 1)));
+      for (auto& t : sp) t = int32_t(below(3));
+    }
     for (int it = 0; it < iters / 40; ++it) {
       const Snapshot before = snap(a, nblocks, ids);
-      const uint32_t op = below(8);
+      const uint32_t op = below(10);
       pkv_status st = PKV_OK;
       if (op == 0) {
         const int32_t n = int32_t(below(uint32_t(3 * bs + 2)));
@@ -86,6 +94,17 @@ int main(int argc, char** argv) {
         st = op == 6 ? pkv_seq_swap_out(a, id, nblocks, blocks.data(), &nb)
                      : pkv_seq_swap_in(a, id, nblocks, blocks.data(), &nb);
         if (st == PKV_OK && (nb < 0 || nb > nblocks)) return fail("swap block count", it);
+      } else if (op == 8 || op == 9) {
+        std::vector<int32_t> toks = systems[below(3)];
+        for (uint32_t k = below(uint32_t(2 * bs + 2)); k > 0; --k) toks.push_back(int32_t(below(3)));
+        std::vector<int64_t> slots(toks.size() + 1);
+        int32_t ncached = -1;
+        st = pkv_seq_add_tokens(a, ids[below(8)], toks.empty() ? nullptr : toks.data(),
+                                int32_t(toks.size()), slots.data(), &ncached);
+        if (st == PKV_OK && (ncached < 0 || ncached > int32_t(toks.size()) || ncached % bs))
+          return fail("cached token count", it);
+        for (int32_t t = 0; st == PKV_OK && t < int32_t(toks.size()); ++t)
+          if ((t < ncached) != (slots[t] < 0)) return fail("cached slots", it);
       } else if (op == 5) {
         const int32_t n = int32_t(below(uint32_t(2 * bs + 3)));
         std::vector<int64_t> slots(size_t(n) + 1);
@@ -120,6 +139,7 @@ int main(int argc, char** argv) {
         referenced += count[b] > 0;
       }
       if (referenced + after.free_blocks != nblocks) return fail("free + referenced", it);
+      if (after.cached_blocks < 0 || after.cached_blocks > nblocks) return fail("cached count", it);
       int32_t shared = -1;
       for (const auto& kv : after.tables) {
         int64_t id = kv.first;

@@ -233,3 +233,33 @@ def test_swap_capacity_and_unknown_ids():
         a.pkv_seq_swap_in(5, 8)
     assert e.value.name == "PKV_ERR_UNKNOWN_SEQ"
     assert a.pkv_seq_swap_in(0, 8).tolist() == [2, 1, 0] and a.pkv_seq_length(0) == 9
+
+
+def test_add_tokens_validation_and_accounting():
+    l = lib()
+    a = pkv.PkvAlloc(6, 2)
+    h = a._h
+    toks = (ctypes.c_int32 * 4)(1, 2, 3, 4)
+    slots = (ctypes.c_int64 * 4)()
+    nc = ctypes.c_int32(-7)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    assert l.pkv_seq_add_tokens(h, 0, toks, 4, slots, None) == 1        # no n_cached_out
+    assert l.pkv_seq_add_tokens(h, 0, None, 4, slots, ctypes.byref(nc)) == 1
+    assert l.pkv_seq_add_tokens(h, 0, toks, 4, None, ctypes.byref(nc)) == 1
+    assert l.pkv_seq_add_tokens(h, 0, toks, -1, slots, ctypes.byref(nc)) == 1
+    assert l.pkv_seq_add_tokens(None, 0, toks, 4, slots, ctypes.byref(nc)) == 1
+    assert nc.value == -7 and a.pkv_num_free_blocks() == 6 and a.pkv_num_cached_blocks() == 0
+    assert l.pkv_seq_add_tokens(h, 0, None, 0, None, ctypes.byref(nc)) == 0 and nc.value == 0
+    assert l.pkv_seq_add_tokens(h, 0, toks, 4, slots, ctypes.byref(nc)) == 4   # duplicate id
+    s, n = a.pkv_seq_add_tokens(1, [1, 2, 3, 4, 5])
+    assert n == 0 and a.pkv_num_cached_blocks() == 2 and a.pkv_num_free_blocks() == 3
+    s, n = a.pkv_seq_add_tokens(2, [1, 2, 3, 4])
+    assert n == 4 and s.tolist() == [-1] * 4 and a.pkv_num_free_blocks() == 3
+    a.pkv_seq_free(1)
+    a.pkv_seq_free(2)
+    # Everything is takeable again; the two prompt blocks stay cached until needed.
+    assert a.pkv_num_free_blocks() == 6 and a.pkv_num_cached_blocks() == 2
+    assert a.pkv_usage() == (0, 0)
+    a.pkv_seq_add(3, 12)  # all six blocks: both cached ones are evicted
+    assert a.pkv_num_cached_blocks() == 0 and a.pkv_num_free_blocks() == 0
+    assert l.pkv_num_cached_blocks(None) == -1

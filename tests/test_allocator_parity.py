@@ -33,6 +33,9 @@ def run_both(o, c, kind, *args):
         elif kind == "extend":
             s, p = o.extend(*args)
             ro = ("ok", (list(s), [list(x) for x in p]))
+        elif kind == "prompt":
+            sl, nc = o.add_tokens(*args)
+            ro = ("ok", (list(sl), nc))
         elif kind == "swap_out":
             ro = ("ok", list(o.swap_out(args[0])))
         elif kind == "swap_in":
@@ -54,6 +57,9 @@ def run_both(o, c, kind, *args):
         elif kind == "extend":
             s, p = c.pkv_seq_extend(*args)
             rc = ("ok", (s.tolist(), p.tolist()))
+        elif kind == "prompt":
+            sl, nc = c.pkv_seq_add_tokens(*args)
+            rc = ("ok", (sl.tolist(), nc))
         elif kind == "swap_out":
             rc = ("ok", c.pkv_seq_swap_out(args[0], 64).tolist())
         elif kind == "swap_in":
@@ -68,6 +74,7 @@ def run_both(o, c, kind, *args):
 
 def same_state(o, c):
     assert c.pkv_num_free_blocks() == o.num_free()
+    assert c.pkv_num_cached_blocks() == o.num_cached()
     assert [c.pkv_block_refcount(b) for b in range(o.num_blocks)] == o.ref
     assert c.pkv_block_refcount(-1) == -1 and c.pkv_block_refcount(o.num_blocks) == -1
     seqs = sorted(o.tables)
@@ -88,7 +95,7 @@ def same_state(o, c):
 
 
 ops = st.lists(st.tuples(st.sampled_from(["add", "fork", "append", "free", "extend", "swap_out",
-                                          "swap_in"]),
+                                          "swap_in", "prompt", "prompt"]),
                          st.integers(0, 6), st.integers(0, 6), st.integers(0, 11)),
                min_size=1, max_size=80)
 
@@ -100,8 +107,13 @@ def test_random_operation_sequences(ops, bs, nblocks, seed, use_order):
     order = np.random.default_rng(seed).permutation(nblocks).astype(np.int32) if use_order else None
     o = oracle.OracleAllocator(nblocks, bs, order)
     c = pkv.PkvAlloc(nblocks, bs, order)
+    rng = np.random.default_rng(seed)
+    # Prompts start with one of a few "system prompts" so that prefixes repeat.
+    systems = [[int(t) for t in rng.integers(0, 3, size=int(rng.integers(0, 9)))] for _ in range(4)]
     for kind, x, y, n in ops:
-        if kind == "add":
+        if kind == "prompt":
+            args = (x, systems[y % 4] + [int(t) for t in rng.integers(0, 3, size=n % 6)])
+        elif kind == "add":
             args = (x, n)
         elif kind == "fork":
             args = (x, y)

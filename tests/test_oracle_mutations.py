@@ -186,3 +186,94 @@ def test_prefill_mistakes_are_caught(monkeypatch, kw):
         pins.test_prefill_on_cached_context_equals_masked_sdpa()
     with pytest.raises(FAIL):
         pins.test_prefill_brute_force_tiny()
+
+
+# -- prefix caching ----------------------------------------------------------------------
+class _LastBlockKeys(dict):
+    """A cache that keys a block by its own tokens only, not by the prefix before them."""
+
+    def __init__(self, bs):
+        super().__init__()
+        self.bs = bs
+
+    def get(self, k, default=None):
+        return super().get(k[-self.bs:], default)
+
+    def __setitem__(self, k, v):
+        super().__setitem__(k[-self.bs:], v)
+
+
+class _BlockContentOnly(oracle.OracleAllocator):
+    def __init__(self, *a, **kw):
+        super().__init__(*a, **kw)
+        self.cache = _LastBlockKeys(self.block_size)
+
+    def _restore(self, snap):
+        super()._restore(snap)
+        c = _LastBlockKeys(self.block_size)
+        dict.update(c, self.cache)
+        self.cache = c
+
+
+class _HeadFirstRelease(oracle.OracleAllocator):
+    def _release(self, blocks):
+        gone = []
+        for b in blocks:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                gone.append(b)
+        for b in gone:
+            (self.evictable if b in self.cached_key else self.free).append(b)
+
+
+class _HitsStayIdle(oracle.OracleAllocator):
+    def add_tokens(self, seq, tokens):
+        idle = list(self.evictable)
+        out = super().add_tokens(seq, tokens)
+        # The shared blocks are put back on the idle list although they are now held.
+        self.evictable = [b for b in idle if b in self.evictable or self.ref[b] > 0]
+        return out
+
+
+class _NoRegistration(oracle.OracleAllocator):
+    def add_tokens(self, seq, tokens):
+        out = super().add_tokens(seq, tokens)
+        for b in self.tables[seq]:
+            if self.ref[b] == 1 and b in self.cached_key:
+                del self.cache[self.cached_key.pop(b)]
+        return out
+
+
+def _prefix_pins():
+    from tests import test_oracle_prefix_cache as pc
+    return pc
+
+
+def test_block_content_only_matching_is_caught(monkeypatch):
+    pc = _prefix_pins()
+    monkeypatch.setattr(oracle, "OracleAllocator", _BlockContentOnly)
+    with pytest.raises(FAIL):
+        pc.test_sharing_needs_the_whole_prefix()
+    with pytest.raises(FAIL):
+        pc.test_random_request_streams_read_back_their_own_tokens()
+
+
+def test_head_first_release_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "OracleAllocator", _HeadFirstRelease)
+    with pytest.raises(FAIL):
+        _prefix_pins().test_eviction_order_worked_example()
+
+
+def test_shared_blocks_left_evictable_are_caught(monkeypatch):
+    pc = _prefix_pins()
+    monkeypatch.setattr(oracle, "OracleAllocator", _HitsStayIdle)
+    with pytest.raises(FAIL):
+        pc.test_eviction_order_worked_example_exact()
+    with pytest.raises(FAIL):
+        pc.test_random_request_streams_read_back_their_own_tokens()
+
+
+def test_missing_registration_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "OracleAllocator", _NoRegistration)
+    with pytest.raises(FAIL + (oracle.OracleError,)):
+        _prefix_pins().test_page_example_by_content(pins_golden())

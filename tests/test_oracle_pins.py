@@ -133,11 +133,17 @@ def check_invariants(a: oracle.OracleAllocator):
             counts[b] += 1
     assert counts == a.ref
     free = set(a.free)
-    assert len(free) == len(a.free)
-    assert all(a.ref[b] == 0 for b in free)
+    idle = set(a.evictable)
+    assert len(free) == len(a.free) and len(idle) == len(a.evictable)
+    assert all(a.ref[b] == 0 for b in free | idle)
     referenced = {b for b in range(a.num_blocks) if a.ref[b] > 0}
-    assert not (free & referenced)
-    assert len(free) + len(referenced) == a.num_blocks
+    assert not (free & referenced) and not (free & idle)
+    assert len(free) + len(idle) + len(referenced) == a.num_blocks
+    # Cached content: free blocks hold none, idle ones do; a reachable entry's block is
+    # registered under that very prefix.
+    assert not (free & set(a.cached_key)) and idle <= set(a.cached_key)
+    for key, b in a.cache.items():
+        assert a.cached_key[b] == key and len(key) % a.block_size == 0
 
 
 op_strategy = st.lists(

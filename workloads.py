@@ -294,3 +294,107 @@ def step_ops(w: Workload):
     if w.n_new is not None:
         return [("extend", b, int(w.n_new[b])) for b in range(w.batch)]
     return [("append", list(range(w.batch)))]
+
+
+# -- independently arriving requests that share system prompts ------------------------------
+@dataclasses.dataclass(frozen=True)
+class PromptStreamConfig:
+    """Requests arriving one at a time, each one of ``num_systems`` system prompts followed by
+    its own text ("PagedAttention 与 vLLM 推理加速", §3.2 (3): requests with one system prompt
+    and different questions).  At most ``live`` requests run at once: when one more arrives,
+    the oldest finishes first.  Afterwards the ``live`` remaining requests decode one token.
+    System prompt and own lengths are drawn uniformly in the inclusive ranges given."""
+
+    name: str
+    cfg_id: int
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    num_requests: int
+    num_systems: int
+    system_len: tuple
+    own_len: tuple
+    live: int
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+PROMPT_STREAMS = {
+    # Small enough for the oracle; the pool is tight so idle cached blocks get evicted.
+    "prompt_stream_small": PromptStreamConfig("prompt_stream_small", 9, "f16", 8, 4, 128, 16, 96,
+                                              40, 3, (20, 200), (1, 60), 6),
+    # LLaMA-7B heads, 256 requests over 4 system prompts of 512-2048 tokens.
+    "prompt_stream_llama7b": PromptStreamConfig("prompt_stream_llama7b", 10, "f16", 32, 32, 128,
+                                                16, 16384, 256, 4, (512, 2048), (16, 512), 64),
+}
+
+
+@dataclasses.dataclass
+class PromptStream:
+    cfg: PromptStreamConfig
+    system_of: np.ndarray      # [R] which system prompt each request starts with
+    system_lens: np.ndarray    # [S]
+    own_lens: np.ndarray       # [R]
+    free_order: np.ndarray     # physical placement (pop order)
+    ops: list                  # ("prompt", r) / ("free", r), in arrival order
+    live: list                 # requests alive at the end, in arrival order
+    sys_k: torch.Tensor        # [S, max system_len, Hkv, D]
+    sys_v: torch.Tensor
+    own_k: torch.Tensor        # [R, max own_len + 1, Hkv, D]  (+1: the decoded token)
+    own_v: torch.Tensor
+    q: torch.Tensor            # [len(live), Hq, D]
+
+    def tokens(self, r: int) -> np.ndarray:
+        """Token ids of request r's prompt: its system prompt's, then its own (int32)."""
+        s = int(self.system_of[r])
+        ls, lo = int(self.system_lens[s]), int(self.own_lens[r])
+        return np.concatenate([s * 100_000 + np.arange(ls),
+                               500_000_000 + r * 100_000 + np.arange(lo)]).astype(np.int32)
+
+    def token_kv(self, r: int, lo: int, hi: int):
+        """K/V rows of request r's positions lo .. hi-1 (its system prompt's rows first; the
+        position right after the prompt is the decoded token)."""
+        s = int(self.system_of[r])
+        ls = int(self.system_lens[s])
+        ks, vs = [], []
+        if lo < ls:
+            ks.append(self.sys_k[s, lo:min(hi, ls)])
+            vs.append(self.sys_v[s, lo:min(hi, ls)])
+        if hi > ls:
+            ks.append(self.own_k[r, max(lo, ls) - ls:hi - ls])
+            vs.append(self.own_v[r, max(lo, ls) - ls:hi - ls])
+        return torch.cat(ks), torch.cat(vs)
+
+
+def make_prompt_stream(cfg: PromptStreamConfig, device="cpu") -> PromptStream:
+    streams = seed_streams(cfg.cfg_id)
+    rng = np.random.Generator(np.random.PCG64(streams[0]))
+    S, R = cfg.num_systems, cfg.num_requests
+    system_lens = rng.integers(cfg.system_len[0], cfg.system_len[1] + 1, size=S)
+    system_of = rng.integers(0, S, size=R)
+    own_lens = rng.integers(cfg.own_len[0], cfg.own_len[1] + 1, size=R)
+    placement = np.random.Generator(np.random.PCG64(streams[1]))
+    free_order = placement.permutation(cfg.num_blocks).astype(np.int32)
+    ops, alive = [], []
+    for r in range(R):
+        if len(alive) == cfg.live:
+            ops.append(("free", alive.pop(0)))
+        ops.append(("prompt", r))
+        alive.append(r)
+    h, d, dt = cfg.num_kv_heads, cfg.head_dim, DTYPES[cfg.dtype]
+    ms, mo = int(system_lens.max()), int(own_lens.max()) + 1
+    k = draw_normal((S * ms + R * mo, h, d), streams[3], dt, device)
+    v = draw_normal((S * ms + R * mo, h, d), streams[4], dt, device)
+    q = draw_normal((len(alive), cfg.num_q_heads, d), streams[2], dt, device)
+    return PromptStream(cfg, system_of, system_lens, own_lens, free_order, ops, alive,
+                        k[: S * ms].view(S, ms, h, d), v[: S * ms].view(S, ms, h, d),
+                        k[S * ms:].view(R, mo, h, d), v[S * ms:].view(R, mo, h, d), q)
