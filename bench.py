@@ -32,6 +32,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 HOST_LINK_GBS = 64.0  # MI355X host interface, PCIe 5.0 x16: 32 GT/s x 16 lanes per direction
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -109,6 +110,9 @@ def parse():
                          "the block-move kernels write and read the pinned host copy themselves")
     ap.add_argument("--swap-every", type=int, default=8,
                     help="--swap: every n-th sequence of the batch is a victim")
+    ap.add_argument("--prefix-cache", action="store_true",
+                    help="measure prompt admission with prefix caching (prompt_stream_llama7b) "
+                         "instead of decode")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries of --config from rocprofv3 output in DIR "
                          "(kt_<config>/, pmc_fetch_<config>/, pmc_write_<config>/, kt_<config>.log)")
@@ -537,6 +541,170 @@ def main_swap(args):
     print(json.dumps(res), flush=True)
 
 
+def main_prefix_cache(args):
+    """One step = admitting the whole request stream (256 LLaMA-7B-shaped requests over 4
+    system prompts, at most 64 running) as a serving loop would, in batches of 16 arrivals:
+    each prompt is placed by the allocator (pkv_seq_add_tokens; pkv_seq_add when sharing is
+    off), then per batch one upload of the slots, one pkv_reshape_and_cache of the tokens
+    that need writing, one upload of the batch's block tables, and one causal paged prefill
+    of the tokens not found in the cache against the whole prompt (with sharing off: every
+    token).  Finished requests are freed as new ones arrive.  Prompt K/V rows and queries
+    are resident in HBM before timing.  ``value`` is prompt tokens admitted per second with
+    prefix caching; the same stream without sharing is timed beside it.  ``roofline`` rates
+    the prefill (the causal attention flops it has to do, over its time)."""
+    import torch
+    import workloads as W
+    import paged_kv_cache_359_amd as pkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    c = W.PROMPT_STREAMS["prompt_stream_llama7b"]
+    print(f"[bench] building {c.name}", file=sys.stderr, flush=True)
+    ps = W.make_prompt_stream(c, device=dev)
+    R, batch, bs = c.num_requests, 16, c.block_size
+    toks = [ps.tokens(r) for r in range(R)]
+    n_tok = np.array([t.size for t in toks], dtype=np.int64)
+    offs = np.concatenate([[0], np.cumsum(n_tok)]).astype(np.int64)
+    total_tokens = int(offs[-1])
+    # Every prompt's K/V rows and queries, in arrival order (requests arrive as 0, 1, 2, ...).
+    rows = [ps.token_kv(r, 0, int(n_tok[r])) for r in range(R)]
+    k_all = torch.cat([x[0] for x in rows])
+    v_all = torch.cat([x[1] for x in rows])
+    del rows
+    q_all = W.draw_normal((total_tokens, c.num_q_heads, c.head_dim), W.seed_streams(c.cfg_id)[2],
+                          c.torch_dtype, dev)
+    row_bytes = 2 * c.num_kv_heads * c.head_dim * DTYPE_BYTES[c.dtype]  # K and V of one token
+    shape = (c.num_blocks, c.num_kv_heads, bs, c.head_dim)
+    k_cache = torch.zeros(shape, dtype=c.torch_dtype, device=dev)
+    v_cache = torch.zeros_like(k_cache)
+    # Untimed dry run: how many leading tokens of each prompt the cache already holds.
+    probe = pkv.PkvAlloc(c.num_blocks, bs, ps.free_order)
+    n_cached = np.zeros(R, dtype=np.int64)
+    for op, r in ps.ops:
+        if op == "free":
+            probe.pkv_seq_free(r)
+        else:
+            n_cached[r] = probe.pkv_seq_add_tokens(r, toks[r])[1]
+    del probe
+    batches = [list(range(b, min(b + batch, R))) for b in range(0, R, batch)]
+    max_blocks = int(-(-n_tok.max() // bs))
+    slots_h = torch.empty(total_tokens, dtype=torch.int64, pin_memory=True)
+    slots_d = torch.empty(total_tokens, dtype=torch.int64, device=dev)
+    tab_h = torch.empty((len(batches), batch, max_blocks), dtype=torch.int32, pin_memory=True)
+    tab_d = torch.empty((len(batches), batch, max_blocks), dtype=torch.int32, device=dev)
+    lens_d = [torch.from_numpy(n_tok[bt].astype(np.int32)).to(dev) for bt in batches]
+    stream = torch.cuda.current_stream(dev)
+
+    def plan(share):
+        """Per batch: query rows of the tokens to prefill, their query_start, and the sizes."""
+        new = n_tok - (n_cached if share else 0)
+        idx = np.concatenate([np.arange(offs[r + 1] - new[r], offs[r + 1]) for r in range(R)])
+        q = q_all.index_select(0, torch.from_numpy(idx).to(dev))
+        qoff = np.concatenate([[0], np.cumsum(new)])
+        out = []
+        for bt in batches:
+            qs = (qoff[bt[0]: bt[-1] + 2] - qoff[bt[0]]).astype(np.int32)
+            out.append(dict(q=q[qoff[bt[0]]: qoff[bt[-1] + 1]], qs=torch.from_numpy(qs).to(dev),
+                            max_q=int(new[bt].max()), max_ctx=int(n_tok[bt].max())))
+        return new, q, out
+
+    def admit(share, pl, ev_out):
+        alloc = pkv.PkvAlloc(c.num_blocks, bs, ps.free_order)
+        sh, th = slots_h.numpy(), tab_h.numpy()
+        written, host, done = 0, 0.0, 0
+        for op, r in ps.ops:
+            if op == "free":
+                alloc.pkv_seq_free(r)
+                continue
+            h0 = time.perf_counter()
+            if share:
+                sl, nc = alloc.pkv_seq_add_tokens(r, toks[r])
+                assert nc == n_cached[r]
+            else:
+                sl = alloc.pkv_seq_add(r, int(n_tok[r]))
+            host += time.perf_counter() - h0
+            sh[offs[r]:offs[r + 1]] = sl
+            written += int(n_tok[r] - (n_cached[r] if share else 0))
+            bi = r // batch
+            bt = batches[bi]
+            if r != bt[-1]:
+                continue
+            lo, hi = int(offs[bt[0]]), int(offs[bt[-1] + 1])
+            slots_d[lo:hi].copy_(slots_h[lo:hi], non_blocking=True)
+            alloc.pkv_get_block_tables(bt, max_blocks, th[bi, :len(bt)])
+            tab_d[bi, :len(bt)].copy_(tab_h[bi, :len(bt)], non_blocking=True)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            pkv.pkv_reshape_and_cache(k_all[lo:hi], v_all[lo:hi], slots_d[lo:hi], k_cache, v_cache)
+            e[1].record(stream)
+            b = pl[bi]
+            o = torch.empty_like(b["q"])
+            pkv.pkv_paged_attention_prefill(o, b["q"], k_cache, v_cache, tab_d[bi, :len(bt)],
+                                            lens_d[bi], b["qs"], b["max_q"], b["max_ctx"], c.scale)
+            e[2].record(stream)
+            ev_out.append(e)
+            done += 1
+        return written, host, alloc
+
+    results = {}
+    for share in (True, False):
+        new, q, pl = plan(share)
+        for _ in range(args.warmup):
+            admit(share, pl, [])
+            torch.cuda.synchronize()  # the pinned buffers are rewritten next pass
+        times, hosts, evs = [], [], []
+        for rep in range(args.steps):
+            box, ev = {}, []
+            elapsed = run_timed(lambda _: box.update(out=admit(share, pl, ev)), 0, 1,
+                                torch.cuda.synchronize)
+            times.append(elapsed)
+            hosts.append(box["out"][1])
+            evs.append(ev)
+        written, _, alloc = box["out"]
+        wr_ms = float(np.median([sum(e[0].elapsed_time(e[1]) for e in ev) for ev in evs]))
+        pf_ms = float(np.median([sum(e[1].elapsed_time(e[2]) for e in ev) for ev in evs]))
+        flops = prefill_flops(c, n_tok, new)
+        results[share] = dict(ms=1e3 * float(np.median(times)), host_ms=1e3 * float(np.median(hosts)),
+                              written=written, write_ms=wr_ms, prefill_ms=pf_ms, flops=flops,
+                              cached_blocks=alloc.pkv_num_cached_blocks())
+        del q, pl
+    sh, un = results[True], results[False]
+    rate = lambda r: total_tokens / (r["ms"] * 1e-3)
+    tf = sh["flops"] / (sh["prefill_ms"] * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[c.dtype]
+    res = {
+        "metric": "prompt admission with prefix caching: prompt tokens/s (allocator + K/V cache "
+                  "write + causal paged prefill of the uncached tokens), 1 GPU",
+        "value": round(rate(sh), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sh["ms"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": f"{c.name}: {R} requests over {c.num_systems} system prompts of "
+                               f"{c.system_len[0]}-{c.system_len[1]} tokens plus {c.own_len[0]}-"
+                               f"{c.own_len[1]} own tokens, at most {c.live} running, admitted "
+                               f"{batch} at a time, Hq={c.num_q_heads}, Hkv={c.num_kv_heads}, "
+                               f"D={c.head_dim}, block={bs}, {c.dtype}",
+                   "prompt_tokens": total_tokens},
+        "shared_token_fraction": round(float(n_cached.sum()) / total_tokens, 5),
+        "speedup_vs_without_sharing": round(un["ms"] / sh["ms"], 3),
+        "without_sharing": {"tokens_per_s": round(rate(un), 1), "ms_per_step": round(un["ms"], 4),
+                            "cache_write_ms": round(un["write_ms"], 4),
+                            "prefill_ms": round(un["prefill_ms"], 4),
+                            "prefill_tflop": round(un["flops"] / 1e12, 4),
+                            "host_us_per_request": round(1e3 * un["host_ms"] / R, 3)},
+        "cache_write_ms": round(sh["write_ms"], 4), "prefill_ms": round(sh["prefill_ms"], 4),
+        "prefill_tflop": round(sh["flops"] / 1e12, 4),
+        "tokens_written": sh["written"], "host_us_per_request": round(1e3 * sh["host_ms"] / R, 3),
+        "cached_blocks_at_end": sh["cached_blocks"],
+        "cache_write_GBs": round(2 * sh["written"] * row_bytes / (sh["write_ms"] * 1e-3) / 1e9, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tf / peak, 5), "traffic": None,
+                     "kernel": "paged_attention_prefill (uncached tokens)",
+                     "flops_per_launch": round(sh["flops"] / len(batches))},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def summarize(config, outdir):
     """Writes profiles/paged_decode_<config>_kernel_trace.txt and _hbm_traffic.txt from the
     rocprofv3 output of the three runs named in those files (one kernel trace, one
@@ -644,6 +812,8 @@ def main():
         return summarize(args.config, args.summarize)
     if args.swap:
         return main_swap(args)
+    if args.prefix_cache:
+        return main_prefix_cache(args)
 
     import torch
     import workloads as W

@@ -25,7 +25,6 @@
 #include <cstring>
 #include <list>
 #include <new>
-#include <string>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
@@ -50,11 +49,15 @@ struct pkv_alloc {
   // Sequences preempted to the host: length and number of blocks to restore.
   std::unordered_map<int64_t, std::pair<int32_t, int32_t>> swapped;
 
-  // Prefix cache.  key = 8 bytes of the parent block's content id (-1 for the first block)
-  // followed by the block's block_size token ids.  Content ids are never reused, so a key
-  // whose parent was evicted can no longer be formed by a lookup.
-  std::unordered_map<std::string, int32_t> cache;
-  std::vector<std::string> key_of;  // per block, while registered
+  // Prefix cache.  A registered block is found by its content: the content id of the
+  // block before it (-1 for a first block) and its own block_size token ids.  Entries are
+  // indexed by a 64-bit hash of that content and confirmed by comparing it in full, so a
+  // hash collision never makes a false match.  Content ids are never reused, so content
+  // whose parent was evicted can no longer be looked up.
+  std::unordered_multimap<uint64_t, int32_t> cache;
+  std::vector<int32_t> blk_tokens;  // [num_blocks * block_size]: a registered block's tokens
+  std::vector<int64_t> parent_of;   // per block: parent content id while registered
+  std::vector<uint64_t> hash_of;    // per block: content hash while registered
   std::vector<int64_t> cid;         // per block: content id, -1 when not registered
   int64_t next_cid = 0;
   int32_t n_registered = 0;
@@ -82,18 +85,48 @@ struct pkv_alloc {
     return b;
   }
   void unregister(int32_t b) {
-    auto it = cache.find(key_of[b]);
-    if (it != cache.end() && it->second == b) cache.erase(it);
-    key_of[b].clear();
-    key_of[b].shrink_to_fit();
+    auto range = cache.equal_range(hash_of[b]);
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == b) {
+        cache.erase(it);
+        break;
+      }
     cid[b] = -1;
     --n_registered;
   }
-  std::string make_key(int64_t parent, const int32_t* toks) const {
-    std::string k(sizeof(int64_t) + size_t(block_size) * sizeof(int32_t), '\0');
-    std::memcpy(&k[0], &parent, sizeof(int64_t));
-    std::memcpy(&k[sizeof(int64_t)], toks, size_t(block_size) * sizeof(int32_t));
-    return k;
+  uint64_t content_hash(int64_t parent, const int32_t* toks) const {
+    // 64-bit multiply-xorshift mixing of the parent id and each token.
+    uint64_t h = uint64_t(parent) * 0x9E3779B97F4A7C15ull ^ 0xD6E8FEB86659FD93ull;
+    for (int32_t i = 0; i < block_size; ++i) {
+      h ^= uint32_t(toks[i]);
+      h *= 0xBF58476D1CE4E5B9ull;
+      h ^= h >> 31;
+    }
+#ifdef PKV_HASH_BITS
+    // Test builds narrow the hash so that different contents collide all the time.
+    h &= (uint64_t(1) << PKV_HASH_BITS) - 1;
+#endif
+    return h;
+  }
+  // The registered block holding this content, or -1.
+  int32_t find(int64_t parent, const int32_t* toks) const {
+    auto range = cache.equal_range(content_hash(parent, toks));
+    for (auto it = range.first; it != range.second; ++it) {
+      const int32_t b = it->second;
+      if (parent_of[b] == parent &&
+          std::memcmp(&blk_tokens[size_t(b) * block_size], toks,
+                      size_t(block_size) * sizeof(int32_t)) == 0)
+        return b;
+    }
+    return -1;
+  }
+  void register_block(int32_t b, int64_t parent, const int32_t* toks) {
+    cid[b] = next_cid++;
+    parent_of[b] = parent;
+    hash_of[b] = content_hash(parent, toks);
+    std::memcpy(&blk_tokens[size_t(b) * block_size], toks, size_t(block_size) * sizeof(int32_t));
+    cache.emplace(hash_of[b], b);
+    ++n_registered;
   }
   // One reference less on each block of a table (logical order).  Blocks left with none go
   // onto the free stack in logical order, or, if they hold a cached prefix, to the back of
@@ -129,7 +162,9 @@ pkv_status pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_
   a->num_blocks = num_blocks;
   a->block_size = block_size;
   a->ref.assign(num_blocks, 0);
-  a->key_of.resize(num_blocks);
+  a->blk_tokens.assign(size_t(num_blocks) * block_size, 0);
+  a->parent_of.assign(num_blocks, -1);
+  a->hash_of.assign(num_blocks, 0);
   a->cid.assign(num_blocks, -1);
   a->evict_pos.resize(num_blocks);
   a->in_evictable.assign(num_blocks, 0);
@@ -183,9 +218,8 @@ pkv_status pkv_seq_add_tokens(pkv_alloc* a, int64_t seq_id, const int32_t* token
   int64_t parent = -1;
   int64_t reused_idle = 0;
   for (int32_t j = 0; j < full; ++j) {
-    auto it = a->cache.find(a->make_key(parent, tokens + int64_t(j) * bs));
-    if (it == a->cache.end()) break;
-    const int32_t b = it->second;
+    const int32_t b = a->find(parent, tokens + int64_t(j) * bs);
+    if (b < 0) break;
     hits.push_back(b);
     if (a->ref[b] == 0) ++reused_idle;
     parent = a->cid[b];
@@ -206,10 +240,7 @@ pkv_status pkv_seq_add_tokens(pkv_alloc* a, int64_t seq_id, const int32_t* token
     const int32_t b = a->pop();
     s.table.push_back(b);
     if ((j + 1) * bs <= num_tokens) {  // a full prompt block: register its content
-      a->cid[b] = a->next_cid++;
-      a->key_of[b] = a->make_key(parent, tokens + j * bs);
-      a->cache[a->key_of[b]] = b;
-      ++a->n_registered;
+      a->register_block(b, parent, tokens + j * bs);
       parent = a->cid[b];
     }
   }

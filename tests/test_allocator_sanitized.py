@@ -1,6 +1,8 @@
 """The host allocator built with AddressSanitizer and UndefinedBehaviorSanitizer (g++, host
 code only), driven by randomised operation sequences through its C ABI
-(tests/native/allocator_fuzz.cpp checks the invariants after every call)."""
+(tests/native/allocator_fuzz.cpp checks the invariants and every sequence's read-back content
+after every call).  A second build narrows the prefix cache's content hash to 2 bits, so that
+different block contents collide constantly: a match must still mean equal content."""
 import os
 import shutil
 import subprocess
@@ -11,9 +13,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
-def test_allocator_under_sanitizers(tmp_path):
+@pytest.mark.parametrize("defines", [[], ["-DPKV_HASH_BITS=2"]], ids=["full_hash", "2_bit_hash"])
+def test_allocator_under_sanitizers(tmp_path, defines):
     exe = tmp_path / "allocator_fuzz"
-    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", *defines,
            "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
            "-I", os.path.join(ROOT, "include"),
            os.path.join(ROOT, "tests", "native", "allocator_fuzz.cpp"),
