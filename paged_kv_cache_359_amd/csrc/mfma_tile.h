@@ -24,6 +24,10 @@ namespace pkv {
 // For bf16 the probabilities are split into a bf16 high part and a bf16 remainder (two
 // products), so P keeps ~16 significant bits; fp16 P keeps 11.
 // =========================================================================================
+// Largest amount (log2 units) by which a score may exceed the softmax reference before
+// the reference moves: probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.f;
+
 template <int DT, int D, int BS>
 struct Mfma {
   static_assert(DT == DT_F16 || DT == DT_BF16, "16-bit only");
@@ -66,11 +70,12 @@ struct Mfma {
   }
 
   // The K/V of one 32-token chunk as this lane holds it: K rows cs + 16hf + lane%16 (8
-  // elements per k-step) and V rows cs + 16hf + 4*(lane/16) + i, elements
-  // [E*(lane%16), E*(lane%16) + E).  compute() zeroes the V rows of tokens that do not exist.
+  // elements per k-step), and the V^T operands of the E output tiles, built from V rows
+  // cs + 16hf + 4*(lane/16) + i, elements [E*(lane%16), E*(lane%16) + E), with the rows of
+  // tokens that do not exist zeroed.  Built once per chunk, they serve every column tile.
   struct Chunk {
     uint4 kr[2][KK];
-    uint32_t vr[2][4][E / 2];
+    vec8 vop[E];
     bool vok[2][4];
     bool need_mask;  // wave-uniform: some row of this chunk does not exist
   };
@@ -108,6 +113,7 @@ struct Mfma {
         vp[hf][i] = vb + size_t(vv ? idv : 0) * blk_bytes + size_t(tv % BS) * D * 2 + E * n16 * 2;
       }
     }
+    uint32_t vr[2][4][E / 2];
     if (cached) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -117,10 +123,10 @@ struct Mfma {
         for (int i = 0; i < 4; ++i) {
           if constexpr (E == 8) {
             const uint4 w = load_cached(vp[hf][i]);
-            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y, ck.vr[hf][i][2] = w.z, ck.vr[hf][i][3] = w.w;
+            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
           } else {
             const uint2 w = load_cached8(vp[hf][i]);
-            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y;
+            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
           }
         }
       }
@@ -133,22 +139,76 @@ struct Mfma {
         for (int i = 0; i < 4; ++i) {
           if constexpr (E == 8) {
             const uint4 w = load_stream(vp[hf][i]);
-            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y, ck.vr[hf][i][2] = w.z, ck.vr[hf][i][3] = w.w;
+            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
           } else {
             const uint2 w = load_stream8(vp[hf][i]);
-            ck.vr[hf][i][0] = w.x, ck.vr[hf][i][1] = w.y;
+            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
           }
         }
       }
     }
     ck.need_mask = need_mask;
+    if (need_mask) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!ck.vok[hf][i])
+#pragma unroll
+            for (int q = 0; q < E / 2; ++q) vr[hf][i][q] = 0u;  // unused slots may hold anything
+    }
+    make_vop(vr, ck);
+  }
+
+  // V^T operand of output tile r: element r of each of the lane's eight token rows.
+  __device__ static void make_vop(const uint32_t (&vr)[2][4][E / 2], Chunk& ck) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = vr[(2 * q) >> 2][(2 * q) & 3][r >> 1];
+        const uint32_t hi = vr[(2 * q + 1) >> 2][(2 * q + 1) & 3][r >> 1];
+        // One byte permute: the low (r even) or high (r odd) 16-bit halves of lo and hi, lo's
+        // in the result's low half.  Selector bytes 0-3 name lo's bytes, 4-7 hi's.
+        w[q] = __builtin_amdgcn_perm(hi, lo, (r & 1) ? 0x07060302u : 0x05040100u);
+      }
+      ck.vop[r] = __builtin_bit_cast(vec8, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  }
+
+  // The same chunk from an LDS copy: 32 K rows at kl and 32 V rows at vl, `pitch` bytes
+  // apart, rows of tokens that do not exist already zero.  vok and need_mask are the
+  // caller's.
+  __device__ static void load_lds(const char* kl, const char* vl, int pitch, int lane, Chunk& ck) {
+    const int n16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        ck.kr[hf][kk] = *reinterpret_cast<const uint4*>(kl + (16 * hf + n16) * pitch + (32 * kk + 8 * g4) * 2);
+    uint32_t vr[2][4][E / 2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const char* p = vl + (16 * hf + 4 * g4 + i) * pitch + E * n16 * 2;
+        if constexpr (E == 8) {
+          const uint4 w = *reinterpret_cast<const uint4*>(p);
+          vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2*>(p);
+          vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
+        }
+      }
+    make_vop(vr, ck);
   }
 
   // Online-softmax update of one 16-column tile with a loaded chunk starting at token cs.
   // CAUSAL: the lane's column may only see keys at positions <= lim; lim_min is the smallest
   // lim of the tile (wave-uniform).
   template <bool CAUSAL = false>
-  __device__ static void compute(const DecodeArgs& a, Chunk& ck, int cs, int lane,
+  __device__ static void compute(const DecodeArgs& a, const Chunk& ck, int cs, int lane,
                                  const vec8 (&qop)[KK], State& st, int lim = 0, int lim_min = 0) {
     const int g4 = lane >> 4;
     bool need_mask = ck.need_mask;
@@ -168,29 +228,35 @@ struct Mfma {
       for (int i = 0; i < 4; ++i) {
         sv[hf][i] = s[hf][i] * a.scale_log2;
         if (need_mask) {
-          if (!ck.vok[hf][i]) {
-            sv[hf][i] = kNegInf;
-#pragma unroll
-            for (int q = 0; q < E / 2; ++q) ck.vr[hf][i][q] = 0u;  // unused slots may hold anything
-          }
+          if (!ck.vok[hf][i]) sv[hf][i] = kNegInf;
           if constexpr (CAUSAL) {
             if (cs + 16 * hf + 4 * g4 + i > lim) sv[hf][i] = kNegInf;  // a later token
           }
         }
       }
-    float cm = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
-    cm = xor_max_16_32(cm);
-    const float mn = fmaxf(st.m, cm);
-    const float mu = mn == kNegInf ? 0.f : mn;
-    const float alpha = exp2_hw(st.m - mu);
-    st.m = mn;
+    const float lm = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                           fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    // Lazy rescaling: st.m is a reference, not necessarily the running maximum, and the same
+    // for the four lanes of a column.  l and acc are sums of 2^(s - st.m); the reference
+    // moves up (rescaling them) only when a score exceeds it by more than kRescaleSlack, so
+    // every probability stays below 2^kRescaleSlack.  Usually no lane's own maximum does,
+    // and then neither the column maximum (a cross-lane reduction) nor a rescale is needed.
+    // A reference of -inf (no key seen yet) moves for any finite score.
+    if (__builtin_amdgcn_ballot_w64(lm > st.m + kRescaleSlack)) {
+      const float cm = xor_max_16_32(lm);
+      const bool grow = cm > st.m + kRescaleSlack;
+      const float mn = grow ? cm : st.m;
+      const float alpha = exp2_hw(st.m - (mn == kNegInf ? 0.f : mn));
+      st.l *= alpha;
+#pragma unroll
+      for (int r = 0; r < E; ++r) st.acc[r] *= alpha;
+      st.m = mn;
+    }
+    const float mu = st.m == kNegInf ? 0.f : st.m;
     float p[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) p[j] = exp2_hw(sv[j >> 2][j & 3] - mu);
-    st.l = st.l * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-#pragma unroll
-    for (int r = 0; r < E; ++r) st.acc[r] *= alpha;
+    st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     vec8 phi, plo;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -200,16 +266,8 @@ struct Mfma {
     // O^T += V^T . P^T, one output tile per element position r of the lane's V slices.
 #pragma unroll
     for (int r = 0; r < E; ++r) {
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = ck.vr[(2 * q) >> 2][(2 * q) & 3][r >> 1];
-        const uint32_t hi = ck.vr[(2 * q + 1) >> 2][(2 * q + 1) & 3][r >> 1];
-        w[q] = (r & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-      }
-      const vec8 vop = __builtin_bit_cast(vec8, make_uint4(w[0], w[1], w[2], w[3]));
-      st.acc[r] = mma(vop, phi, st.acc[r]);
-      if constexpr (SPLIT_P) st.acc[r] = mma(vop, plo, st.acc[r]);
+      st.acc[r] = mma(ck.vop[r], phi, st.acc[r]);
+      if constexpr (SPLIT_P) st.acc[r] = mma(ck.vop[r], plo, st.acc[r]);
     }
   }
 

@@ -11,31 +11,47 @@ namespace pkv {
 // =========================================================================================
 // Prefill: one workgroup of 4 waves per (query head, 64 * NT consecutive new tokens,
 // sequence); wave w takes NT tiles of 16 new tokens each as the columns of the MFMA inner
-// loop, so every loaded K/V chunk serves 16 * NT columns.  Sequence b's new tokens are q rows
-// query_start[b] .. query_start[b+1]; with ctx_b tokens cached (the new ones included), new
-// token j sits at position ctx_b - n_b + j and sees keys 0 .. that position.  Neighbouring
-// tiles and the query heads of a group read the same K/V, so K/V goes through the caches.
+// loop.  One tile per wave keeps the accumulators in registers at two waves per SIMD, which
+// measured faster than two tiles per wave at one.  Sequence b's new tokens are q rows query_start[b] .. query_start[b+1]; with ctx_b
+// tokens cached (the new ones included), new token j sits at position ctx_b - n_b + j and
+// sees keys 0 .. that position.
+// The workgroup walks the keys its rows need in 32-token chunks.  Each chunk's K and V rows
+// are gathered through the block table once per workgroup into LDS (rows padded by 16 bytes
+// so that the waves' row reads spread over the banks), double-buffered: the global loads of
+// chunk c+1 are in flight while the waves compute chunk c from LDS.  Neighbouring workgroups
+// and the query heads of a group read the same K/V, so it is read through the caches.
 // =========================================================================================
-constexpr int kPrefillTiles = 2;  // 16-column tiles per wave
+constexpr int kPrefillTiles = 1;  // 16-column tiles per wave
 constexpr int kPrefillRows = 4 * 16 * kPrefillTiles;  // new tokens per workgroup
 
 template <int DT, int D, int BS>
 __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   using M = Mfma<DT, D, BS>;
   constexpr int NT = kPrefillTiles;
+  constexpr int CH = kMfmaChunk;
+  constexpr int PITCH = D * 2 + 16;         // LDS bytes per K or V row
+  constexpr int VECS = D * 2 / 16;          // 16-byte vectors per row
+  constexpr int PER = 2 * CH * VECS / 256;  // vectors each thread moves per chunk
+  static_assert(PER * 256 == 2 * CH * VECS, "chunk must split evenly over the workgroup");
+  __shared__ __attribute__((aligned(16))) char lds[2][2 * CH * PITCH];
+
   const int h = blockIdx.x;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
   const int n16 = lane & 15, g4 = lane >> 4;
   const int r0 = a.query_start[b];
   const int n = a.query_start[b + 1] - r0;
-  const int j0 = blockIdx.y * kPrefillRows + wave * 16 * NT;  // first new token of this wave
-  if (r0 < 0 || n <= 0 || j0 >= n || r0 + j0 >= a.num_tokens) return;
-  const int nq = min(min(16 * NT, n - j0), a.num_tokens - r0 - j0);  // columns with a row
+  const int jw = blockIdx.y * kPrefillRows;  // first new token of the workgroup
+  // Uniform over the workgroup, so returning here skips no barrier another wave waits at.
+  if (r0 < 0 || n <= 0 || jw >= n || r0 + jw >= a.num_tokens) return;
+  const int nw = min(min(kPrefillRows, n - jw), a.num_tokens - r0 - jw);  // rows of the workgroup
   const int ctx = clamp_ctx(a, b);
-  const int first = ctx - n;                 // position of new token 0
-  const int t1 = min(ctx, first + j0 + nq);  // keys 0 .. t1 - 1
+  const int first = ctx - n;                           // position of new token 0
+  const int t1 = max(0, min(ctx, first + jw + nw));    // keys the workgroup needs: 0 .. t1 - 1
+  const int j0 = jw + wave * 16 * NT;                  // first new token of this wave
+  const int nq = max(0, min(16 * NT, jw + nw - j0));   // columns of this wave that have a row
 
   typename M::vec8 qop[NT][M::KK];
   typename M::State st[NT];
@@ -47,31 +63,120 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
     const bool col = 16 * t + n16 < nq;
     lim[t] = col ? first + jt + n16 : -1;
     lim_min[t] = first + jt;
-    lim_max[t] = first + jt + min(16, max(0, nq - 16 * t)) - 1;  // wave-uniform
-    const char* qp = static_cast<const char*>(a.q) + ((size_t(r0 + (col ? jt + n16 : j0)) * a.num_q_heads + h) * D) * 2;
+    // Last key position of the tile's columns; -1 for a tile without columns (wave-uniform).
+    lim_max[t] = nq > 16 * t ? first + jt + min(16, nq - 16 * t) - 1 : -1;
 #pragma unroll
     for (int kk = 0; kk < M::KK; ++kk) {
-      const uint4 w = col ? *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2) : make_uint4(0, 0, 0, 0);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (col) {
+        const char* qp = static_cast<const char*>(a.q) + ((size_t(r0 + jt + n16) * a.num_q_heads + h) * D) * 2;
+        w = *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2);
+      }
       qop[t][kk] = __builtin_bit_cast(typename M::vec8, w);
     }
   }
-  if (t1 > 0) {
-    const int kvh = h / a.group;
-    const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
-    const size_t head_off = size_t(kvh) * BS * D * 2;
-    const char* kb = static_cast<const char*>(a.k_cache) + head_off;
-    const char* vb = static_cast<const char*>(a.v_cache) + head_off;
-    const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
-    const int nchunks = (t1 + kMfmaChunk - 1) / kMfmaChunk;
-    for (int c = 0; c < nchunks; ++c) {
-      const int cs = c * kMfmaChunk;
+  // Let the query loads complete here, before any K/V prefetch is in flight: the chunk loop
+  // then never has to wait for all outstanding loads just to read a query register.
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kk = 0; kk < M::KK; ++kk) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qop[t][kk])));
+
+  const int kvh = h / a.group;
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
+  const size_t head_off = size_t(kvh) * BS * D * 2;
+  const char* kb = static_cast<const char*>(a.k_cache) + head_off;
+  const char* vb = static_cast<const char*>(a.v_cache) + head_off;
+  const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
+  const int nch = (t1 + CH - 1) / CH;
+
+  // Block ids of a chunk's tokens (wave-uniform; -1 past t1), read two chunks ahead so that
+  // no K/V load waits for its table entry.
+  constexpr int NB = CH / BS;  // blocks per chunk (block sizes divide the chunk)
+  static_assert(NB * BS == CH, "block size must divide the chunk");
+  auto load_ids = [&](int cs, int (&ids)[NB]) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int tok = cs + k * BS;
+      ids[k] = uniform(tok < t1 ? tbl[tok / BS] : -1);
+    }
+  };
+  // The id of the block holding token cs + off (0 <= off < CH).
+  auto id_of = [&](const int (&ids)[NB], int off) {
+    int id = ids[0];
+#pragma unroll
+    for (int k = 1; k < NB; ++k)
+      if (off >= k * BS) id = ids[k];
+    return id;
+  };
+
+  // Vector v of a chunk: row v / VECS (rows 0 .. CH-1 are K, CH .. 2CH-1 are V), 16-byte
+  // column v % VECS.  Rows of tokens past t1 or in blocks outside the pool are zero.
+  uint4 pre[PER];
+  auto fetch = [&](int cs, const int (&ids)[NB]) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int v = tid + 256 * k;
+      const int row = v / VECS, col = v % VECS;
+      const int off = row % CH;
+      const int id = cs + off < t1 ? id_of(ids, off) : -1;
+      pre[k] = make_uint4(0, 0, 0, 0);
+      if ((unsigned)id < (unsigned)a.num_blocks)
+        pre[k] = load_cached((row < CH ? kb : vb) + size_t(id) * blk_bytes + size_t(off % BS) * D * 2 + col * 16);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int v = tid + 256 * k;
+      *reinterpret_cast<uint4*>(&lds[buf][(v / VECS) * PITCH + (v % VECS) * 16]) = pre[k];
+    }
+  };
+
+  int ids_cur[NB], ids_next[NB], ids_after[NB];
+  if (nch > 0) {
+    load_ids(0, ids_cur);
+    load_ids(CH, ids_next);
+    fetch(0, ids_cur);
+    stash(0);
+  }
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int cs = c * CH;
+    if (c + 1 < nch) {
+      fetch(cs + CH, ids_next);
+      load_ids(cs + 2 * CH, ids_after);
+    }
+    bool busy = false;  // wave-uniform: some tile of this wave still needs keys from here
+#pragma unroll
+    for (int t = 0; t < NT; ++t) busy |= cs <= lim_max[t];
+    if (busy) {
       typename M::Chunk ck;
-      M::load(a, tbl, kb, vb, blk_bytes, cs, t1, true, lane, ck);
+      // Masking is needed where the chunk runs past t1 or a block id is outside the pool.
+      bool need_mask = cs + CH > t1;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) need_mask |= (unsigned)ids_cur[k] >= (unsigned)a.num_blocks;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int off = 16 * hf + 4 * g4 + i;
+          ck.vok[hf][i] = cs + off < t1 && (unsigned)id_of(ids_cur, off) < (unsigned)a.num_blocks;
+        }
+      ck.need_mask = need_mask;
+      M::load_lds(lds[c & 1], lds[c & 1] + CH * PITCH, PITCH, lane, ck);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         if (cs <= lim_max[t])  // a tile whose columns all precede this chunk skips it
           M::template compute<true>(a, ck, cs, lane, qop[t], st[t], lim[t], lim_min[t]);
     }
+    if (c + 1 < nch) stash((c + 1) & 1);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      ids_cur[k] = ids_next[k];
+      ids_next[k] = ids_after[k];
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
