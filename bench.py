@@ -110,6 +110,8 @@ def parse():
                          "the block-move kernels write and read the pinned host copy themselves")
     ap.add_argument("--swap-every", type=int, default=8,
                     help="--swap: every n-th sequence of the batch is a victim")
+    ap.add_argument("--cascade", action="store_true",
+                    help="time cascade decode against plain decode on a shared-prefix --config")
     ap.add_argument("--prefix-cache", action="store_true",
                     help="measure prompt admission with prefix caching (prompt_stream_llama7b) "
                          "instead of decode")
@@ -541,6 +543,111 @@ def main_swap(args):
     print(json.dumps(res), flush=True)
 
 
+def main_cascade(args):
+    """One step = one decode of the whole batch of a shared-prefix workload (default
+    shared_prefix_bs16: 128 sequences whose first 1024 tokens are one shared set of blocks),
+    done three ways on the same resident cache and tables: cascade decode (the shared
+    prefix read once per group of 16 queries on matrix cores, each sequence's own tokens by
+    the decode kernels, log-sum-exp merge), plain decode with the shared-block hint, and
+    plain decode without it.  All three compute the same outputs (checked within the
+    attention bar of each other).  ``value`` is the logical K/V bytes (each sequence's whole
+    context) per second of the cascade; ``unique`` bytes count the shared blocks once."""
+    import torch
+    import workloads as W
+    import paged_kv_cache_359_amd as pkv
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    name = args.config if args.config != "llama13b" else "shared_prefix_bs16"
+    c = W.get_config(name, steps=1)
+    print(f"[bench] building {c.name}: {c.batch} sequences (cascade)", file=sys.stderr, flush=True)
+    w = W.make_workload(c, device=dev)
+    B, bs = w.batch, c.block_size
+    alloc, k_cache, v_cache = build_resident(w, dev)
+    # The step's appended token, then the tables as the decode sees them.
+    ids = np.arange(B, dtype=np.int64)
+    pos = np.array([alloc.pkv_seq_length(b) for b in range(B)])
+    slots, pairs = alloc.pkv_seq_append(ids)
+    if pairs.size:
+        pkv.pkv_copy_blocks(k_cache, v_cache, torch.from_numpy(pairs).to(dev))
+    idx = torch.from_numpy(w.tok_offsets[:B] + pos - c.prefix_len).to(dev)
+    pkv.pkv_reshape_and_cache(w.k_tok.index_select(0, idx), w.v_tok.index_select(0, idx),
+                              torch.from_numpy(slots).to(dev), k_cache, v_cache)
+    lens_h = np.array([alloc.pkv_seq_length(b) for b in range(B)], dtype=np.int32)
+    max_ctx = int(lens_h.max())
+    t_h, l_h = alloc.pkv_get_block_tables(ids, -(-max_ctx // bs))
+    tables, lens = torch.from_numpy(t_h).to(dev), torch.from_numpy(l_h).to(dev)
+    starts, shared = alloc.pkv_prefix_groups(ids)
+    starts_d, shared_d = torch.from_numpy(starts).to(dev), torch.from_numpy(shared).to(dev)
+    hint = torch.from_numpy(alloc.pkv_shared_prefix_blocks(ids)).to(dev)
+    gsz = int(np.max(np.diff(starts)))
+    q = w.q[0]
+    ws_c = torch.empty(max(16, pkv.pkv_cascade_workspace_bytes(B, c.num_q_heads, c.num_kv_heads,
+                                                               c.head_dim, bs, max_ctx, c.dtype, -1)),
+                       dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(16, pkv.pkv_decode_workspace_bytes(B, c.num_q_heads, c.num_kv_heads,
+                                                              c.head_dim, bs, max_ctx, c.dtype, -1)),
+                       dtype=torch.uint8, device=dev)
+    outs = {k: torch.empty_like(q) for k in ("cascade", "hint", "plain")}
+    runs = {
+        "cascade": lambda: pkv.pkv_paged_attention_cascade(outs["cascade"], q, k_cache, v_cache,
+                                                           tables, lens, starts_d, shared_d, gsz,
+                                                           max_ctx, c.scale, ws_c),
+        "hint": lambda: pkv.pkv_paged_attention_decode(outs["hint"], q, k_cache, v_cache, tables,
+                                                       lens, max_ctx, c.scale, -1, ws_d, hint),
+        "plain": lambda: pkv.pkv_paged_attention_decode(outs["plain"], q, k_cache, v_cache, tables,
+                                                        lens, max_ctx, c.scale, -1, ws_d),
+    }
+    stream = torch.cuda.current_stream(dev)
+    times = {}
+    for key, fn in runs.items():
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+
+        def one(i):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+
+        run_timed(one, 0, args.steps, torch.cuda.synchronize)
+        times[key] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ref = outs["plain"].double()
+    for key in ("cascade", "hint"):
+        dev_ = float((outs[key].double() - ref).abs().max())
+        if not dev_ <= 1e-2:
+            raise SystemExit(f"[bench] {key} differs from plain decode by {dev_}")
+    kvpt = 2 * c.num_kv_heads * c.head_dim * c.dsize
+    logical = kvpt * int(lens_h.sum())
+    # Unique bytes: each group's shared blocks once, plus every row's own tokens.
+    group_prefix = sum(int(shared[starts[g]]) * bs for g in range(len(starts) - 1))
+    unique = kvpt * (int(lens_h.sum()) - int(shared.astype(np.int64).sum()) * bs + group_prefix)
+    gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 3)
+    ms = times["cascade"]
+    res = {
+        "metric": "shared-prefix decode: logical K/V GB/s of cascade decode, 1 GPU",
+        "value": gbs(logical, ms), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
+        "config": workload_desc(c, w.lengths),
+        "groups": len(starts) - 1, "shared_blocks": int(shared.max()),
+        "logical_bytes": logical, "unique_bytes": unique,
+        "cascade_ms": round(ms, 5), "decode_with_hint_ms": round(times["hint"], 5),
+        "decode_plain_ms": round(times["plain"], 5),
+        "speedup_vs_hint": round(times["hint"] / ms, 3),
+        "speedup_vs_plain": round(times["plain"] / ms, 3),
+        "unique_GBs": gbs(unique, ms),
+        "roofline": {"bound": "hbm", "achieved": gbs(unique, ms), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(unique / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                     "traffic": None,
+                     "kernel": "paged_attention_cascade (prefix pass + decode + merge), unique bytes",
+                     "bytes_per_launch": unique},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main_prefix_cache(args):
     """One step = admitting the whole request stream (256 LLaMA-7B-shaped requests over 4
     system prompts, at most 64 running) as a serving loop would, in batches of 16 arrivals:
@@ -814,6 +921,8 @@ def main():
         return main_swap(args)
     if args.prefix_cache:
         return main_prefix_cache(args)
+    if args.cascade:
+        return main_cascade(args)
 
     import torch
     import workloads as W

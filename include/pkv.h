@@ -175,6 +175,20 @@ pkv_status pkv_get_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int3
 pkv_status pkv_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
                                     int32_t* out);
 
+/* Groups for pkv_paged_attention_cascade (cascade attention: "LLM Systems 24: Efficient LLM
+ * Inference with PagedAttention and vLLM", §2.2.1.3, names it among the kernels a runtime
+ * picks per batch).  For the batch rows seq_ids[0..n) (host): a group is a maximal run of
+ * at least two consecutive rows whose block tables start with the same physical block; it
+ * shares the longest run of leading table entries all its members agree on, cut to the
+ * full blocks every member's length covers.  Rows in no group (or whose group would share
+ * nothing) stand alone with 0 shared blocks.  Writes group_start_out (host, n + 1 int32:
+ * group g is rows group_start[g] .. group_start[g+1] - 1), shared_blocks_out (host, n
+ * int32, per row) and *n_groups_out.  Order the batch so that sharers are adjacent.
+ * UNKNOWN_SEQ if an id is missing (outputs untouched). */
+pkv_status pkv_prefix_groups(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
+                             int32_t* group_start_out, int32_t* shared_blocks_out,
+                             int32_t* n_groups_out);
+
 /* Length (tokens) of one sequence. */
 pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out);
 
@@ -303,6 +317,41 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
                                       int32_t max_blocks_per_seq, int32_t max_context_len,
                                       float scale, pkv_dtype dtype, int32_t partition_size,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Cascade decode: the same result as pkv_paged_attention_decode (plain attention of each
+ * sequence's query over its whole context, up to fp32 rounding order), computed with the
+ * shared prefix of each group of sequences read once per group.  Cascade attention is named
+ * among the kernels a runtime picks per batch ("LLM Systems 24: Efficient LLM Inference
+ * with PagedAttention and vLLM", §2.2.1.3); requests sharing a system prompt share its
+ * blocks ("PagedAttention 与 vLLM 推理加速", §3.2 (3)).  Three launches on `stream`:
+ *   1. per (KV head, group, 16 columns): the group's members' queries (every query head of
+ *      the KV head) attend to the shared blocks, read once, on matrix cores;
+ *   2. per sequence: the decode kernels attend to the rest of its context;
+ *   3. the two parts are merged by their log-sum-exp.
+ * group_start (device, num_groups + 1 int32) and shared_blocks (device, num_seqs int32)
+ * are pkv_prefix_groups's output for the batch rows in order (any grouping with the same
+ * guarantees works: the rows of group g are group_start[g] .. group_start[g+1] - 1, all
+ * share their first shared_blocks[row] table entries (the same count for the group), and
+ * those blocks lie within every member's context; shared_blocks[row] = 0 for a row alone).
+ * max_group_size: an upper bound of the group sizes (sizes the launch).
+ * workspace: at least pkv_cascade_workspace_bytes(...) bytes, 16-byte aligned.
+ * Other arguments as for pkv_paged_attention_decode (no cache hint: the prefix pass reads
+ * shared blocks through the caches, the per-sequence pass streams the rest).
+ * Supported: fp16 and bf16, head_dim 64 or 128, block_size 8, 16 or 32; otherwise
+ * PKV_ERR_UNSUPPORTED (use pkv_paged_attention_decode). */
+size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                   pkv_dtype dtype, int32_t partition_size);
+pkv_status pkv_paged_attention_cascade(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, const int32_t* group_start,
+                                       const int32_t* shared_blocks, int32_t num_groups,
+                                       int32_t max_group_size, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       float scale, pkv_dtype dtype, int32_t partition_size,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Paged causal prefill attention (a prompt, or one chunk of it, for several sequences at
  * once).  Each new token attends to every earlier token of its sequence and to itself

@@ -293,6 +293,41 @@ class OracleAllocator:
         return list(self.tables[seq])
 
     # -- queries -----------------------------------------------------------------------
+    def prefix_groups(self, seqs):
+        """Groups for a decode that reads a shared prefix once per group (cascade attention,
+        "LLM Systems 24", §2.2.1.3 names it among runtime-chosen kernels).  A group is a
+        maximal run of at least two consecutive rows of ``seqs`` whose tables start with the
+        same physical block; it shares the longest common run of leading table entries, cut
+        to the full blocks every member's length covers.  Rows in no group (or whose group
+        would share nothing) stand alone with 0 shared blocks.
+        Returns (group_start [G + 1], shared [n]): rows group_start[g] .. group_start[g+1]-1
+        form group g and each shares shared[row] leading blocks."""
+        seqs = list(seqs)
+        for s in seqs:
+            if s not in self.tables:
+                raise UnknownSeq(s)
+        n, bs = len(seqs), self.block_size
+        starts, shared = [0], [0] * n
+        i = 0
+        while i < n:
+            first = self.tables[seqs[i]][:1]
+            j = i + 1
+            while j < n and first and self.tables[seqs[j]][:1] == first:
+                j += 1
+            members = [self.tables[seqs[r]] for r in range(i, j)]
+            common = 0
+            while (j - i >= 2 and all(common < len(t) for t in members)
+                   and len({t[common] for t in members}) == 1):
+                common += 1
+            k = min([common] + [self.lens[seqs[r]] // bs for r in range(i, j)])
+            if j - i >= 2 and k > 0:
+                shared[i:j] = [k] * (j - i)
+                starts.append(j)
+            else:
+                starts.extend(range(i + 1, j + 1))
+            i = j
+        return starts, shared
+
     def block_tables(self, seqs, max_blocks: int):
         """Row-per-sequence tables padded with -1, and the sequence lengths."""
         rows, lens = [], []

@@ -169,6 +169,18 @@ class PkvAlloc:
         _check(self._lib.pkv_seq_length(self._h, int(seq_id), ctypes.byref(out)), "pkv_seq_length")
         return out.value
 
+    def pkv_prefix_groups(self, seq_ids):
+        """(group_start int32 [G + 1], shared_blocks int32 [n]) for cascade decode."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64).reshape(-1)
+        n = ids.size
+        starts = np.empty(n + 1, dtype=np.int32)
+        shared = np.empty(max(n, 1), dtype=np.int32)
+        ng = ctypes.c_int32(0)
+        _check(self._lib.pkv_prefix_groups(self._h, _ptr(ids, ctypes.c_int64) if n else None, n,
+                                           _ptr(starts, ctypes.c_int32), _ptr(shared, ctypes.c_int32),
+                                           ctypes.byref(ng)), "pkv_prefix_groups")
+        return starts[: ng.value + 1], shared[:n]
+
     def pkv_num_free_blocks(self) -> int:
         return int(self._lib.pkv_num_free_blocks(self._h))
 
@@ -365,6 +377,48 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
         cached_ptr, nb, hq, hkv, d, bs, n, block_tables.shape[1], int(max_context_len),
         float(scale), _dtype_code(k_cache), int(partition_size), ws_ptr, ws_bytes, _stream(q)),
         "pkv_paged_attention_decode")
+    return out
+
+
+def pkv_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_context_len, dtype, partition_size=-1) -> int:
+    """dtype: "f32" | "f16" | "bf16" or a torch dtype."""
+    code = DTYPE_CODES[dtype] if isinstance(dtype, str) else _dtype_code_of(dtype)
+    return int(_lib.load().pkv_cascade_workspace_bytes(int(num_seqs), int(num_q_heads),
+                                                       int(num_kv_heads), int(head_dim),
+                                                       int(block_size), int(max_context_len),
+                                                       code, int(partition_size)))
+
+
+def pkv_paged_attention_cascade(out, q, k_cache, v_cache, block_tables, context_lens, group_start,
+                                shared_blocks, max_group_size: int, max_context_len: int,
+                                scale: float, workspace, partition_size: int = -1):
+    """As pkv_paged_attention_decode; group_start [G + 1] and shared_blocks [B] are int32
+    device tensors (pkv_prefix_groups's output); workspace: a uint8 device tensor of at least
+    pkv_cascade_workspace_bytes(...) bytes."""
+    import torch
+    nb, hq, d = q.shape
+    n, hkv, bs, d2 = k_cache.shape
+    if d2 != d or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == out.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    for x in (block_tables, context_lens, group_start, shared_blocks):
+        if x.dtype != torch.int32:
+            raise TypeError("tables, lengths, group_start and shared_blocks must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != nb or context_lens.shape != (nb,):
+        raise ValueError("table shape")
+    if shared_blocks.shape != (nb,) or group_start.dim() != 1 or group_start.numel() < 1:
+        raise ValueError("group_start [G + 1] and shared_blocks [num_seqs]")
+    if nb == 0:
+        return out
+    ng = group_start.numel() - 1
+    _check(_lib.load().pkv_paged_attention_cascade(
+        _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
+        _dev(group_start), _dev(shared_blocks), ng, int(max_group_size), nb, hq, hkv, d, bs, n,
+        block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(k_cache),
+        int(partition_size), _dev(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q)), "pkv_paged_attention_cascade")
     return out
 
 

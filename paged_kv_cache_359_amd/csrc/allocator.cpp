@@ -433,6 +433,50 @@ pkv_status pkv_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq_ids, 
   return PKV_OK;
 }
 
+pkv_status pkv_prefix_groups(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
+                             int32_t* group_start_out, int32_t* shared_blocks_out,
+                             int32_t* n_groups_out) {
+  if (!a || n < 0 || !group_start_out || !n_groups_out) return PKV_ERR_INVALID_ARG;
+  if (n > 0 && (!seq_ids || !shared_blocks_out)) return PKV_ERR_INVALID_ARG;
+  std::vector<const Sequence*> rows(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    rows[i] = &it->second;
+  }
+  int32_t g = 0;
+  group_start_out[0] = 0;
+  for (int32_t i = 0; i < n;) {
+    // The run of rows whose tables start with row i's first block.
+    int32_t j = i + 1;
+    if (!rows[i]->table.empty())
+      while (j < n && !rows[j]->table.empty() && rows[j]->table[0] == rows[i]->table[0]) ++j;
+    // Leading entries all members agree on, cut to the full blocks every member's length covers.
+    int64_t k = 0;
+    if (j - i >= 2) {
+      k = int64_t(rows[i]->table.size());
+      for (int32_t r = i; r < j; ++r) {
+        const auto& t = rows[r]->table;
+        int64_t c = 0;
+        while (c < k && c < int64_t(t.size()) && t[c] == rows[i]->table[c]) ++c;
+        k = std::min<int64_t>({k, c, rows[r]->len / a->block_size});
+      }
+    }
+    if (k > 0) {
+      for (int32_t r = i; r < j; ++r) shared_blocks_out[r] = int32_t(k);
+      group_start_out[++g] = j;
+    } else {
+      for (int32_t r = i; r < j; ++r) {
+        shared_blocks_out[r] = 0;
+        group_start_out[++g] = r + 1;
+      }
+    }
+    i = j;
+  }
+  *n_groups_out = g;
+  return PKV_OK;
+}
+
 pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out) {
   if (!a || !len_out) return PKV_ERR_INVALID_ARG;
   auto it = a->seqs.find(seq_id);

@@ -153,11 +153,13 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
   const int h = blockIdx.x;
   const int part = blockIdx.y;
   const int b = blockIdx.z;
-  const int ctx = clamp_ctx(a, b);
+  const int ctx_all = clamp_ctx(a, b);
+  const int sk = skipped_blocks(a, b, ctx_all, BS);
+  const int ctx = ctx_all - sk * BS;  // attended here: tokens sk * BS .. ctx_all - 1
   const int tid = threadIdx.x;
   const size_t out_row = (size_t(b) * a.num_q_heads + h) * D;
   if (ctx == 0) {
-    if (part == 0)
+    if (part == 0 && !a.partials_only)
       for (int d = tid; d < D; d += NW * 64) store_elt<DT>(a.out, out_row + d, 0.f);
     return;
   }
@@ -171,14 +173,14 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
   const int row = lane / V::LPT;
   const int col = lane % V::LPT;
   const int kvh = h / a.group;
-  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks + sk;
   const size_t lane_off = (size_t(kvh) * BS * D + size_t(col) * V::VEC) * V::ES;
   const char* kb = static_cast<const char*>(a.k_cache) + lane_off;
   const char* vb = static_cast<const char*>(a.v_cache) + lane_off;
   const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * V::ES;
   const uint4 qv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
                                                     (out_row + size_t(col) * V::VEC) * V::ES);
-  const int ncached = cached_blocks(a, b);
+  const int ncached = cached_blocks(a, b) - sk;
   typename V::State st;
   V::init(st);
   const int nchunks = (t1 - t0 + V::CT - 1) / V::CT;
@@ -210,10 +212,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
         O += s_o[r][d] * w;
       }
     }
-    if (nparts == 1) {
+    if (nparts == 1 && !a.partials_only) {
       store_elt<DT>(a.out, out_row + d, L > 0.f ? O / L : 0.f);
     } else {
-      const size_t pi = (size_t(b) * a.num_q_heads + h) * a.max_parts + part;
+      const size_t pi = (size_t(b) * a.num_q_heads + h) * a.max_parts + a.part_base + part;
       a.part_o[pi * D + d] = O;
       if (d == 0) {
         a.part_m[pi] = M;
@@ -239,11 +241,13 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   const int b = blockIdx.z;
   const int h0 = kvh * a.group + hg * 16;             // first query head of this workgroup
   const int nh = min(16, a.group - hg * 16);          // query heads in this workgroup
-  const int ctx = clamp_ctx(a, b);
+  const int ctx_all = clamp_ctx(a, b);
+  const int sk = skipped_blocks(a, b, ctx_all, BS);
+  const int ctx = ctx_all - sk * BS;  // attended here: tokens sk * BS .. ctx_all - 1
   const int tid = threadIdx.x;
   const size_t q_row0 = size_t(b) * a.num_q_heads + h0;
   if (ctx == 0) {
-    if (part == 0)
+    if (part == 0 && !a.partials_only)
       for (int i = tid; i < nh * D; i += NW * 64) store_elt<DT>(a.out, q_row0 * D + i, 0.f);
     return;
   }
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int n16 = lane & 15, g4 = lane >> 4;
-  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks + sk;
   const size_t head_off = size_t(kvh) * BS * D * 2;
   const char* kb = static_cast<const char*>(a.k_cache) + head_off;
   const char* vb = static_cast<const char*>(a.v_cache) + head_off;
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
   typename M::vec8 qop[M::KK];
   M::load_q(a, q_row0, nh, lane, qop);
-  const int ncached = cached_blocks(a, b);
+  const int ncached = cached_blocks(a, b) - sk;
   typename M::State st;
   M::init(st);
   const int nchunks = (t1 - t0 + kMfmaChunk - 1) / kMfmaChunk;
@@ -299,10 +303,10 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
         O += mo[(w * 16 + hh) * D + d] * sc;
       }
     }
-    if (nparts == 1) {
+    if (nparts == 1 && !a.partials_only) {
       store_elt<DT>(a.out, (q_row0 + hh) * D + d, L > 0.f ? O / L : 0.f);
     } else {
-      const size_t pi = ((size_t(b) * a.num_q_heads + h0 + hh) * a.max_parts + part);
+      const size_t pi = ((size_t(b) * a.num_q_heads + h0 + hh) * a.max_parts + a.part_base + part);
       a.part_o[pi * D + d] = O;
       if (d == 0) {
         a.part_m[pi] = Mx;
@@ -320,22 +324,117 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 template <int DT, int D>
 __global__ __launch_bounds__(128) void reduce_partitions(DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
-  const int ctx = clamp_ctx(a, b);
-  const int nparts = (ctx + a.part_size - 1) / a.part_size;
-  if (nparts <= 1) return;
+  const int ctx_all = clamp_ctx(a, b);
+  const int sk = skipped_blocks(a, b, ctx_all, a.block_size);
+  const int ctx = ctx_all - sk * a.block_size;
+  // Slots part_base .. part_base + nparts - 1 hold this call's partitions; in a cascade,
+  // slot 0 holds the shared prefix's partial when the sequence has one.
+  const int p0 = sk > 0 ? 0 : a.part_base;
+  const int p1 = a.part_base + (ctx + a.part_size - 1) / a.part_size;
+  if (!a.partials_only && p1 - p0 <= 1) return;  // a single partition wrote the output itself
   const size_t base = (size_t(b) * a.num_q_heads + h) * a.max_parts;
   float M = kNegInf;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.part_m[base + p]);
+  for (int p = p0; p < p1; ++p) M = fmaxf(M, a.part_m[base + p]);
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float L = 0.f, O = 0.f;
     if (M != kNegInf) {
-      for (int p = 0; p < nparts; ++p) {
+      for (int p = p0; p < p1; ++p) {
         const float w = exp2_hw(a.part_m[base + p] - M);
         L += a.part_l[base + p] * w;
         O += a.part_o[(base + p) * D + d] * w;
       }
     }
     store_elt<DT>(a.out, (size_t(b) * a.num_q_heads + h) * D + d, L > 0.f ? O / L : 0.f);
+  }
+}
+
+// =========================================================================================
+// Cascade decode, shared-prefix pass: one workgroup of 4 waves per (KV head, tile of 16
+// columns, group).  The columns are the group's (member row, query head of this KV head)
+// pairs, so the group's shared prefix blocks are read once per tile for up to 16 queries
+// instead of once per sequence; the tile's chunks are dealt to the waves in turn and merged
+// through LDS, and the result goes to partial slot 0 of each column's (row, head).
+// =========================================================================================
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(256) void cascade_prefix(DecodeArgs a) {
+  using M = Mfma<DT, D, BS>;
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) float smem[NW * 16 * (D + 2)];
+
+  const int kvh = blockIdx.x;
+  const int g = blockIdx.z;
+  const int m0 = min(max(a.group_start[g], 0), a.num_seqs);       // first row of the group
+  const int m1 = min(max(a.group_start[g + 1], m0), a.num_seqs);  // one past its last row
+  const int cols = (m1 - m0) * a.group;
+  const int c0 = blockIdx.y * 16;
+  if (m1 - m0 < 1 || c0 >= cols) return;
+  const int sk = skipped_blocks(a, m0, clamp_ctx(a, m0), BS);  // shared blocks of the group
+  if (sk == 0) return;
+  const int nc = min(16, cols - c0);
+  const int t1 = sk * BS;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int n16 = lane & 15, g4 = lane >> 4;
+
+  // Q^T operand: column n16 is (row m0 + c / group, head kvh * group + c % group), c = c0 + n16.
+  typename M::vec8 qop[M::KK];
+  {
+    const int c = c0 + (n16 < nc ? n16 : 0);
+    const size_t qrow = size_t(m0 + c / a.group) * a.num_q_heads + kvh * a.group + c % a.group;
+    const char* qp = static_cast<const char*>(a.q) + qrow * D * 2;
+#pragma unroll
+    for (int kk = 0; kk < M::KK; ++kk) {
+      const uint4 w = n16 < nc ? *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2)
+                               : make_uint4(0, 0, 0, 0);
+      qop[kk] = __builtin_bit_cast(typename M::vec8, w);
+    }
+  }
+  const int32_t* tbl = a.tables + size_t(m0) * a.max_blocks;  // every member's first sk entries
+  const size_t head_off = size_t(kvh) * BS * D * 2;
+  const char* kb = static_cast<const char*>(a.k_cache) + head_off;
+  const char* vb = static_cast<const char*>(a.v_cache) + head_off;
+  const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
+  typename M::State st;
+  M::init(st);
+  const int nchunks = (t1 + kMfmaChunk - 1) / kMfmaChunk;
+  for (int c = wave; c < nchunks; c += NW)  // the prefix is re-read by every tile: cached loads
+    M::chunk(a, tbl, kb, vb, blk_bytes, c * kMfmaChunk, t1, true, lane, qop, st);
+  st.l = xor_sum_16_32(st.l);
+
+  float* mo = smem;              // [NW][16][D]
+  float* mm = mo + NW * 16 * D;  // [NW][16]
+  float* ml = mm + NW * 16;      // [NW][16]
+#pragma unroll
+  for (int r = 0; r < M::E; ++r)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) mo[(wave * 16 + n16) * D + M::out_d(g4, v, r)] = st.acc[r][v];
+  if (g4 == 0) {
+    mm[wave * 16 + n16] = st.m;
+    ml[wave * 16 + n16] = st.l;
+  }
+  __syncthreads();
+  for (int i = tid; i < nc * D; i += NW * 64) {
+    const int cc = i / D, d = i % D;
+    float Mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, mm[w * 16 + cc]);
+    float L = 0.f, O = 0.f;
+    if (Mx != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float sc = exp2_hw(mm[w * 16 + cc] - Mx);
+        L += ml[w * 16 + cc] * sc;
+        O += mo[(w * 16 + cc) * D + d] * sc;
+      }
+    }
+    const int c = c0 + cc;
+    const size_t pi = (size_t(m0 + c / a.group) * a.num_q_heads + kvh * a.group + c % a.group) * a.max_parts;
+    a.part_o[pi * D + d] = O;
+    if (d == 0) {
+      a.part_m[pi] = Mx;
+      a.part_l[pi] = L;
+    }
   }
 }
 
@@ -439,6 +538,30 @@ kernel_fn pick_reduce(pkv_dtype dt, int d) {
          : dt == PKV_F16 ? pick_reduce<DT_F16>(d) : pick_reduce<DT_BF16>(d);
 }
 
+template <int DT, int D>
+kernel_fn pick_cascade_bs(int bs) {
+  switch (bs) {
+    case 8: return cascade_prefix<DT, D, 8>;
+    case 16: return cascade_prefix<DT, D, 16>;
+    case 32: return cascade_prefix<DT, D, 32>;
+  }
+  return nullptr;
+}
+
+kernel_fn pick_cascade(pkv_dtype dt, int d, int bs) {
+  if (dt == PKV_F32) return nullptr;
+  if (d == 64) return dt == PKV_F16 ? pick_cascade_bs<DT_F16, 64>(bs) : pick_cascade_bs<DT_BF16, 64>(bs);
+  if (d == 128) return dt == PKV_F16 ? pick_cascade_bs<DT_F16, 128>(bs) : pick_cascade_bs<DT_BF16, 128>(bs);
+  return nullptr;
+}
+
+// Partitions of the per-sequence (suffix) pass of a cascade decode, plus slot 0 for the
+// shared prefix.
+int64_t cascade_slots(int32_t partition_size, int32_t max_context_len, int64_t rows) {
+  const int p = resolve_partition(partition_size, max_context_len, rows);
+  return 1 + (int64_t(max_context_len) + p - 1) / p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -513,6 +636,8 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
   a.part_size = part;
   a.max_parts = max_parts;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.block_size = block_size;
   if (max_parts > 1) {
     const size_t need =
         size_t(num_seqs) * num_q_heads * max_parts * (size_t(head_dim) + 2) * sizeof(float);
@@ -535,6 +660,102 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
     return launch_status("reduce_partitions");
   }
   return PKV_OK;
+}
+
+size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                   pkv_dtype dtype, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads != 0 ||
+      !valid_dtype(dtype) || partition_size < -1)
+    return 0;
+  const int64_t rows = rows_per_seq(dtype, num_q_heads, num_kv_heads, head_dim, block_size);
+  const int64_t slots = cascade_slots(partition_size, max_context_len > 0 ? max_context_len : 1,
+                                      int64_t(num_seqs) * rows);
+  return size_t(num_seqs) * num_q_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
+}
+
+pkv_status pkv_paged_attention_cascade(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, const int32_t* group_start,
+                                       const int32_t* shared_blocks, int32_t num_groups,
+                                       int32_t max_group_size, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       float scale, pkv_dtype dtype, int32_t partition_size,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0 || num_groups < 0 || max_group_size < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return PKV_ERR_INVALID_ARG;
+  if (partition_size < -1) return PKV_ERR_INVALID_ARG;
+  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+    return PKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
+  kernel_fn pk = pick_cascade(dtype, head_dim, block_size);
+  if (!pk) return PKV_ERR_UNSUPPORTED;  // the shared-prefix pass runs on matrix cores
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !shared_blocks ||
+      (num_groups > 0 && !group_start))
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t cap = int64_t(max_blocks_per_seq) * block_size;
+  const int group = num_q_heads / num_kv_heads;
+  const bool mfma = use_mfma(dtype, head_dim, block_size, group);
+  const int64_t rows = rows_per_seq(dtype, num_q_heads, num_kv_heads, head_dim, block_size);
+  const int mc = max_context_len > 0 ? max_context_len : 1;
+  const int part = resolve_partition(partition_size, mc, int64_t(num_seqs) * rows);
+  const int64_t slots = cascade_slots(partition_size, mc, int64_t(num_seqs) * rows);
+  const int64_t tiles = (int64_t(max_group_size) * group + 15) / 16;
+  if (slots > 65535 || num_seqs > 65535 || num_groups > 65535 || tiles > 65535)
+    return PKV_ERR_UNSUPPORTED;
+  const size_t need = size_t(num_seqs) * num_q_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
+
+  DecodeArgs a = {};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.ctx_limit = int32_t(max_context_len < cap ? max_context_len : cap);
+  a.part_size = part;
+  a.max_parts = int(slots);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.skip = shared_blocks;
+  a.group_start = group_start;
+  a.num_seqs = num_seqs;
+  a.block_size = block_size;
+  a.part_base = 1;
+  a.partials_only = 1;
+  float* w = static_cast<float*>(workspace);
+  a.part_o = w;
+  a.part_m = w + size_t(num_seqs) * num_q_heads * slots * head_dim;
+  a.part_l = a.part_m + size_t(num_seqs) * num_q_heads * slots;
+  kernel_fn k = pick_decode(dtype, head_dim, block_size, mfma);
+  kernel_fn r = pick_reduce(dtype, head_dim);
+  if (!k || !r) return PKV_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  clear_stale_error();
+  if (num_groups > 0 && tiles > 0) {
+    hipLaunchKernelGGL(pk, dim3(unsigned(num_kv_heads), unsigned(tiles), unsigned(num_groups)),
+                       dim3(256), 0, st, a);
+    if (launch_status("cascade_prefix") != PKV_OK) return PKV_ERR_HIP;
+  }
+  hipLaunchKernelGGL(k, dim3(unsigned(rows), unsigned(slots - 1), unsigned(num_seqs)),
+                     dim3(mfma ? 256 : 64 * kValuWaves), 0, st, a);
+  if (launch_status("paged_attention_decode") != PKV_OK) return PKV_ERR_HIP;
+  hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(128), 0, st, a);
+  return launch_status("reduce_partitions");
 }
 
 }  // extern "C"

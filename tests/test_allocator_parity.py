@@ -91,6 +91,10 @@ def same_state(o, c):
                 k += 1
             shared.append(k)
         assert c.pkv_shared_prefix_blocks(seqs).tolist() == shared
+        # Cascade groups, rows ordered so that sharers are adjacent.
+        rows = sorted(seqs, key=lambda s: (o.tables[s][:1], s))
+        gs, sb = c.pkv_prefix_groups(rows)
+        assert (gs.tolist(), sb.tolist()) == tuple(o.prefix_groups(rows))
     assert c.pkv_usage() == o.usage()
 
 

@@ -189,3 +189,77 @@ def test_random_request_streams_read_back_their_own_tokens(ops, bs, nblocks, see
             assert got == toks[s], (kind, s)
         used = sum(1 for r in a.ref if r > 0)
         assert used + a.num_free() == nblocks
+
+
+# -- cascade groups -------------------------------------------------------------------------
+def test_prefix_groups_page_example(golden_dir):
+    # The pages' three requests forked from one six-block prompt form one group sharing it.
+    with open(os.path.join(golden_dir, "prefix_sharing.json")) as f:
+        g = json.load(f)
+    bs = g["block_size"]
+    a = oracle.OracleAllocator(g["num_blocks"], bs, g["free_order"])
+    a.add("p", g["prompt_tokens"])
+    for r in range(3):
+        a.fork("p", r)
+    a.free_seq("p")
+    for r, n in enumerate(g["suffix_tokens"]):
+        for _ in range(n):
+            a.append([r])
+    assert a.prefix_groups([0, 1, 2]) == ([0, 3], [6, 6, 6])
+    # Reordered rows form the same group; a single row shares nothing with itself.
+    assert a.prefix_groups([2, 0]) == ([0, 2], [6, 6])
+    assert a.prefix_groups([1]) == ([0, 1], [0])
+
+
+def test_prefix_groups_worked_example():
+    a = oracle.OracleAllocator(32, 4)
+    a.add("x", 8)          # blocks 0, 1
+    a.fork("x", "x2")
+    a.add("solo", 3)       # block 2
+    a.add("y", 10)         # blocks 3, 4, 5 (last one partial)
+    a.fork("y", "y2")
+    a.fork("y", "y3")
+    a.append(["y2"])       # y2 copies block 5 on write: y, y3 still share it
+    a.add("short", 0)
+    # Rows: x, x2 | solo | y, y2, y3 | short | x  (x again, not next to x2)
+    starts, shared = a.prefix_groups(["x", "x2", "solo", "y", "y2", "y3", "short", "x"])
+    assert starts == [0, 2, 3, 6, 7, 8]
+    # x/x2 share both blocks (8 tokens = 2 full blocks).  y, y2, y3 share blocks 3 and 4
+    # (block 5 differs for y2), and 10 // 4 = 2 full blocks anyway.
+    assert shared == [2, 2, 0, 2, 2, 2, 0, 0]
+    a.fork("y", "y4")  # y and y4 share block 5 too, but it is not full: cut to 2
+    assert a.prefix_groups(["y", "y4"]) == ([0, 2], [2, 2])
+
+
+@settings(max_examples=200, deadline=None)
+@given(ops=st.lists(st.tuples(st.sampled_from(["add", "fork", "fork", "append", "free"]),
+                              st.integers(0, 5), st.integers(0, 5), st.integers(0, 12)),
+                    min_size=1, max_size=40),
+       bs=st.sampled_from([1, 2, 4]), seed=st.integers(0, 100))
+def test_prefix_groups_properties(ops, bs, seed):
+    a = oracle.OracleAllocator(64, bs, np.random.default_rng(seed).permutation(64))
+    for kind, x, y, n in ops:
+        try:
+            {"add": lambda: a.add(x, n), "fork": lambda: a.fork(x, y),
+             "append": lambda: a.append([x]), "free": lambda: a.free_seq(x)}[kind]()
+        except oracle.OracleError:
+            pass
+    rows = sorted(a.tables, key=lambda s: (a.tables[s][:1], s))
+    starts, shared = a.prefix_groups(rows)
+    assert starts[0] == 0 and starts[-1] == len(rows) and starts == sorted(set(starts))
+    for g0, g1 in zip(starts, starts[1:]):
+        tabs = [a.tables[rows[r]] for r in range(g0, g1)]
+        k = shared[g0]
+        assert all(shared[r] == k for r in range(g0, g1))
+        if g1 - g0 == 1:
+            assert k == 0
+            continue
+        assert k > 0 and all(t[:k] == tabs[0][:k] for t in tabs)  # the same physical blocks
+        assert all(a.lens[rows[r]] >= k * bs for r in range(g0, g1))  # full for every member
+        longer = all(len(t) > k for t in tabs) and len({t[k] for t in tabs}) == 1
+        assert not longer or any(a.lens[rows[r]] < (k + 1) * bs for r in range(g0, g1))
+    for r in range(len(rows) - 1):  # runs are maximal
+        if r + 1 not in starts[1:-1]:
+            continue
+        t0, t1 = a.tables[rows[r]][:1], a.tables[rows[r + 1]][:1]
+        assert not t0 or t0 != t1 or shared[r] == 0 or shared[r + 1] == 0
