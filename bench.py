@@ -118,6 +118,11 @@ def parse():
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries of --config from rocprofv3 output in DIR "
                          "(kt_<config>/, pmc_fetch_<config>/, pmc_write_<config>/, kt_<config>.log)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TAG", "DIR"),
+                    help="write profiles/<TAG>_kernel_trace.txt from DIR/kt_<TAG>/ and "
+                         "DIR/kt_<TAG>.log (a kernel trace of bench.py run with --trace-args)")
+    ap.add_argument("--trace-args", default="",
+                    help="with --summarize-trace: the bench.py arguments the traced run used")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (scales HBM counters)")
     return ap.parse_args()
@@ -812,6 +817,29 @@ def main_prefix_cache(args):
     print(json.dumps(res), flush=True)
 
 
+def summarize_trace(tag, outdir, bench_args):
+    """A short kernel-trace summary of any bench.py mode: the commands, the bench line of the
+    traced run and the per-kernel statistics."""
+    import csv
+    rel = os.path.relpath(outdir, ROOT)
+    stats = list(csv.DictReader(open(os.path.join(outdir, f"kt_{tag}", f"{tag}_kernel_stats.csv"))))
+    line = [l for l in open(os.path.join(outdir, f"kt_{tag}.log")) if l.startswith("{")][-1].strip()
+    short = lambda n: (n.replace("void ", "").split("(")[0] if "pkv::" in n else n)[:70]
+    L = [f"Kernel trace of `bench.py {bench_args}` on one MI355X (gfx950).", "",
+         "Command (repository root on the GPU box), then the summary:",
+         f"  rocprofv3 --kernel-trace --stats -f csv -d {rel}/kt_{tag} -o {tag} -- python3 bench.py "
+         f"{bench_args} > {rel}/kt_{tag}.log",
+         f"  python3 bench.py --summarize-trace {tag} {rel} --trace-args \"{bench_args}\"", "",
+         "bench.py line of the traced run:", "  " + line, "",
+         "Kernel statistics (all dispatches of the run, including set-up; ns):",
+         f"  {'kernel':72s} {'calls':>6s} {'avg':>11s} {'min':>9s} {'max':>9s} {'share%':>7s}"]
+    for r in stats:
+        L.append(f"  {short(r['Name']):72s} {r['Calls']:>6s} {float(r['AverageNs']):11.1f} "
+                 f"{r['MinNs']:>9s} {r['MaxNs']:>9s} {float(r['Percentage']):7.2f}")
+    open(os.path.join(ROOT, "profiles", f"{tag}_kernel_trace.txt"), "w").write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
 def summarize(config, outdir):
     """Writes profiles/paged_decode_<config>_kernel_trace.txt and _hbm_traffic.txt from the
     rocprofv3 output of the three runs named in those files (one kernel trace, one
@@ -917,6 +945,8 @@ def main():
 
     if args.summarize:
         return summarize(args.config, args.summarize)
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.trace_args)
     if args.swap:
         return main_swap(args)
     if args.prefix_cache:

@@ -263,3 +263,47 @@ def test_add_tokens_validation_and_accounting():
     a.pkv_seq_add(3, 12)  # all six blocks: both cached ones are evicted
     assert a.pkv_num_cached_blocks() == 0 and a.pkv_num_free_blocks() == 0
     assert l.pkv_num_cached_blocks(None) == -1
+
+
+def cascade(**kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, lens=FAKE, gs=FAKE, shared=FAKE,
+                ng=1, gmax=2, nseq=2, hq=4, hkv=4, d=128, bs=16, nblocks=100, maxb=8, maxctx=128,
+                scale=0.1, dtype=1, part=-1, ws=None, wsb=0, stream=None)
+    args.update(kw)
+    a = args
+    return lib().pkv_paged_attention_cascade(a["out"], a["q"], a["k"], a["v"], a["tables"],
+                                             a["lens"], a["gs"], a["shared"], a["ng"], a["gmax"],
+                                             a["nseq"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                             a["nblocks"], a["maxb"], a["maxctx"], a["scale"],
+                                             a["dtype"], a["part"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), 5),                # fp32: the shared-prefix pass runs on matrix cores
+    (dict(d=8), 5),
+    (dict(bs=4), 5),
+    (dict(hq=6, hkv=4), 1),
+    (dict(dtype=7), 1),
+    (dict(part=24), 1),
+    (dict(ng=-1), 1),
+    (dict(gmax=-1), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(shared=None), 1),
+    (dict(gs=None), 1),                # groups given but no group_start
+    (dict(q=MIS), 1),
+    (dict(), 6),                       # the cascade always needs a workspace
+    (dict(ws=FAKE, wsb=100), 6),
+    (dict(ws=MIS, wsb=1 << 20), 6),    # misaligned workspace
+    (dict(nseq=0), 0),                 # nothing to do
+])
+def test_cascade_validation(kw, status):
+    assert cascade(**kw) == status
+
+
+def test_cascade_workspace_bytes():
+    f = pkv.pkv_cascade_workspace_bytes
+    # Slot 0 (shared prefix) plus the per-sequence partitions, each (m, l, o).
+    assert f(2, 4, 4, 128, 16, 512, "f16", 512) == 2 * 4 * 2 * 130 * 4
+    assert f(2, 4, 4, 128, 16, 4096, "f16", 512) == 2 * 4 * 9 * 130 * 4
+    assert f(0, 4, 4, 128, 16, 512, "f16", 512) == 0
+    assert f(2, 6, 4, 128, 16, 512, "f16", 512) == 0
