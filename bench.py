@@ -37,15 +37,16 @@ HOST_LINK_GBS = 64.0  # MI355X host interface, PCIe 5.0 x16: 32 GT/s x 16 lanes 
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix-core peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "paged_kv_cache_359_amd", "csrc")
-# Sources the decode kernels are built from: counters taken on them stay valid while these
-# files are unchanged.
-DECODE_SOURCES = ["device.h", "mfma_tile.h", "host.h", "decode.hip"]
+# What the decode kernels are built from (sources and build flags): counters taken on them
+# stay valid while these files are unchanged.
+DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("device.h", "mfma_tile.h", "host.h", "decode.hip")] + \
+    [os.path.join(ROOT, "paged_kv_cache_359_amd", "build.py")]
 
 
 def decode_source_sha():
     h = hashlib.sha256()
     for f in DECODE_SOURCES:
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        h.update(open(f, "rb").read())
     return h.hexdigest()
 
 

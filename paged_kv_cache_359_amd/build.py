@@ -22,6 +22,13 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
 
+# Per-source additions.  The attention kernels keep their matrix-core accumulators in
+# ordinary VGPRs: with the default heuristic the compiler placed them in AGPRs and moved
+# them back and forth every chunk around the softmax rescale, and the extra registers cost a
+# wave per SIMD of occupancy.
+_VGPR_MFMA = ["-mllvm", "--amdgpu-mfma-vgpr-form"]
+SOURCE_FLAGS = {"prefill.hip": _VGPR_MFMA, "decode.hip": _VGPR_MFMA}
+
 
 def build(verbose: bool = False, extra_flags=None) -> str:
     hipcc = os.path.join(ROCM, "bin", "hipcc")
@@ -31,7 +38,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         path = os.path.join(CSRC, src)
         obj = os.path.join(CSRC, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, *lang, "-c", path, "-o", obj]
+        cmd = [hipcc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), *(extra_flags or []), "-I", INCLUDE,
+               *lang, "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True, capture_output=not verbose)

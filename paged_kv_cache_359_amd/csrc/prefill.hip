@@ -11,8 +11,8 @@ namespace pkv {
 // =========================================================================================
 // Prefill: one workgroup of 4 waves per (query head, 64 * NT consecutive new tokens,
 // sequence); wave w takes NT tiles of 16 new tokens each as the columns of the MFMA inner
-// loop.  One tile per wave keeps the accumulators in registers at two waves per SIMD, which
-// measured faster than two tiles per wave at one.  Sequence b's new tokens are q rows query_start[b] .. query_start[b+1]; with ctx_b
+// loop.  With the accumulators in VGPRs, two tiles per wave (each loaded chunk serves 32
+// columns) still fit two waves per SIMD.  Sequence b's new tokens are q rows query_start[b] .. query_start[b+1]; with ctx_b
 // tokens cached (the new ones included), new token j sits at position ctx_b - n_b + j and
 // sees keys 0 .. that position.
 // The workgroup walks the keys its rows need in 32-token chunks.  Each chunk's K and V rows
@@ -21,7 +21,7 @@ namespace pkv {
 // chunk c+1 are in flight while the waves compute chunk c from LDS.  Neighbouring workgroups
 // and the query heads of a group read the same K/V, so it is read through the caches.
 // =========================================================================================
-constexpr int kPrefillTiles = 1;  // 16-column tiles per wave
+constexpr int kPrefillTiles = 2;  // 16-column tiles per wave
 constexpr int kPrefillRows = 4 * 16 * kPrefillTiles;  // new tokens per workgroup
 
 template <int DT, int D, int BS>

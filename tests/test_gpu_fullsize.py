@@ -4,7 +4,8 @@ partitions), checked against the oracle where it can compute outputs one by one:
     table) replayed on the oracle allocator: bit-exact;
   * sampled cache rows read back from the pools: bit-exact against the token they hold;
   * sampled (sequence, head) outputs against the plain fp64 definition over that sequence's
-    contiguous K/V: within 5e-3 (fp16/bf16 K/V).
+    contiguous K/V: within 5e-3 (fp16/bf16 K/V); for the shared-prefix workloads also the
+    cascade decode's.
 """
 import numpy as np
 import pytest
@@ -53,6 +54,11 @@ def test_full_size_sampled(name):
     # The automatic split the benchmark times; the long-context GQA workload also in the
     # 512-token partitions its description names.
     outs = {p: g.decode(partition_size=p) for p in ([-1, 512] if name == "gqa_long" else [-1])}
+    if cfg.prefix_len:  # the shared-prefix workloads are also timed as a cascade decode
+        from tests.test_gpu_cascade import cascade
+        outs["cascade"], (starts, shared) = cascade(g.alloc, list(range(w.batch)), w.q[0],
+                                                    g.k_cache, g.v_cache, cfg.scale)
+        assert starts.tolist() == [0, w.batch] and int(shared[0]) == cfg.prefix_len // bs
     order = np.argsort(w.lengths)
     picks = {(int(order[0]), 0), (int(order[-1]), cfg.num_q_heads - 1)}
     while len(picks) < 24:
