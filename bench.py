@@ -122,6 +122,14 @@ def parse():
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TAG", "DIR"),
                     help="write profiles/<TAG>_kernel_trace.txt from DIR/kt_<TAG>/ and "
                          "DIR/kt_<TAG>.log (a kernel trace of bench.py run with --trace-args)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("TAG", "KERNEL", "RUNS"),
+                    help="write profiles/<TAG>_counters.txt: the mean per dispatch of every "
+                         "counter in the comma-separated rocprofv3 --pmc output directories RUNS "
+                         "(each holding <name>_counter_collection.csv), for kernels whose name "
+                         "contains KERNEL; --trace-args names the bench.py arguments, "
+                         "--counter-sets the counters of each run")
+    ap.add_argument("--counter-sets", default="",
+                    help="with --summarize-counters: ';'-separated counter lists, one per run")
     ap.add_argument("--trace-args", default="",
                     help="with --summarize-trace: the bench.py arguments the traced run used")
     ap.add_argument("--calib-copy", action="store_true",
@@ -841,6 +849,30 @@ def summarize_trace(tag, outdir, bench_args):
     print("\n".join(L))
 
 
+def summarize_counters(tag, kernel, runs, bench_args, counter_sets):
+    """Mean per dispatch of each hardware counter for one kernel, from rocprofv3 --pmc runs
+    (one counter group per run)."""
+    import csv
+    import glob
+    sets = counter_sets.split(";") if counter_sets else [""] * len(runs.split(","))
+    L = [f"Hardware counters of {kernel} under `bench.py {bench_args}`, one MI355X (gfx950).", "",
+         "Commands (repository root on the GPU box; one counter group per run), then the summary:"]
+    vals = {}
+    for run, cs in zip(runs.split(","), sets):
+        rel = os.path.relpath(run, ROOT)
+        L.append(f"  rocprofv3 --pmc {cs} -f csv -d {rel} -o <name> -- python3 bench.py {bench_args}")
+        for f in glob.glob(os.path.join(run, "*_counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                if kernel in r["Kernel_Name"]:
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    L.append(f"  python3 bench.py --summarize-counters {tag} {kernel} <runs> --trace-args \"{bench_args}\"")
+    L += ["", f"Mean per dispatch ({len(next(iter(vals.values()), []))} dispatches of the kernel):"]
+    for k in sorted(vals):
+        L.append(f"  {k:32s} {np.mean(vals[k]):16.0f}")
+    open(os.path.join(ROOT, "profiles", f"{tag}_counters.txt"), "w").write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
 def summarize(config, outdir):
     """Writes profiles/paged_decode_<config>_kernel_trace.txt and _hbm_traffic.txt from the
     rocprofv3 output of the three runs named in those files (one kernel trace, one
@@ -946,6 +978,9 @@ def main():
 
     if args.summarize:
         return summarize(args.config, args.summarize)
+    if args.summarize_counters:
+        t, k, r = args.summarize_counters
+        return summarize_counters(t, k, r, args.trace_args, args.counter_sets)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace[0], args.summarize_trace[1], args.trace_args)
     if args.swap:
