@@ -211,8 +211,11 @@ struct Mfma {
   __device__ static void compute(const DecodeArgs& a, const Chunk& ck, int cs, int lane,
                                  const vec8 (&qop)[KK], State& st, int lim = 0, int lim_min = 0) {
     const int g4 = lane >> 4;
-    bool need_mask = ck.need_mask;
-    if constexpr (CAUSAL) need_mask |= cs + kMfmaChunk - 1 > lim_min;
+    // Two independent reasons to mask (both wave-uniform): rows of tokens that do not exist
+    // (ck.vok is only meaningful when ck.need_mask is set), and keys past a column's causal
+    // limit.
+    const bool mask_rows = ck.need_mask;
+    const bool mask_causal = CAUSAL && cs + kMfmaChunk - 1 > lim_min;
     // S = K . Q^T for both halves.
     float4_t s[2];
 #pragma unroll
@@ -227,12 +230,8 @@ struct Mfma {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sv[hf][i] = s[hf][i] * a.scale_log2;
-        if (need_mask) {
-          if (!ck.vok[hf][i]) sv[hf][i] = kNegInf;
-          if constexpr (CAUSAL) {
-            if (cs + 16 * hf + 4 * g4 + i > lim) sv[hf][i] = kNegInf;  // a later token
-          }
-        }
+        if (mask_rows && !ck.vok[hf][i]) sv[hf][i] = kNegInf;
+        if (mask_causal && cs + 16 * hf + 4 * g4 + i > lim) sv[hf][i] = kNegInf;  // a later token
       }
     const float lm = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
                            fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));

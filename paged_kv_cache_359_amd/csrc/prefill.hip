@@ -113,13 +113,24 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   // Vector v of a chunk: row v / VECS (rows 0 .. CH-1 are K, CH .. 2CH-1 are V), 16-byte
   // column v % VECS.  Rows of tokens past t1 or in blocks outside the pool are zero.
   uint4 pre[PER];
+  // The 256 threads cover 256 / VECS rows per vector k.  When those rows lie in one block
+  // (whole 16-row groups and blocks of at least 16 tokens), the block id is wave-uniform and
+  // each load is a scalar base plus a per-lane offset.
+  constexpr int ROWS_PER_K = 256 / VECS;
+  constexpr bool UNIFORM_ROWS = ROWS_PER_K <= BS && CH % ROWS_PER_K == 0;
   auto fetch = [&](int cs, const int (&ids)[NB]) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int v = tid + 256 * k;
       const int row = v / VECS, col = v % VECS;
       const int off = row % CH;
-      const int id = cs + off < t1 ? id_of(ids, off) : -1;
+      int id;
+      if constexpr (UNIFORM_ROWS) {
+        const int off0 = (ROWS_PER_K * k) % CH;  // first row of this vector's rows
+        id = cs + off < t1 ? ids[off0 / BS] : -1;
+      } else {
+        id = cs + off < t1 ? id_of(ids, off) : -1;
+      }
       pre[k] = make_uint4(0, 0, 0, 0);
       if ((unsigned)id < (unsigned)a.num_blocks)
         pre[k] = load_cached((row < CH ? kb : vb) + size_t(id) * blk_bytes + size_t(off % BS) * D * 2 + col * 16);
@@ -152,17 +163,20 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
     for (int t = 0; t < NT; ++t) busy |= cs <= lim_max[t];
     if (busy) {
       typename M::Chunk ck;
-      // Masking is needed where the chunk runs past t1 or a block id is outside the pool.
+      // Masking rows is needed where the chunk runs past t1 or a block id is outside the
+      // pool; the tile looks at the rows' validity flags only then.
       bool need_mask = cs + CH > t1;
 #pragma unroll
       for (int k = 0; k < NB; ++k) need_mask |= (unsigned)ids_cur[k] >= (unsigned)a.num_blocks;
+      if (need_mask) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int off = 16 * hf + 4 * g4 + i;
-          ck.vok[hf][i] = cs + off < t1 && (unsigned)id_of(ids_cur, off) < (unsigned)a.num_blocks;
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int off = 16 * hf + 4 * g4 + i;
+            ck.vok[hf][i] = cs + off < t1 && (unsigned)id_of(ids_cur, off) < (unsigned)a.num_blocks;
+          }
+      }
       ck.need_mask = need_mask;
       M::load_lds(lds[c & 1], lds[c & 1] + CH * PITCH, PITCH, lane, ck);
 #pragma unroll
