@@ -201,6 +201,149 @@ def cpu_baseline(w, budget_s):
                       f"{c.num_q_heads} heads), median of {len(times)} runs"}
 
 
+def _grow_sample(build, run, limit, budget_s, start=1):
+    """Runs the oracle on a growing prefix of the work (``limit`` units) until one run costs
+    about a third of the budget; returns (units, median seconds, runs)."""
+    n = min(limit, start)
+    while True:
+        args = build(n)
+        dt = run(n, args)
+        if dt >= budget_s / 3 or n == limit:
+            break
+        n = min(limit, max(n + 1, int(n * (budget_s / 3) / max(dt, 1e-3))))
+    times = [dt]
+    while len(times) < 3 and sum(times) < budget_s:
+        times.append(run(n, args))
+    return n, float(np.median(times)), len(times)
+
+
+def _threads():
+    from threadpoolctl import threadpool_info
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
+
+
+def cpu_baseline_prefill(w, budget_s):
+    """The oracle's causal prefill, untouched, on the first sequences of the batch."""
+    import oracle
+    c = w.cfg
+    qs = w.query_start
+    q_bits = oracle.bits_of(w.q.cpu(), c.dtype)
+
+    def build(nseq):
+        nb = sum(-(-int(w.lengths[b]) // c.block_size) for b in range(nseq)) + 1
+        a = oracle.OracleAllocator(nb, c.block_size)
+        kp = oracle.new_pool(nb, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
+        vp = oracle.new_pool(nb, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
+        for b in range(nseq):
+            n = int(w.lengths[b])
+            slots = a.add(b, n)
+            k, v = w.token_kv(b, 0, n)
+            oracle.cache_write(kp, oracle.bits_of(k.cpu(), c.dtype), slots)
+            oracle.cache_write(vp, oracle.bits_of(v.cpu(), c.dtype), slots)
+        tables, lens = a.block_tables(range(nseq), max(len(a.tables[b]) for b in range(nseq)))
+        return kp, vp, tables, lens
+
+    def run(nseq, args):
+        kp, vp, tables, lens = args
+        t = time.perf_counter()
+        oracle.prefill(q_bits[: qs[nseq]], kp, vp, tables, lens, qs[: nseq + 1], c.scale, c.dtype)
+        return time.perf_counter() - t
+
+    nseq, dt, runs = _grow_sample(build, run, w.batch, budget_s)
+    flops = prefill_flops(c, w.lengths[:nseq], w.n_new[:nseq])
+    return {"value": round(flops / dt / 1e12, 9), "unit": "TFLOP/s", "cores": _threads(),
+            "kind": "oracle", "seconds_per_run": round(dt, 3), "runs": runs,
+            "sample": f"fp64 oracle causal prefill (row by row) of the first {nseq} of {w.batch} "
+                      f"sequences ({int(qs[nseq])} new tokens, {c.num_q_heads} heads), median of "
+                      f"{runs} runs"}
+
+
+def cpu_baseline_swap(w, victims, budget_s):
+    """The oracle's swap-out and swap-in (allocator plus whole-block copies to and from a host
+    copy), untouched, on the first victims, in a pool holding just those sequences."""
+    import oracle
+    c = w.cfg
+    bs = c.block_size
+
+    def build(nv):
+        vs = victims[:nv]
+        nb = sum(-(-int(w.lengths[v]) // bs) for v in vs) + 1
+        a = oracle.OracleAllocator(nb, bs)
+        kp = oracle.new_pool(nb, c.num_kv_heads, bs, c.head_dim, c.dtype)
+        vp = oracle.new_pool(nb, c.num_kv_heads, bs, c.head_dim, c.dtype)
+        for v in vs:
+            n = int(w.lengths[v]) - 1  # the cached context before the step
+            slots = a.add(v, n)
+            k, vv = w.token_kv(v, 0, n)
+            oracle.cache_write(kp, oracle.bits_of(k.cpu(), c.dtype), slots)
+            oracle.cache_write(vp, oracle.bits_of(vv.cpu(), c.dtype), slots)
+        return a, kp, vp, vs
+
+    def run(nv, args):
+        a, kp, vp, vs = args
+        t = time.perf_counter()
+        host = {}
+        for v in vs:
+            blocks = a.swap_out(v)
+            host[v] = (oracle.gather_blocks(kp, blocks), oracle.gather_blocks(vp, blocks))
+        for v in vs:
+            blocks = a.swap_in(v)
+            oracle.scatter_blocks(kp, blocks, host[v][0])
+            oracle.scatter_blocks(vp, blocks, host[v][1])
+        return time.perf_counter() - t
+
+    nv, dt, runs = _grow_sample(build, run, len(victims), budget_s)
+    nblk = sum(-(-(int(w.lengths[v]) - 1) // bs) for v in victims[:nv])
+    moved = 2 * nblk * c.num_kv_heads * bs * c.head_dim * c.dsize
+    return {"value": round(2 * moved / dt / 1e9, 6), "unit": "GB/s", "cores": _threads(),
+            "kind": "oracle", "seconds_per_run": round(dt, 3), "runs": runs,
+            "sample": f"oracle allocator swap-out/in with whole-block bit copies (NumPy) of the "
+                      f"first {nv} of {len(victims)} victims ({nblk} blocks, {moved / 1e6:.1f} MB "
+                      f"each way), median of {runs} runs"}
+
+
+def cpu_baseline_admission(ps, budget_s):
+    """The oracle admitting the first requests of the stream the way the GPU path does:
+    add_tokens, the cache write of the tokens not found cached, and the causal prefill of
+    those tokens over the whole prompt; in a pool sized for the sample."""
+    import oracle
+    c = ps.cfg
+    bs = c.block_size
+    R = c.num_requests
+    toks = [ps.tokens(r) for r in range(R)]
+    qall = ps.q  # [live, Hq, D] of the stream; reused as queries for the sampled rows
+    q_bits_row = oracle.bits_of(qall[:1].cpu(), c.dtype)[0]
+
+    def build(nr):
+        return nr
+
+    def run(nr, _):
+        nb = sum(-(-t.size // bs) for t in toks[:nr]) + 1
+        a = oracle.OracleAllocator(nb, bs)
+        kp = oracle.new_pool(nb, c.num_kv_heads, bs, c.head_dim, c.dtype)
+        vp = oracle.new_pool(nb, c.num_kv_heads, bs, c.head_dim, c.dtype)
+        t0 = time.perf_counter()
+        for r in range(nr):
+            slots, nc = a.add_tokens(r, toks[r].tolist())
+            n = toks[r].size
+            k, v = ps.token_kv(r, 0, n)
+            oracle.cache_write(kp, oracle.bits_of(k.cpu(), c.dtype), slots)
+            oracle.cache_write(vp, oracle.bits_of(v.cpu(), c.dtype), slots)
+            new = n - nc
+            q = np.broadcast_to(q_bits_row, (new,) + q_bits_row.shape).copy()
+            tab, lens = a.block_tables([r], len(a.tables[r]))
+            oracle.prefill(q, kp, vp, tab, lens, [0, new], c.scale, c.dtype)
+        return time.perf_counter() - t0
+
+    nr, dt, runs = _grow_sample(build, run, R, budget_s, start=2)
+    tokens = int(sum(t.size for t in toks[:nr]))
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": _threads(),
+            "kind": "oracle", "seconds_per_run": round(dt, 3), "runs": runs,
+            "sample": f"fp64 oracle admission (add_tokens, cache write, row-by-row causal prefill "
+                      f"of the uncached tokens) of the first {nr} of {R} requests ({tokens} prompt "
+                      f"tokens), median of {runs} runs"}
+
+
 def prefill_flops(cfg, lengths, n_new):
     """Causal attention flops of one prefill step: q.k and p.v, 2*D each, per (row, key) pair
     and query head; new token i of n sees ctx - n + i + 1 keys."""
@@ -312,7 +455,7 @@ def main_prefill(args, cfg):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": None,
                      "kernel": "paged_attention_prefill", "flops_per_launch": flops},
-        "cpu_baseline": None,
+        "cpu_baseline": (None if args.no_cpu_baseline else cpu_baseline_prefill(w, args.cpu_seconds)),
     }
     print(json.dumps(res), flush=True)
 
@@ -552,7 +695,7 @@ def main_swap(args):
                       "traffic": None,
                       "kernel": "gather_blocks (swap-out straight to pinned host memory)",
                       "bytes_per_launch": moved}),
-        "cpu_baseline": None,
+        "cpu_baseline": (None if args.no_cpu_baseline else cpu_baseline_swap(w, victims, args.cpu_seconds)),
     }
     print(json.dumps(res), flush=True)
 
@@ -657,7 +800,7 @@ def main_cascade(args):
                      "traffic": None,
                      "kernel": "paged_attention_cascade (prefix pass + decode + merge), unique bytes",
                      "bytes_per_launch": unique},
-        "cpu_baseline": None,
+        "cpu_baseline": (None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)),
     }
     print(json.dumps(res), flush=True)
 
@@ -821,7 +964,7 @@ def main_prefix_cache(args):
                      "frac": round(tf / peak, 5), "traffic": None,
                      "kernel": "paged_attention_prefill (uncached tokens)",
                      "flops_per_launch": round(sh["flops"] / len(batches))},
-        "cpu_baseline": None,
+        "cpu_baseline": (None if args.no_cpu_baseline else cpu_baseline_admission(ps, args.cpu_seconds)),
     }
     print(json.dumps(res), flush=True)
 
