@@ -12,9 +12,9 @@ namespace pkv {
 // Prefill: one workgroup of 4 waves per (query head, 64 * NT consecutive new tokens,
 // sequence); wave w takes NT tiles of 16 new tokens each as the columns of the MFMA inner
 // loop.  With the accumulators in VGPRs, two tiles per wave (each loaded chunk serves 32
-// columns) still fit two waves per SIMD.  Sequence b's new tokens are q rows query_start[b] .. query_start[b+1]; with ctx_b
-// tokens cached (the new ones included), new token j sits at position ctx_b - n_b + j and
-// sees keys 0 .. that position.
+// columns) still fit two waves per SIMD.  Sequence b's new tokens are q rows
+// query_start[b] .. query_start[b+1]; with ctx_b tokens cached (the new ones included), new
+// token j sits at position ctx_b - n_b + j and sees keys 0 .. that position.
 // The workgroup walks the keys its rows need in 32-token chunks.  Each chunk's K and V rows
 // are gathered through the block table once per workgroup into LDS (rows padded by 16 bytes
 // so that the waves' row reads spread over the banks), double-buffered: the global loads of
