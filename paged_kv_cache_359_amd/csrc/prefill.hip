@@ -21,6 +21,34 @@ namespace pkv {
 // chunk c+1 are in flight while the waves compute chunk c from LDS.  Neighbouring workgroups
 // and the query heads of a group read the same K/V, so it is read through the caches.
 // =========================================================================================
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Four 16-bit elements per lane, transposed across each group of 16 lanes
+// (ds_read_b64_tr_b16): lane i of a group receives, as element j, element i % 4 of the 8
+// bytes that lane 4j + i / 4 of the group points at.
+__device__ __forceinline__ uint2 read_tr16(lds_char* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_short4*>(p)));
+}
+
+// Four consecutive output elements (8 bytes of 16-bit values).
+template <int DT>
+__device__ __forceinline__ void store4(void* base, size_t idx, const float (&v)[4]) {
+  uint32_t w[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if constexpr (DT == DT_F16) {
+      const half2_t h = {_Float16(v[2 * k]), _Float16(v[2 * k + 1])};
+      w[k] = __builtin_bit_cast(uint32_t, h);
+    } else {
+      const bf162_t h = {__bf16(v[2 * k]), __bf16(v[2 * k + 1])};
+      w[k] = __builtin_bit_cast(uint32_t, h);
+    }
+  }
+  *reinterpret_cast<uint2*>(static_cast<char*>(base) + idx * 2) = make_uint2(w[0], w[1]);
+}
+
 constexpr int kPrefillTiles = 2;  // 16-column tiles per wave
 constexpr int kPrefillRows = 4 * 16 * kPrefillTiles;  // new tokens per workgroup
 
@@ -29,11 +57,16 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   using M = Mfma<DT, D, BS>;
   constexpr int NT = kPrefillTiles;
   constexpr int CH = kMfmaChunk;
-  constexpr int PITCH = D * 2 + 16;         // LDS bytes per K or V row
+  // LDS bytes per K row and per V row, padded so that the waves' reads spread over the banks
+  // (16-byte K row reads by 16 lanes; 8-byte transposed V reads by 4 x 4 lanes).
+  constexpr int PK = D * 2 + 16;
+  constexpr int PV = D * 2 + 32;
+  constexpr int VBASE = CH * PK;            // V rows follow the K rows in a buffer
+  constexpr int BUF = CH * PK + CH * PV;
   constexpr int VECS = D * 2 / 16;          // 16-byte vectors per row
   constexpr int PER = 2 * CH * VECS / 256;  // vectors each thread moves per chunk
   static_assert(PER * 256 == 2 * CH * VECS, "chunk must split evenly over the workgroup");
-  __shared__ __attribute__((aligned(16))) char lds[2][2 * CH * PITCH];
+  __shared__ __attribute__((aligned(16))) char lds[2][BUF];
 
   const int h = blockIdx.x;
   const int b = blockIdx.z;
@@ -140,7 +173,9 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int v = tid + 256 * k;
-      *reinterpret_cast<uint4*>(&lds[buf][(v / VECS) * PITCH + (v % VECS) * 16]) = pre[k];
+      const int row = v / VECS, col = v % VECS;
+      const int off = row < CH ? row * PK : VBASE + (row - CH) * PV;
+      *reinterpret_cast<uint4*>(&lds[buf][off + col * 16]) = pre[k];
     }
   };
 
@@ -178,7 +213,26 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
           }
       }
       ck.need_mask = need_mask;
-      M::load_lds(lds[c & 1], lds[c & 1] + CH * PITCH, PITCH, lane, ck);
+      // K operands: row cs + 16hf + lane%16, elements 32kk + 8(lane/16) .. + 8.
+      const char* kl = lds[c & 1];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int kk = 0; kk < M::KK; ++kk)
+          ck.kr[hf][kk] = *reinterpret_cast<const uint4*>(kl + (16 * hf + n16) * PK + (32 * kk + 8 * g4) * 2);
+      // V^T operand of output tile r, which here covers head elements 16r .. 16r + 15 (row
+      // lane%16 of the tile is element 16r + lane%16): element j of lane l is V of token
+      // 16(j/4) + 4(l/16) + j%4, the token the lane's score slot j holds.  One transposed
+      // read per 16-token half: lane l points at row 16hf + 4(l/16) + (l%16)/4, elements
+      // 16r + 4(l%4) .. + 4.
+      lds_char* vl = (lds_char*)(lds[c & 1]) + VBASE +
+                     (4 * g4 + (n16 >> 2)) * PV + (4 * (lane & 3)) * 2;
+#pragma unroll
+      for (int r = 0; r < M::E; ++r) {
+        const uint2 lo = read_tr16(vl + 32 * r);
+        const uint2 hi = read_tr16(vl + 16 * PV + 32 * r);
+        ck.vop[r] = __builtin_bit_cast(typename M::vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         if (cs <= lim_max[t])  // a tile whose columns all precede this chunk skips it
@@ -196,13 +250,15 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   for (int t = 0; t < NT; ++t) {
     st[t].l = xor_sum_16_32(st[t].l);
     if (16 * t + n16 < nq) {
-      float v[4 * M::E];
+      // Accumulator (r, v) of the lane is head element 16r + 4(lane/16) + v.
       const float inv = st[t].l > 0.f ? 1.f / st[t].l : 0.f;
+      const size_t row = (size_t(r0 + j0 + 16 * t + n16) * a.num_q_heads + h) * D;
 #pragma unroll
-      for (int r = 0; r < M::E; ++r)
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) v[vv * M::E + r] = st[t].acc[r][vv] * inv;
-      store_row<DT, 4 * M::E>(a.out, (size_t(r0 + j0 + 16 * t + n16) * a.num_q_heads + h) * D + 4 * M::E * g4, v);
+      for (int r = 0; r < M::E; ++r) {
+        const float v[4] = {st[t].acc[r][0] * inv, st[t].acc[r][1] * inv, st[t].acc[r][2] * inv,
+                            st[t].acc[r][3] * inv};
+        store4<DT>(a.out, row + 16 * r + 4 * g4, v);
+      }
     }
   }
 }
