@@ -16,8 +16,12 @@ stream, requiring bit-identical results.
 
 Prints one JSON line.  ``value`` is the whole step's logical KV throughput (bytes of K and V
 that the batch attends to, per second); ``roofline`` rates the decode kernels alone, timed
-with HIP events on the stream they run on; ``cpu_baseline`` times the fp64 CPU oracle on a
-bounded sample of the same batch.
+with HIP events on the stream they run on, and ``roofline.measured_read`` also against the
+read rates a plain probe kernel reaches over a 4 GiB buffer on the same device (in address
+order, and in random order at one KV head's block slice); ``kernel_protocol`` times the decode call
+alone on the final state (10 warm-up and 100 timed calls, each between its own events, 1 GiB
+written and another 1 GiB read between calls to clear the caches; median); ``cpu_baseline`` times the fp64 CPU
+oracle on a bounded sample of the same batch.
 """
 from __future__ import annotations
 
@@ -87,6 +91,68 @@ def counted_traffic(config_name):
             "source": os.path.relpath(path, ROOT)}
 
 
+def read_ceiling(dev, slice_bytes, nbytes=4 << 30, runs=10, warmup=3):
+    """Read rates the probe kernel reaches over a buffer of ``nbytes`` on ``dev``, the median
+    of ``runs`` event-timed launches each: in address order (1 MiB chunks), and in a seeded
+    random order of chunks one KV head's block slice long (the longest piece the decode
+    kernels read contiguously), when that slice is a power of two of at least 1 KiB.  The
+    buffer's size is fixed, not the workload's pool size, so that the launch's fixed costs
+    weigh the same in every workload's figure."""
+    import torch
+    import paged_kv_cache_359_amd as pkv
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    cs = torch.zeros(1, dtype=torch.int32, device=buf.device)
+
+    def rate(chunk, order):
+        n = nbytes // chunk
+        evs = []
+        for _ in range(warmup + runs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pkv.pkv_read_probe(buf, chunk, cs, order, n)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs[warmup:]]))
+        return n * chunk / (ms * 1e-3) / 1e9
+
+    res = {"buffer_bytes": nbytes, "stream_gbs": round(rate(1 << 20, None), 1)}
+    if slice_bytes >= 1024 and slice_bytes & (slice_bytes - 1) == 0:
+        g = torch.Generator().manual_seed(0)
+        order = torch.randperm(nbytes // slice_bytes, generator=g).to(torch.int32).to(buf.device)
+        res["paged_gbs"] = round(rate(slice_bytes, order), 1)
+        res["chunk_bytes"] = slice_bytes
+    return res
+
+
+def kernel_protocol(launch, nbytes, dev, warmup=10, runs=100, evict_bytes=1 << 30):
+    """``warmup`` untimed, then ``runs`` timed calls of ``launch``, each between its own pair
+    of HIP events on the current stream, with ``evict_bytes`` written to a scratch buffer
+    before every call (outside the events) so that no call finds the previous one's data in
+    the L2 or the last-level cache.  A read of a second buffer of the same size follows the
+    write, so that the write's dirty lines go back to HBM before the timed call rather than
+    during it.  Returns the median and the rate of ``nbytes``."""
+    import torch
+    scratch = torch.empty(evict_bytes, dtype=torch.uint8, device=dev)
+    clean = torch.zeros(evict_bytes // 4, dtype=torch.int32, device=dev)
+    evs = []
+    for i in range(warmup + runs):
+        scratch.fill_(i & 0xFF)
+        clean.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs[warmup:]]
+    med = float(np.median(ms))
+    return {"warmup": warmup, "runs": runs, "evict_bytes": evict_bytes,
+            "median_ms": round(med, 5), "min_ms": round(float(np.min(ms)), 5),
+            "max_ms": round(float(np.max(ms)), 5), "bytes": int(nbytes),
+            "gbs": round(nbytes / (med * 1e-3) / 1e9, 3)}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +168,9 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="run each step's uploads and cache write on a second stream during the "
                          "previous step's decode (whole tables uploaded per step)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measured read ceilings and the kernel timing protocol that "
+                         "follow the timed steps (profiling runs count the steps' launches only)")
     ap.add_argument("--check", action="store_true",
                     help="verify every timed step's output against a serial re-decode")
     ap.add_argument("--swap", action="store_true",
@@ -1057,7 +1126,7 @@ def summarize(config, outdir):
     pf, pw = per_kernel(fetch), per_kernel(write)
     main_k = [k for k in pf if "decode" in k][0]
     red = [k for k in pf if "reduce" in k]
-    run = "python3 bench.py --config {} --steps 2 --warmup 1 --no-cpu-baseline --calib-copy".format(C)
+    run = "python3 bench.py --config {} --steps 2 --warmup 1 --no-cpu-baseline --no-extras --calib-copy".format(C)
     T = [f"HBM traffic of the paged decode kernels, {C} workload, one MI355X (gfx950).", "",
          "Commands (repository root on the GPU box; one counter per run), then the summary:",
          f"  rocprofv3 --pmc FETCH_SIZE -f csv -d {rel}/pmc_fetch_{C} -o {C} -- {run}",
@@ -1088,7 +1157,7 @@ def summarize(config, outdir):
     L = [f"Kernel trace of the paged decode benchmark, {C} workload, one MI355X (gfx950).", "",
          "Command (repository root on the GPU box), then the summary:",
          f"  rocprofv3 --kernel-trace --stats -f csv -d {rel}/kt_{C} -o {C} -- python3 bench.py "
-         f"--config {C} --steps 16 --warmup 4 --no-cpu-baseline > {rel}/kt_{C}.log",
+         f"--config {C} --steps 16 --warmup 4 --no-cpu-baseline --no-extras > {rel}/kt_{C}.log",
          f"  python3 bench.py --config {C} --summarize {rel}",
          f"decode_source_sha256: {sha}", "",
          "bench.py line of the same run (HIP events on the launch stream, 16 timed steps):",
@@ -1266,6 +1335,25 @@ def main():
     value = bytes_avg / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = B / (ms_per_step * 1e-3)
 
+    ceiling = protocol = None
+    if not args.no_extras:
+        # The decode call alone on the final state, by the kernel timing protocol, and the
+        # read rates of the probe kernel on the same device.
+        lens_final = torch.from_numpy((w.lengths + total_steps - 1).astype(np.int32)).to(dev)
+        hint_final = torch.from_numpy(alloc.pkv_shared_prefix_blocks(ids)).to(dev) if use_hint else None
+        final_bytes = kv_per_token * int(np.sum(w.lengths + total_steps - 1))
+        protocol = kernel_protocol(
+            lambda: pkv.pkv_paged_attention_decode(out, q[total_steps - 1], k_cache, v_cache,
+                                                   final_tables(), lens_final, max_len_final,
+                                                   c.scale, args.partition, workspace, hint_final),
+            final_bytes, dev)
+        ceiling = read_ceiling(dev, c.block_size * c.head_dim * c.dsize)
+        ceiling["frac_of_stream"] = round(achieved / ceiling["stream_gbs"], 5)
+        if "paged_gbs" in ceiling:
+            ceiling["frac_of_paged"] = round(achieved / ceiling["paged_gbs"], 5)
+        print(f"[bench] kernel protocol median {protocol['median_ms']} ms; read ceiling "
+              f"{ceiling}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
@@ -1292,7 +1380,9 @@ def main():
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
                      "traffic_detail": traffic,
                      "kernel": "paged_attention_decode (decode + partition merge)",
-                     "bytes_per_launch": round(bytes_avg)},
+                     "bytes_per_launch": round(bytes_avg),
+                     "measured_read": ceiling},
+        "kernel_protocol": protocol,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

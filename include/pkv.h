@@ -378,6 +378,24 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        int32_t max_query_len, int32_t max_context_len, float scale,
                                        pkv_dtype dtype, void* stream);
 
+/* ======================================================================================
+ * Measurement
+ * ====================================================================================== */
+
+/* Read-bandwidth probe.  Decode attention is bound by memory traffic ("LLM Systems 24:
+ * Efficient LLM Inference with PagedAttention and vLLM", §2.2.3.6), so its kernels are rated
+ * against the read rate this call reaches on the same device.  Reads num_chunks chunks of
+ * chunk_bytes bytes of buf (device, 16-byte aligned, at least num_chunks * chunk_bytes
+ * bytes): the i-th chunk read is chunk chunk_order[i] (device, num_chunks int32; entries
+ * outside [0, num_chunks) are skipped), or chunk i when chunk_order is NULL.  The XOR of
+ * every 32-bit word read is XORed into *checksum (device, 4-byte aligned; the caller sets it
+ * first, usually to 0), so with a permutation as the order the result is the XOR of the
+ * whole buffer.  chunk_bytes: a power of two from 1024 to 2^30, and num_chunks * chunk_bytes
+ * at most 2^41, else INVALID_ARG.
+ * num_chunks == 0 is a no-op.  Enqueued on stream; nothing is written but *checksum. */
+pkv_status pkv_read_probe(const void* buf, const int32_t* chunk_order, int64_t num_chunks,
+                          int32_t chunk_bytes, uint32_t* checksum, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,7 @@ SIGNATURES = {
     "pkv_paged_attention_prefill": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                             c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                             c_i32, c_f32, c_i32, c_vp]),
+    "pkv_read_probe": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_vp, c_vp]),
 }
 
 _lib = None

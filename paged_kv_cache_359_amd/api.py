@@ -447,3 +447,24 @@ def pkv_paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_
         int(max_context_len), float(scale), _dtype_code(k_cache), _stream(q)),
         "pkv_paged_attention_prefill")
     return out
+
+
+def pkv_read_probe(buf, chunk_bytes: int, checksum, chunk_order=None, num_chunks=None):
+    """Reads ``num_chunks`` chunks of ``chunk_bytes`` bytes of the GPU tensor ``buf`` (default:
+    all of it) in address order, or in the order ``chunk_order`` (device int32) gives, and
+    XORs every 32-bit word read into ``checksum`` (device, one int32/uint32 element)."""
+    import torch
+    nbytes = buf.numel() * buf.element_size()
+    if num_chunks is None:
+        num_chunks = nbytes // chunk_bytes
+    if num_chunks * chunk_bytes > nbytes:
+        raise ValueError("the chunks extend past the end of buf")
+    if checksum.dtype not in (torch.int32, torch.uint32) or checksum.numel() < 1:
+        raise TypeError("checksum must hold one 32-bit integer")
+    order = 0
+    if chunk_order is not None:
+        if chunk_order.dtype != torch.int32 or chunk_order.numel() != num_chunks:
+            raise ValueError("chunk_order must be num_chunks int32")
+        order = _dev(chunk_order)
+    _check(_lib.load().pkv_read_probe(_dev(buf), order or None, int(num_chunks), int(chunk_bytes),
+                                      _dev(checksum), _stream(buf)), "pkv_read_probe")

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-SOURCES = ["allocator.cpp", "cache_ops.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["allocator.cpp", "cache_ops.hip", "decode.hip", "prefill.hip", "probe.hip"]
 
 # Device code is built without packed-fp32 instructions (compiler-generated v_pk_* fp32 ops
 # are avoided on this target); the host pass only warns that it does not know the feature.

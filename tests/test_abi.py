@@ -307,3 +307,19 @@ def test_cascade_workspace_bytes():
     assert f(2, 4, 4, 128, 16, 4096, "f16", 512) == 2 * 4 * 9 * 130 * 4
     assert f(0, 4, 4, 128, 16, 512, "f16", 512) == 0
     assert f(2, 6, 4, 128, 16, 512, "f16", 512) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, None, -1, 4096, FAKE), 1),       # negative chunk count
+    ((FAKE, None, 4, 512, FAKE), 1),         # chunks below 1 KiB
+    ((FAKE, None, 4, 3072, FAKE), 1),        # not a power of two
+    ((FAKE, None, 4, -4096, FAKE), 1),      # negative chunk size
+    ((None, None, 4, 4096, FAKE), 1),        # no buffer
+    ((MIS, None, 4, 4096, FAKE), 1),         # misaligned buffer
+    ((FAKE, None, 4, 4096, None), 1),        # no checksum word
+    ((FAKE, None, 4, 4096, ctypes.c_void_p(0x100002)), 1),  # misaligned checksum word
+    ((FAKE, None, (1 << 29) + 1, 4096, FAKE), 1),  # more than 2^31 1 KiB pieces
+    ((FAKE, None, 0, 4096, FAKE), 0),        # nothing to read: no-op
+])
+def test_read_probe_validation(args, status):
+    assert lib().pkv_read_probe(*args, None) == status
