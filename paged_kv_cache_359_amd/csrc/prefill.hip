@@ -49,6 +49,71 @@ __device__ __forceinline__ void store4(void* base, size_t idx, const float (&v)[
   *reinterpret_cast<uint2*>(static_cast<char*>(base) + idx * 2) = make_uint2(w[0], w[1]);
 }
 
+// Online-softmax update of one 16-column tile with the chunk in ck (keys cs .. cs + 31), as
+// the shared tile's compute does, in two forms.  c = |scale| * log2(e); the query operands
+// carry the scale's sign, so c >= 0 and the maximum of the unscaled scores times c is the
+// maximum of the scaled ones.  MASKED = false: every row of the chunk exists and no key is
+// past any column's causal limit; the scale is folded into the exponent (one fused
+// multiply-add per score) and only the lane's maximum is scaled.  MASKED = true: the rows
+// whose bit in okbits is clear (bit 4hf + i for the lane's row 16hf + 4(lane/16) + i) and keys
+// past the column's limit lim get -inf scores.  The chunk loop picks the form per chunk with
+// a uniform branch, so the usual chunk runs no masking instructions at all.
+template <typename M, bool MASKED>
+__device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs, int g4, float c,
+                                            const typename M::vec8 (&qop)[M::KK],
+                                            typename M::State& st, int lim, uint32_t okbits) {
+  float4_t s[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    s[hf] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < M::KK; ++kk)
+      s[hf] = M::mma(__builtin_bit_cast(typename M::vec8, ck.kr[hf][kk]), qop[kk], s[hf]);
+  }
+  float sv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int hf = j >> 2, i = j & 3;
+    sv[j] = s[hf][i];
+    if constexpr (MASKED) {
+      sv[j] *= c;
+      if (!((okbits >> j) & 1u) || cs + 16 * hf + 4 * g4 + i > lim) sv[j] = kNegInf;
+    }
+  }
+  float lm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                   fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  if constexpr (!MASKED) lm *= c;
+  // Lazy rescaling exactly as in the shared tile: the reference st.m moves (with a
+  // cross-lane maximum and a rescale) only when a score exceeds it by more than
+  // kRescaleSlack.
+  if (__builtin_amdgcn_ballot_w64(lm > st.m + kRescaleSlack)) {
+    const float cm = xor_max_16_32(lm);
+    const bool grow = cm > st.m + kRescaleSlack;
+    const float mn = grow ? cm : st.m;
+    const float alpha = exp2_hw(st.m - (mn == kNegInf ? 0.f : mn));
+    st.l *= alpha;
+#pragma unroll
+    for (int r = 0; r < M::E; ++r) st.acc[r] *= alpha;
+    st.m = mn;
+  }
+  const float mu = st.m == kNegInf ? 0.f : st.m;
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = MASKED ? exp2_hw(sv[j] - mu) : exp2_hw(__builtin_fmaf(sv[j], c, -mu));
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  typename M::vec8 phi, plo;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    phi[j] = typename M::elt(p[j]);
+    if constexpr (M::SPLIT_P) plo[j] = typename M::elt(p[j] - float(phi[j]));
+  }
+#pragma unroll
+  for (int r = 0; r < M::E; ++r) {
+    st.acc[r] = M::mma(ck.vop[r], phi, st.acc[r]);
+    if constexpr (M::SPLIT_P) st.acc[r] = M::mma(ck.vop[r], plo, st.acc[r]);
+  }
+}
+
 constexpr int kPrefillTiles = 2;  // 16-column tiles per wave
 constexpr int kPrefillRows = 4 * 16 * kPrefillTiles;  // new tokens per workgroup
 
@@ -105,6 +170,9 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
         const char* qp = static_cast<const char*>(a.q) + ((size_t(r0 + jt + n16) * a.num_q_heads + h) * D) * 2;
         w = *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2);
       }
+      if (a.scale_log2 < 0.f) {  // the scale's sign goes into the query (exact)
+        w.x ^= 0x80008000u, w.y ^= 0x80008000u, w.z ^= 0x80008000u, w.w ^= 0x80008000u;
+      }
       qop[t][kk] = __builtin_bit_cast(typename M::vec8, w);
     }
   }
@@ -115,6 +183,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
 #pragma unroll
     for (int kk = 0; kk < M::KK; ++kk) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qop[t][kk])));
 
+  const float c_abs = fabsf(a.scale_log2);
   const int kvh = h / a.group;
   const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
   const size_t head_off = size_t(kvh) * BS * D * 2;
@@ -187,7 +256,10 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
     stash(0);
   }
   __syncthreads();
-  for (int c = 0; c < nch; ++c) {
+  // One chunk: prefetch the next chunk's rows and the block ids two ahead, update the tiles
+  // from LDS, stash the prefetched rows.  MASKED selects the tile update's form.
+  auto step = [&](int c, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cs = c * CH;
     if (c + 1 < nch) {
       fetch(cs + CH, ids_next);
@@ -198,21 +270,22 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
     for (int t = 0; t < NT; ++t) busy |= cs <= lim_max[t];
     if (busy) {
       typename M::Chunk ck;
-      // Masking rows is needed where the chunk runs past t1 or a block id is outside the
-      // pool; the tile looks at the rows' validity flags only then.
-      bool need_mask = cs + CH > t1;
+      // Rows that do not exist (past t1, or in a block outside the pool) have their bit in
+      // okbits cleared; only the masked form reads it.
+      uint32_t okbits = 0xFFu;
+      if constexpr (MASKED) {
+        bool need_mask = cs + CH > t1;
 #pragma unroll
-      for (int k = 0; k < NB; ++k) need_mask |= (unsigned)ids_cur[k] >= (unsigned)a.num_blocks;
-      if (need_mask) {
+        for (int k = 0; k < NB; ++k) need_mask |= (unsigned)ids_cur[k] >= (unsigned)a.num_blocks;
+        if (need_mask) {
+          okbits = 0;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int off = 16 * hf + 4 * g4 + i;
-            ck.vok[hf][i] = cs + off < t1 && (unsigned)id_of(ids_cur, off) < (unsigned)a.num_blocks;
+          for (int j = 0; j < 8; ++j) {
+            const int off = 16 * (j >> 2) + 4 * g4 + (j & 3);
+            if (cs + off < t1 && (unsigned)id_of(ids_cur, off) < (unsigned)a.num_blocks) okbits |= 1u << j;
           }
+        }
       }
-      ck.need_mask = need_mask;
       // K operands: row cs + 16hf + lane%16, elements 32kk + 8(lane/16) .. + 8.
       const char* kl = lds[c & 1];
 #pragma unroll
@@ -236,7 +309,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         if (cs <= lim_max[t])  // a tile whose columns all precede this chunk skips it
-          M::template compute<true>(a, ck, cs, lane, qop[t], st[t], lim[t], lim_min[t]);
+          tile_update<M, MASKED>(ck, cs, g4, c_abs, qop[t], st[t], lim[t], okbits);
     }
     if (c + 1 < nch) stash((c + 1) & 1);
 #pragma unroll
@@ -245,7 +318,21 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
       ids_next[k] = ids_after[k];
     }
     __syncthreads();
+  };
+  // Chunks that end at or before the workgroup's first query position lie wholly before
+  // every column's causal limit and inside the context, so they need no masking unless a
+  // table entry is outside the pool; the first such entry ends the unmasked loop.  The rest
+  // (the diagonal chunks and the context's tail) take the masked form.
+  const int n_plain = min(nch, max(0, (first + jw + 1) / CH));
+  int c = 0;
+  for (; c < n_plain; ++c) {
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) bad |= (unsigned)ids_cur[k] >= (unsigned)a.num_blocks;
+    if (bad) break;
+    step(c, std::false_type{});
   }
+  for (; c < nch; ++c) step(c, std::true_type{});
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     st[t].l = xor_sum_16_32(st[t].l);

@@ -178,9 +178,11 @@ class GpuState:
         return out
 
 
-    def prefill(self, q=None, query_start=None, lens=None, max_query_len=None):
+    def prefill(self, q=None, query_start=None, lens=None, max_query_len=None, tables=None,
+                scale=None):
         c = self.w.cfg
-        tables, l = self.tables()
+        t_own, l = self.tables()
+        tables = t_own if tables is None else tables
         lens = l if lens is None else lens
         qs = self.w.query_start if query_start is None else query_start
         q = self.w.q if q is None else q
@@ -190,7 +192,7 @@ class GpuState:
         qsd = torch.from_numpy(np.ascontiguousarray(qs, dtype=np.int32)).to(self.device)
         mq = int(np.max(np.diff(qs))) if max_query_len is None else max_query_len
         pkv.pkv_paged_attention_prefill(out, q, self.k_cache, self.v_cache, t, ld, qsd, mq,
-                                        int(np.max(lens)), c.scale)
+                                        int(np.max(lens)), c.scale if scale is None else scale)
         return out
 
 

@@ -107,12 +107,12 @@ class OracleState:
         return oracle.decode(q_bits, self.k_pool, self.v_pool, tables, lens, c.scale, c.dtype)
 
 
-    def prefill(self):
+    def prefill(self, scale=None):
         c = self.w.cfg
         tables, lens = self.tables()
         q_bits = oracle.bits_of(self.w.q, c.dtype)
         return oracle.prefill(q_bits, self.k_pool, self.v_pool, tables, lens,
-                              self.w.query_start, c.scale, c.dtype)
+                              self.w.query_start, c.scale if scale is None else scale, c.dtype)
 
 
 def build(w: W.Workload, **kw) -> OracleState:

@@ -74,6 +74,49 @@ def test_prefill_shape_sweep(dtype, d, bs, hq, hkv):
         check_all(*both("prefill_llama7b", **cfg))
 
 
+@pytest.mark.parametrize("factor", [-1.0, 0.0, 3.0])
+def test_prefill_any_scale(factor):
+    """Negative, zero and large scales (the kernel folds the scale's sign into the query)."""
+    for dtype in ("f16", "bf16"):
+        w, g, o = both("prefill_chunked_gqa", batch=2, lengths=("fixed", (300, 700)),
+                       new_tokens=("fixed", 140), num_blocks=80, dtype=dtype)
+        scale = factor * w.cfg.scale
+        out = g.prefill(scale=scale).double().cpu().numpy()
+        err = check(out, o.prefill(scale=scale), dtype, f"scale {scale}")
+        print(f"  {dtype} scale {scale:.4g}: max abs err {err:.3g}", flush=True)
+
+
+def test_prefill_invalid_table_entries():
+    """Out-of-range block ids count as empty blocks, in the chunks before the diagonal (where
+    the kernel otherwise skips masking), on the diagonal, and in the first chunk."""
+    w, g, o = both("prefill_chunked_gqa", batch=3, lengths=("fixed", (700, 400, 300)),
+                   new_tokens=("fixed", 150), num_blocks=120)
+    c = w.cfg
+    tables, lens = o.tables()
+    bad = tables.copy()
+    bs = c.block_size
+    holes = {0: [3, 40], 1: [0, (400 - 150) // bs + 2], 2: [17]}  # block indices per row
+    bad[0, 3], bad[0, 40] = -7, c.num_blocks + 5
+    bad[1, 0], bad[1, (400 - 150) // bs + 2] = -1, c.num_blocks
+    bad[2, 17] = 1 << 30
+    out = g.prefill(tables=bad).double().cpu().numpy()
+    q = oracle.to_f64(oracle.bits_of(w.q.cpu(), c.dtype), c.dtype)
+    qs = w.query_start
+    for b, blks in holes.items():
+        n = int(qs[b + 1] - qs[b])
+        ctx = int(lens[b])
+        kv = [(oracle.to_f64(oracle.gather(o.k_pool, tables[b], ctx, g_), c.dtype),
+               oracle.to_f64(oracle.gather(o.v_pool, tables[b], ctx, g_), c.dtype))
+              for g_ in range(c.num_kv_heads)]
+        for i in range(0, n, 7):
+            pos = ctx - n + i
+            keep = [t for t in range(pos + 1) if t // bs not in blks]
+            for h in range(0, c.num_q_heads, 5):
+                k, v = kv[h // c.group]
+                r = oracle.attention_contiguous(q[int(qs[b]) + i, h], k[keep], v[keep], c.scale)
+                check(out[int(qs[b]) + i, h], r, c.dtype, f"b={b} row {i} h={h}")
+
+
 def test_prefill_matches_decode_kernel_on_the_last_row():
     """The newest row of a prefill and a decode of that sequence read the same keys."""
     w, g, o = both("prefill_chunked_gqa", batch=2, lengths=("fixed", (300, 77)), num_blocks=80)
