@@ -51,12 +51,11 @@ __device__ __forceinline__ void store4(void* base, size_t idx, const float (&v)[
 
 // Online-softmax update of one 16-column tile with the chunk in ck (keys cs .. cs + 31), as
 // the shared tile's compute does, in two forms.  c = |scale| * log2(e); the query operands
-// carry the scale's sign, so c >= 0 and the maximum of the unscaled scores times c is the
-// maximum of the scaled ones.  MASKED = false: every row of the chunk exists and no key is
-// past any column's causal limit; the scale is folded into the exponent (one fused
-// multiply-add per score) and only the lane's maximum is scaled.  MASKED = true: the rows
-// whose bit in okbits is clear (bit 4hf + i for the lane's row 16hf + 4(lane/16) + i) and keys
-// past the column's limit lim get -inf scores.  The chunk loop picks the form per chunk with
+// carry the scale's sign, so c >= 0.  Each score becomes its exponent relative to the
+// running reference in one fused multiply-add.  MASKED = false: every row of the chunk
+// exists and no key is past any column's causal limit.  MASKED = true: the rows whose bit
+// in okbits is clear (bit 4hf + i for the lane's row 16hf + 4(lane/16) + i) and keys past
+// the column's limit lim get -inf exponents.  The chunk loop picks the form per chunk with
 // a uniform branch, so the usual chunk runs no masking instructions at all.
 template <typename M, bool MASKED>
 __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs, int g4, float c,
@@ -70,24 +69,26 @@ __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs,
     for (int kk = 0; kk < M::KK; ++kk)
       s[hf] = M::mma(__builtin_bit_cast(typename M::vec8, ck.kr[hf][kk]), qop[kk], s[hf]);
   }
-  float sv[8];
+  // e = exponent of each probability relative to the current reference: s * c - mu.
+  const float mu = st.m == kNegInf ? 0.f : st.m;
+  float e[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int hf = j >> 2, i = j & 3;
-    sv[j] = s[hf][i];
-    if constexpr (MASKED) {
-      sv[j] *= c;
-      if (!((okbits >> j) & 1u) || cs + 16 * hf + 4 * g4 + i > lim) sv[j] = kNegInf;
-    }
+    e[j] = __builtin_fmaf(s[hf][i], c, -mu);
+    if constexpr (MASKED)
+      if (!((okbits >> j) & 1u) || cs + 16 * hf + 4 * g4 + i > lim) e[j] = kNegInf;
   }
-  float lm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                   fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-  if constexpr (!MASKED) lm *= c;
-  // Lazy rescaling exactly as in the shared tile: the reference st.m moves (with a
-  // cross-lane maximum and a rescale) only when a score exceeds it by more than
-  // kRescaleSlack.
-  if (__builtin_amdgcn_ballot_w64(lm > st.m + kRescaleSlack)) {
-    const float cm = xor_max_16_32(lm);
+  const float lm = fmaxf(fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])),
+                         fmaxf(fmaxf(e[4], e[5]), fmaxf(e[6], e[7])));
+  // Lazy rescaling as in the shared tile: the reference st.m moves (with a cross-lane maximum
+  // and a rescale) only when a score exceeds it by more than kRescaleSlack, or when it is
+  // still -inf (no key seen) and a finite score arrives.  The maximum is taken over the
+  // exponents, which are already rounded results, so no extra instruction readies the
+  // matrix-core outputs for the comparison.
+  const float thr = st.m == kNegInf ? kNegInf : kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(lm > thr)) {
+    const float cm = xor_max_16_32(lm) + mu;  // column maximum, absolute
     const bool grow = cm > st.m + kRescaleSlack;
     const float mn = grow ? cm : st.m;
     const float alpha = exp2_hw(st.m - (mn == kNegInf ? 0.f : mn));
@@ -95,17 +96,34 @@ __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs,
 #pragma unroll
     for (int r = 0; r < M::E; ++r) st.acc[r] *= alpha;
     st.m = mn;
+    const float shift = (mn == kNegInf ? 0.f : mn) - mu;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] -= shift;
   }
-  const float mu = st.m == kNegInf ? 0.f : st.m;
   float p[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) p[j] = MASKED ? exp2_hw(sv[j] - mu) : exp2_hw(__builtin_fmaf(sv[j], c, -mu));
+  for (int j = 0; j < 8; ++j) p[j] = exp2_hw(e[j]);
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   typename M::vec8 phi, plo;
+  if constexpr (M::SPLIT_P) {
+    // Pairs: one packed conversion gives both high parts; each reads back as fp32 by a
+    // shift or a mask of its half, and the remainders form the second packed conversion.
+    uint32_t wh[4], wl[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    phi[j] = typename M::elt(p[j]);
-    if constexpr (M::SPLIT_P) plo[j] = typename M::elt(p[j] - float(phi[j]));
+    for (int q = 0; q < 4; ++q) {
+      const bf162_t h = {__bf16(p[2 * q]), __bf16(p[2 * q + 1])};
+      wh[q] = __builtin_bit_cast(uint32_t, h);
+      asm("" : "+v"(wh[q]));  // opaque, so the low half is read back, not converted again
+      const float h0 = __builtin_bit_cast(float, wh[q] << 16);
+      const float h1 = __builtin_bit_cast(float, wh[q] & 0xFFFF0000u);
+      const bf162_t l = {__bf16(p[2 * q] - h0), __bf16(p[2 * q + 1] - h1)};
+      wl[q] = __builtin_bit_cast(uint32_t, l);
+    }
+    phi = __builtin_bit_cast(typename M::vec8, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+    plo = __builtin_bit_cast(typename M::vec8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) phi[j] = typename M::elt(p[j]);
   }
 #pragma unroll
   for (int r = 0; r < M::E; ++r) {
