@@ -214,11 +214,16 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   // no K/V load waits for its table entry.
   constexpr int NB = CH / BS;  // blocks per chunk (block sizes divide the chunk)
   static_assert(NB * BS == CH, "block size must divide the chunk");
+  // The table does not change during the kernel: reading it through the constant address
+  // space makes these scalar loads, which wait on their own counter instead of on every
+  // vector load in flight (the K/V prefetch issued just before).
+  const __attribute__((address_space(4))) int32_t* ctbl =
+      (const __attribute__((address_space(4))) int32_t*)tbl;
   auto load_ids = [&](int cs, int (&ids)[NB]) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int tok = cs + k * BS;
-      ids[k] = uniform(tok < t1 ? tbl[tok / BS] : -1);
+      ids[k] = tok < t1 ? ctbl[tok / BS] : -1;
     }
   };
   // The id of the block holding token cs + off (0 <= off < CH).
@@ -231,7 +236,8 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   };
 
   // Vector v of a chunk: row v / VECS (rows 0 .. CH-1 are K, CH .. 2CH-1 are V), 16-byte
-  // column v % VECS.  Rows of tokens past t1 or in blocks outside the pool are zero.
+  // column v % VECS.  Rows in blocks outside the pool are zero, and so are V rows of tokens
+  // past t1.
   uint4 pre[PER];
   // The 256 threads cover 256 / VECS rows per vector k.  When those rows lie in one block
   // (whole 16-row groups and blocks of at least 16 tokens), the block id is wave-uniform and
@@ -239,21 +245,31 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   constexpr int ROWS_PER_K = 256 / VECS;
   constexpr bool UNIFORM_ROWS = ROWS_PER_K <= BS && CH % ROWS_PER_K == 0;
   auto fetch = [&](int cs, const int (&ids)[NB]) {
+    const bool tail = cs + CH > t1;  // wave-uniform: some row of the chunk is past t1
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int v = tid + 256 * k;
       const int row = v / VECS, col = v % VECS;
       const int off = row % CH;
-      int id;
+      const uint32_t lane_off = uint32_t((off % BS) * D * 2 + col * 16);
       if constexpr (UNIFORM_ROWS) {
-        const int off0 = (ROWS_PER_K * k) % CH;  // first row of this vector's rows
-        id = cs + off < t1 ? ids[off0 / BS] : -1;
+        // One block for the vector's rows, all K or all V: a scalar base plus the lane's
+        // offset.  A block outside the pool is read as block 0 and zeroed.  Rows past t1
+        // inside a real block are read (they lie in the pool): their keys get -inf scores
+        // in the masked tile update, and their values are zeroed, since 0 * garbage may be
+        // NaN.  Both zeroings are rare and sit behind a branch, so the usual chunk issues
+        // its loads and nothing else.
+        const bool is_v = ROWS_PER_K * k >= CH;
+        const int id = ids[((ROWS_PER_K * k) % CH) / BS];
+        const bool valid = (unsigned)id < (unsigned)a.num_blocks;
+        pre[k] = load_cached((is_v ? vb : kb) + size_t(valid ? id : 0) * blk_bytes + lane_off);
+        if (!valid || (is_v && tail && cs + off >= t1)) pre[k] = make_uint4(0, 0, 0, 0);
       } else {
-        id = cs + off < t1 ? id_of(ids, off) : -1;
+        const int id = cs + off < t1 ? id_of(ids, off) : -1;
+        pre[k] = make_uint4(0, 0, 0, 0);
+        if ((unsigned)id < (unsigned)a.num_blocks)
+          pre[k] = load_cached((row < CH ? kb : vb) + size_t(id) * blk_bytes + lane_off);
       }
-      pre[k] = make_uint4(0, 0, 0, 0);
-      if ((unsigned)id < (unsigned)a.num_blocks)
-        pre[k] = load_cached((row < CH ? kb : vb) + size_t(id) * blk_bytes + size_t(off % BS) * D * 2 + col * 16);
     }
   };
   auto stash = [&](int buf) {
