@@ -57,11 +57,10 @@ __device__ __forceinline__ void store4(void* base, size_t idx, const float (&v)[
 // in okbits is clear (bit 4hf + i for the lane's row 16hf + 4(lane/16) + i) and keys past
 // the column's limit lim get -inf exponents.  The chunk loop picks the form per chunk with
 // a uniform branch, so the usual chunk runs no masking instructions at all.
-template <typename M, bool MASKED>
-__device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs, int g4, float c,
-                                            const typename M::vec8 (&qop)[M::KK],
-                                            typename M::State& st, int lim, uint32_t okbits) {
-  float4_t s[2];
+// S = K . Q^T of one tile for both 16-token halves of the chunk.
+template <typename M>
+__device__ __forceinline__ void tile_scores(const typename M::Chunk& ck,
+                                            const typename M::vec8 (&qop)[M::KK], float4_t (&s)[2]) {
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     s[hf] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -69,6 +68,12 @@ __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs,
     for (int kk = 0; kk < M::KK; ++kk)
       s[hf] = M::mma(__builtin_bit_cast(typename M::vec8, ck.kr[hf][kk]), qop[kk], s[hf]);
   }
+}
+
+template <typename M, bool MASKED>
+__device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs, int g4, float c,
+                                            const float4_t (&s)[2], typename M::State& st, int lim,
+                                            uint32_t okbits) {
   // e = exponent of each probability relative to the current reference: s * c - mu.
   const float mu = st.m == kNegInf ? 0.f : st.m;
   float e[8];
@@ -340,10 +345,24 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
         const uint2 hi = read_tr16(vl + 16 * PV + 32 * r);
         ck.vop[r] = __builtin_bit_cast(typename M::vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
+      if constexpr (MASKED) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        if (cs <= lim_max[t])  // a tile whose columns all precede this chunk skips it
-          tile_update<M, MASKED>(ck, cs, g4, c_abs, qop[t], st[t], lim[t], okbits);
+        for (int t = 0; t < NT; ++t)
+          if (cs <= lim_max[t]) {  // a tile whose columns all precede this chunk skips it
+            float4_t sc[2];
+            tile_scores<M>(ck, qop[t], sc);
+            tile_update<M, true>(ck, cs, g4, c_abs, sc, st[t], lim[t], okbits);
+          }
+      } else {
+        // Every tile of the wave is active here (a tile without columns computes on zero
+        // queries and is never stored).  All score products are issued first, so that the
+        // matrix cores work on the later tiles while the earlier tiles' softmax runs.
+        float4_t sc[NT][2];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) tile_scores<M>(ck, qop[t], sc[t]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) tile_update<M, false>(ck, cs, g4, c_abs, sc[t], st[t], lim[t], okbits);
+      }
     }
     if (c + 1 < nch) stash((c + 1) & 1);
 #pragma unroll
