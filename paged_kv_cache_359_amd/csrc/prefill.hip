@@ -345,24 +345,16 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
         const uint2 hi = read_tr16(vl + 16 * PV + 32 * r);
         ck.vop[r] = __builtin_bit_cast(typename M::vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
-      if constexpr (MASKED) {
+      // Every tile of the wave takes part: in the unmasked loop all are active (a tile
+      // without columns computes on zero queries and is never stored), and in the masked
+      // loop a tile whose columns all precede the chunk gets -inf for every key, which
+      // leaves its state unchanged.  All score products are issued first, so that the
+      // matrix cores work on the later tiles while the earlier tiles' softmax runs.
+      float4_t sc[NT][2];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          if (cs <= lim_max[t]) {  // a tile whose columns all precede this chunk skips it
-            float4_t sc[2];
-            tile_scores<M>(ck, qop[t], sc);
-            tile_update<M, true>(ck, cs, g4, c_abs, sc, st[t], lim[t], okbits);
-          }
-      } else {
-        // Every tile of the wave is active here (a tile without columns computes on zero
-        // queries and is never stored).  All score products are issued first, so that the
-        // matrix cores work on the later tiles while the earlier tiles' softmax runs.
-        float4_t sc[NT][2];
+      for (int t = 0; t < NT; ++t) tile_scores<M>(ck, qop[t], sc[t]);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) tile_scores<M>(ck, qop[t], sc[t]);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) tile_update<M, false>(ck, cs, g4, c_abs, sc[t], st[t], lim[t], okbits);
-      }
+      for (int t = 0; t < NT; ++t) tile_update<M, MASKED>(ck, cs, g4, c_abs, sc[t], st[t], lim[t], okbits);
     }
     if (c + 1 < nch) stash((c + 1) & 1);
 #pragma unroll
