@@ -70,7 +70,9 @@ __device__ __forceinline__ void tile_scores(const typename M::Chunk& ck,
   }
 }
 
-template <typename M, bool MASKED>
+// F16PV (bf16 only): the chunk's V rows were staged in LDS as fp16, and the probabilities go
+// into an fp16 product as well (11 significant bits, no remainder product).
+template <typename M, bool MASKED, bool F16PV>
 __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs, int g4, float c,
                                             const float4_t (&s)[2], typename M::State& st, int lim,
                                             uint32_t okbits) {
@@ -109,6 +111,16 @@ __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs,
 #pragma unroll
   for (int j = 0; j < 8; ++j) p[j] = exp2_hw(e[j]);
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  if constexpr (M::SPLIT_P && F16PV) {
+    half8_t ph;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ph[j] = _Float16(p[j]);
+#pragma unroll
+    for (int r = 0; r < M::E; ++r)
+      st.acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ck.vop[r]), ph,
+                                                          st.acc[r], 0, 0, 0);
+    return;
+  }
   typename M::vec8 phi, plo;
   if constexpr (M::SPLIT_P) {
     // Pairs: one packed conversion gives both high parts; each reads back as fp32 by a
@@ -179,7 +191,6 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   int lim[NT], lim_min[NT], lim_max[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    M::init(st[t]);
     const int jt = j0 + 16 * t;
     const bool col = 16 * t + n16 < nq;
     lim[t] = col ? first + jt + n16 : -1;
@@ -277,22 +288,44 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
       }
     }
   };
-  auto stash = [&](int buf) {
+  // F16PV: V rows go to LDS as fp16 (round to nearest; exact for bf16 values below 2^16
+  // in magnitude, and larger ones become inf).
+  auto stash = [&](int buf, auto f16pv) {
+    constexpr bool F16PV = decltype(f16pv)::value;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int v = tid + 256 * k;
       const int row = v / VECS, col = v % VECS;
       const int off = row < CH ? row * PK : VBASE + (row - CH) * PV;
-      *reinterpret_cast<uint4*>(&lds[buf][off + col * 16]) = pre[k];
+      uint4 w = pre[k];
+      if constexpr (F16PV) {
+        if (row >= CH) {
+          uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const half2_t hv = {_Float16(__builtin_bit_cast(float, x[q] << 16)),
+                                _Float16(__builtin_bit_cast(float, x[q] & 0xFFFF0000u))};
+            x[q] = __builtin_bit_cast(uint32_t, hv);
+          }
+          w = make_uint4(x[0], x[1], x[2], x[3]);
+        }
+      }
+      *reinterpret_cast<uint4*>(&lds[buf][off + col * 16]) = w;
     }
   };
 
+  // The whole walk over the chunks, with fresh tile states.  F16PV (bf16 only) stages V as
+  // fp16 and takes the fp16 product for P.V.
+  auto run = [&](auto f16pv) {
+  constexpr bool F16PV = decltype(f16pv)::value;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) M::init(st[t]);
   int ids_cur[NB], ids_next[NB], ids_after[NB];
   if (nch > 0) {
     load_ids(0, ids_cur);
     load_ids(CH, ids_next);
     fetch(0, ids_cur);
-    stash(0);
+    stash(0, f16pv);
   }
   __syncthreads();
   // One chunk: prefetch the next chunk's rows and the block ids two ahead, update the tiles
@@ -354,9 +387,10 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) tile_scores<M>(ck, qop[t], sc[t]);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) tile_update<M, MASKED>(ck, cs, g4, c_abs, sc[t], st[t], lim[t], okbits);
+      for (int t = 0; t < NT; ++t)
+        tile_update<M, MASKED, F16PV>(ck, cs, g4, c_abs, sc[t], st[t], lim[t], okbits);
     }
-    if (c + 1 < nch) stash((c + 1) & 1);
+    if (c + 1 < nch) stash((c + 1) & 1, f16pv);
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       ids_cur[k] = ids_next[k];
@@ -368,7 +402,10 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   // every column's causal limit and inside the context, so they need no masking unless a
   // table entry is outside the pool; the first such entry ends the unmasked loop.  The rest
   // (the diagonal chunks and the context's tail) take the masked form.
-  const int n_plain = min(nch, max(0, (first + jw + 1) / CH));
+  // The exact bf16 walk runs only after an fp16 walk ended non-finite: it keeps to the
+  // masked loop, which handles every chunk, so that its copy of the code stays small.
+  constexpr bool PLAIN_LOOP = !(DT == DT_BF16 && !F16PV);
+  const int n_plain = PLAIN_LOOP ? min(nch, max(0, (first + jw + 1) / CH)) : 0;
   int c = 0;
   for (; c < n_plain; ++c) {
     bool bad = false;
@@ -378,6 +415,31 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
     step(c, std::false_type{});
   }
   for (; c < nch; ++c) step(c, std::true_type{});
+  };
+
+  if constexpr (DT == DT_BF16) {
+    // The fp16 product first.  A V value of 2^16 or more in magnitude becomes inf in fp16,
+    // and an inf in any V row the walk stages makes an accumulator of every column it meets
+    // inf or NaN (0 * inf is NaN), so a finite result means fp16 staging was exact.  If
+    // any column of the workgroup ends non-finite, the workgroup walks the keys again with
+    // V in bf16 and P split into two bf16 products, the exact form; a V that really holds
+    // inf or NaN gives the same non-finite result there.
+    __shared__ int redo;
+    if (tid == 0) redo = 0;
+    run(std::true_type{});
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < M::E; ++r)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bad |= !__builtin_isfinite(st[t].acc[r][v]);
+    if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) redo = 1;
+    __syncthreads();
+    if (redo) run(std::false_type{});
+  } else {
+    run(std::false_type{});
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     st[t].l = xor_sum_16_32(st[t].l);

@@ -117,6 +117,32 @@ def test_prefill_invalid_table_entries():
                 check(out[int(qs[b]) + i, h], r, c.dtype, f"b={b} row {i} h={h}")
 
 
+def test_prefill_bf16_values_beyond_fp16_range():
+    """bf16 kernels stage V as fp16 for the probability product and re-run a workgroup in
+    the exact bf16 form when a V value of 2^16 or more made its result non-finite.  Here: a
+    huge value in a key every row attends, one in a key only later rows attend (masked for
+    the earlier rows, so their 0 * inf must not leak), and one in an unused slot past the
+    context (never read)."""
+    w, g, o = both("prefill_chunked_gqa", batch=2, lengths=("fixed", (300, 700)),
+                   new_tokens=("fixed", 140), num_blocks=80, dtype="bf16")
+    c = w.cfg
+    bs = c.block_size
+    tables, lens = o.tables()
+
+    def put(b, pos, head, d, value):
+        blk, off = int(tables[b][pos // bs]), pos % bs
+        t = torch.tensor([value], dtype=torch.bfloat16)
+        g.v_cache[blk, head, off, d] = t.to(g.v_cache.device)[0]
+        o.v_pool[blk, head, off, d] = oracle.bits_of(t, "bf16")[0]
+
+    put(0, 10, 3, 5, 3.0e5)                        # attended by every row of sequence 0
+    put(1, 700 - 140 + 20, 0, 100, -2.5e5)         # only rows 20.. of sequence 1 see it
+    put(1, 700 + 2, 1, 7, 1.0e6)                   # past the context, inside the last block
+    out = g.prefill().double().cpu().numpy()
+    err = check(out, o.prefill(), "bf16", "V beyond the fp16 range")
+    print(f"  max abs err {err:.3g}", flush=True)
+
+
 def test_prefill_matches_decode_kernel_on_the_last_row():
     """The newest row of a prefill and a decode of that sequence read the same keys."""
     w, g, o = both("prefill_chunked_gqa", batch=2, lengths=("fixed", (300, 77)), num_blocks=80)
