@@ -152,9 +152,23 @@ __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs,
 constexpr int kPrefillTiles = 2;  // 16-column tiles per wave
 constexpr int kPrefillRows = 4 * 16 * kPrefillTiles;  // new tokens per workgroup
 
-template <int DT, int D, int BS>
+// Kernel forms.  kExact: P.V in the cache's type (bf16 with P split into two products).
+// kFast (bf16 only): V staged in LDS as fp16 (round to nearest: exact for bf16 values below
+// 2^16 in magnitude; larger ones become inf) and P.V as one fp16 product.  An inf in any V
+// row the walk stages makes an accumulator of every column it meets inf or NaN (0 * inf is
+// NaN), so when every column of the workgroup ends finite the fp16 staging was exact and
+// the outputs are stored; otherwise the workgroup stores only a NaN in element 0 of its
+// first row.  kFixup (bf16 only, launched after kFast over the same grid): a workgroup
+// whose element 0 of its first row is finite returns at once; any other walks its keys in
+// the exact form and stores them (a V that really holds inf or NaN gives the same
+// non-finite result there).  The exact walk lives in a kernel of its own because, inlined
+// after the fast one, it made the usual walk 5% slower.
+enum { kExact = 0, kFast = 1, kFixup = 2 };
+
+template <int DT, int D, int BS, int MODE>
 __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   using M = Mfma<DT, D, BS>;
+  static_assert(MODE == kExact || DT == DT_BF16, "the fp16 form is for bf16 caches");
   constexpr int NT = kPrefillTiles;
   constexpr int CH = kMfmaChunk;
   // LDS bytes per K row and per V row, padded so that the waves' reads spread over the banks
@@ -179,6 +193,13 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   const int jw = blockIdx.y * kPrefillRows;  // first new token of the workgroup
   // Uniform over the workgroup, so returning here skips no barrier another wave waits at.
   if (r0 < 0 || n <= 0 || jw >= n || r0 + jw >= a.num_tokens) return;
+  const size_t mark = (size_t(r0 + jw) * a.num_q_heads + h) * D;  // element 0 of the first row
+  if constexpr (MODE == kFixup) {
+    const uint32_t bits = static_cast<const uint16_t*>(a.out)[mark];
+    const float x = DT == DT_BF16 ? __builtin_bit_cast(float, bits << 16)
+                                  : float(__builtin_bit_cast(_Float16, uint16_t(bits)));
+    if (__builtin_isfinite(x)) return;  // same element for every thread: uniform
+  }
   const int nw = min(min(kPrefillRows, n - jw), a.num_tokens - r0 - jw);  // rows of the workgroup
   const int ctx = clamp_ctx(a, b);
   const int first = ctx - n;                           // position of new token 0
@@ -402,10 +423,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   // every column's causal limit and inside the context, so they need no masking unless a
   // table entry is outside the pool; the first such entry ends the unmasked loop.  The rest
   // (the diagonal chunks and the context's tail) take the masked form.
-  // The exact bf16 walk runs only after an fp16 walk ended non-finite: it keeps to the
-  // masked loop, which handles every chunk, so that its copy of the code stays small.
-  constexpr bool PLAIN_LOOP = !(DT == DT_BF16 && !F16PV);
-  const int n_plain = PLAIN_LOOP ? min(nch, max(0, (first + jw + 1) / CH)) : 0;
+  const int n_plain = min(nch, max(0, (first + jw + 1) / CH));
   int c = 0;
   for (; c < n_plain; ++c) {
     bool bad = false;
@@ -417,13 +435,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   for (; c < nch; ++c) step(c, std::true_type{});
   };
 
-  if constexpr (DT == DT_BF16) {
-    // The fp16 product first.  A V value of 2^16 or more in magnitude becomes inf in fp16,
-    // and an inf in any V row the walk stages makes an accumulator of every column it meets
-    // inf or NaN (0 * inf is NaN), so a finite result means fp16 staging was exact.  If
-    // any column of the workgroup ends non-finite, the workgroup walks the keys again with
-    // V in bf16 and P split into two bf16 products, the exact form; a V that really holds
-    // inf or NaN gives the same non-finite result there.
+  if constexpr (MODE == kFast) {
     __shared__ int redo;
     if (tid == 0) redo = 0;
     run(std::true_type{});
@@ -436,7 +448,10 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
         for (int v = 0; v < 4; ++v) bad |= !__builtin_isfinite(st[t].acc[r][v]);
     if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) redo = 1;
     __syncthreads();
-    if (redo) run(std::false_type{});
+    if (redo) {  // uniform: leave the workgroup to the exact form
+      if (tid == 0) static_cast<uint16_t*>(a.out)[mark] = DT == DT_BF16 ? 0x7FC0u : 0x7E00u;
+      return;
+    }
   } else {
     run(std::false_type{});
   }
@@ -465,21 +480,33 @@ using namespace pkv;
 
 typedef void (*kernel_fn)(DecodeArgs);
 
-template <int DT, int D>
-kernel_fn pick_prefill_bs(int bs) {
-  switch (bs) {
-    case 8: return prefill_mfma<DT, D, 8>;
-    case 16: return prefill_mfma<DT, D, 16>;
-    case 32: return prefill_mfma<DT, D, 32>;
-  }
-  return nullptr;
+// The kernels of one call: fp16 caches run kExact alone; bf16 caches run kFast, then
+// kFixup over the same grid.
+struct PrefillKernels {
+  kernel_fn first = nullptr, second = nullptr;
+};
+
+template <int DT, int D, int BS>
+PrefillKernels prefill_pair() {
+  if constexpr (DT == DT_BF16) return {prefill_mfma<DT, D, BS, kFast>, prefill_mfma<DT, D, BS, kFixup>};
+  else return {prefill_mfma<DT, D, BS, kExact>, nullptr};
 }
 
-kernel_fn pick_prefill(pkv_dtype dt, int d, int bs) {
-  if (dt == PKV_F32) return nullptr;
+template <int DT, int D>
+PrefillKernels pick_prefill_bs(int bs) {
+  switch (bs) {
+    case 8: return prefill_pair<DT, D, 8>();
+    case 16: return prefill_pair<DT, D, 16>();
+    case 32: return prefill_pair<DT, D, 32>();
+  }
+  return {};
+}
+
+PrefillKernels pick_prefill(pkv_dtype dt, int d, int bs) {
+  if (dt == PKV_F32) return {};
   if (d == 64) return dt == PKV_F16 ? pick_prefill_bs<DT_F16, 64>(bs) : pick_prefill_bs<DT_BF16, 64>(bs);
   if (d == 128) return dt == PKV_F16 ? pick_prefill_bs<DT_F16, 128>(bs) : pick_prefill_bs<DT_BF16, 128>(bs);
-  return nullptr;
+  return {};
 }
 
 }  // namespace
@@ -500,8 +527,8 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   if (num_q_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
   if (!valid_dtype(dtype)) return PKV_ERR_INVALID_ARG;
   if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
-  kernel_fn k = pick_prefill(dtype, head_dim, block_size);
-  if (!k) return PKV_ERR_UNSUPPORTED;
+  const PrefillKernels k = pick_prefill(dtype, head_dim, block_size);
+  if (!k.first) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
   if (num_seqs > 65535 || (int64_t(max_query_len) + kPrefillRows - 1) / kPrefillRows > 65535)
     return PKV_ERR_UNSUPPORTED;
@@ -529,8 +556,13 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   const dim3 grid{unsigned(num_q_heads), unsigned((max_query_len + kPrefillRows - 1) / kPrefillRows),
                   unsigned(num_seqs)};
   clear_stale_error();
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
-  return launch_status("paged_attention_prefill");
+  hipLaunchKernelGGL(k.first, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  if (launch_status("paged_attention_prefill") != PKV_OK) return PKV_ERR_HIP;
+  if (k.second) {
+    hipLaunchKernelGGL(k.second, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+    return launch_status("paged_attention_prefill (exact fix-up)");
+  }
+  return PKV_OK;
 }
 
 }  // extern "C"
