@@ -318,12 +318,23 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
 // =========================================================================================
 // Partition merge: out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p, for
-// (sequence, head) pairs whose context spans more than one partition.  One workgroup per
-// (head, sequence); one thread per output element.
+// (sequence, head) pairs whose context spans more than one partition.  One workgroup of
+// kReduceThreads per (head, sequence).  The threads first take the maximum over the
+// partitions together, then, kReducePass partitions at a time, put each partition's weight
+// 2^(m_p - M) and weighted l_p in LDS; thread d then sums o_p[d] times its weight over the
+// pass with independent loads in flight.
 // =========================================================================================
+constexpr int kReduceThreads = 128;
+constexpr int kReducePass = 256;
+
 template <int DT, int D>
-__global__ __launch_bounds__(128) void reduce_partitions(DecodeArgs a) {
+__global__ __launch_bounds__(kReduceThreads) void reduce_partitions(DecodeArgs a) {
+  static_assert(D <= kReduceThreads, "one thread per output element");
+  __shared__ float s_w[kReducePass];
+  __shared__ float s_lw[kReducePass];
+  __shared__ float s_max[kReduceThreads / 64];
   const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
   const int ctx_all = clamp_ctx(a, b);
   const int sk = skipped_blocks(a, b, ctx_all, a.block_size);
   const int ctx = ctx_all - sk * a.block_size;
@@ -334,18 +345,33 @@ __global__ __launch_bounds__(128) void reduce_partitions(DecodeArgs a) {
   if (!a.partials_only && p1 - p0 <= 1) return;  // a single partition wrote the output itself
   const size_t base = (size_t(b) * a.num_q_heads + h) * a.max_parts;
   float M = kNegInf;
-  for (int p = p0; p < p1; ++p) M = fmaxf(M, a.part_m[base + p]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float L = 0.f, O = 0.f;
-    if (M != kNegInf) {
-      for (int p = p0; p < p1; ++p) {
-        const float w = exp2_hw(a.part_m[base + p] - M);
-        L += a.part_l[base + p] * w;
-        O += a.part_o[(base + p) * D + d] * w;
+  for (int p = p0 + tid; p < p1; p += kReduceThreads) M = fmaxf(M, a.part_m[base + p]);
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) M = fmaxf(M, __shfl_xor(M, sh, 64));
+  if ((tid & 63) == 0) s_max[tid >> 6] = M;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kReduceThreads / 64; ++w) M = fmaxf(M, s_max[w]);
+  float L = 0.f, O = 0.f;
+  const float* po = a.part_o + base * D + tid;
+  for (int c0 = p0; c0 < p1; c0 += kReducePass) {
+    const int n = min(kReducePass, p1 - c0);
+    __syncthreads();  // the previous pass's weights have been read
+    for (int i = tid; i < n; i += kReduceThreads) {
+      const float w = M == kNegInf ? 0.f : exp2_hw(a.part_m[base + c0 + i] - M);
+      s_w[i] = w;
+      s_lw[i] = a.part_l[base + c0 + i] * w;
+    }
+    __syncthreads();
+    if (tid < D) {
+#pragma unroll 8
+      for (int i = 0; i < n; ++i) {
+        L += s_lw[i];
+        O += po[size_t(c0 + i) * D] * s_w[i];
       }
     }
-    store_elt<DT>(a.out, (size_t(b) * a.num_q_heads + h) * D + d, L > 0.f ? O / L : 0.f);
   }
+  if (tid < D) store_elt<DT>(a.out, (size_t(b) * a.num_q_heads + h) * D + tid, L > 0.f ? O / L : 0.f);
 }
 
 // =========================================================================================
@@ -656,7 +682,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
   hipLaunchKernelGGL(k, grid, dim3(mfma ? 256 : 64 * kValuWaves), 0, st, a);
   if (launch_status("paged_attention_decode") != PKV_OK) return PKV_ERR_HIP;
   if (max_parts > 1) {
-    hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(128), 0, st, a);
+    hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(kReduceThreads), 0, st, a);
     return launch_status("reduce_partitions");
   }
   return PKV_OK;
@@ -754,7 +780,7 @@ pkv_status pkv_paged_attention_cascade(void* out, const void* q, const void* k_c
   hipLaunchKernelGGL(k, dim3(unsigned(rows), unsigned(slots - 1), unsigned(num_seqs)),
                      dim3(mfma ? 256 : 64 * kValuWaves), 0, st, a);
   if (launch_status("paged_attention_decode") != PKV_OK) return PKV_ERR_HIP;
-  hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(kReduceThreads), 0, st, a);
   return launch_status("reduce_partitions");
 }
 
