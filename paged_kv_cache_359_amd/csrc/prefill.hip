@@ -9,8 +9,8 @@
 namespace pkv {
 
 // =========================================================================================
-// Prefill: one workgroup of 4 waves per (query head, 64 * NT consecutive new tokens,
-// sequence); wave w takes NT tiles of 16 new tokens each as the columns of the MFMA inner
+// Prefill: one workgroup of 4 waves per (query head, sequence, 64 * NT consecutive new
+// tokens); wave w takes NT tiles of 16 new tokens each as the columns of the MFMA inner
 // loop.  With the accumulators in VGPRs, two tiles per wave (each loaded chunk serves 32
 // columns) still fit two waves per SIMD.  Sequence b's new tokens are q rows
 // query_start[b] .. query_start[b+1]; with ctx_b tokens cached (the new ones included), new
@@ -182,15 +182,18 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   static_assert(PER * 256 == 2 * CH * VECS, "chunk must split evenly over the workgroup");
   __shared__ __attribute__((aligned(16))) char lds[2][BUF];
 
+  // Grid: (query head, sequence, row tile), the row tiles in reverse: the last tiles of the
+  // sequences, which walk the most keys, are dispatched first and the short ones fill in
+  // behind them.
   const int h = blockIdx.x;
-  const int b = blockIdx.z;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int n16 = lane & 15, g4 = lane >> 4;
   const int r0 = a.query_start[b];
   const int n = a.query_start[b + 1] - r0;
-  const int jw = blockIdx.y * kPrefillRows;  // first new token of the workgroup
+  const int jw = int(gridDim.z - 1 - blockIdx.z) * kPrefillRows;  // first new token of the workgroup
   // Uniform over the workgroup, so returning here skips no barrier another wave waits at.
   if (r0 < 0 || n <= 0 || jw >= n || r0 + jw >= a.num_tokens) return;
   const size_t mark = (size_t(r0 + jw) * a.num_q_heads + h) * D;  // element 0 of the first row
@@ -553,8 +556,8 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   a.max_blocks = max_blocks_per_seq;
   a.ctx_limit = int32_t(max_context_len < cap ? max_context_len : cap);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid{unsigned(num_q_heads), unsigned((max_query_len + kPrefillRows - 1) / kPrefillRows),
-                  unsigned(num_seqs)};
+  const dim3 grid{unsigned(num_q_heads), unsigned(num_seqs),
+                  unsigned((max_query_len + kPrefillRows - 1) / kPrefillRows)};
   clear_stale_error();
   hipLaunchKernelGGL(k.first, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
   if (launch_status("paged_attention_prefill") != PKV_OK) return PKV_ERR_HIP;
