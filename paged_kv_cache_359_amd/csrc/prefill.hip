@@ -150,7 +150,9 @@ __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs,
 }
 
 constexpr int kPrefillTiles = 2;  // 16-column tiles per wave
-constexpr int kPrefillRows = 4 * 16 * kPrefillTiles;  // new tokens per workgroup
+constexpr int kPrefillWaves = 4;  // waves per workgroup
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
+constexpr int kPrefillRows = kPrefillWaves * 16 * kPrefillTiles;  // new tokens per workgroup
 
 // Kernel forms.  kExact: P.V in the cache's type (bf16 with P split into two products).
 // kFast (bf16 only): V staged in LDS as fp16 (round to nearest: exact for bf16 values below
@@ -166,7 +168,7 @@ constexpr int kPrefillRows = 4 * 16 * kPrefillTiles;  // new tokens per workgrou
 enum { kExact = 0, kFast = 1, kFixup = 2 };
 
 template <int DT, int D, int BS, int MODE>
-__global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   using M = Mfma<DT, D, BS>;
   static_assert(MODE == kExact || DT == DT_BF16, "the fp16 form is for bf16 caches");
   constexpr int NT = kPrefillTiles;
@@ -180,8 +182,8 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   constexpr int VBASE = CH * PK;            // V rows follow the K rows in a buffer
   constexpr int BUF = CH * PK + CH * PV;
   constexpr int VECS = D * 2 / 16;          // 16-byte vectors per row
-  constexpr int PER = 2 * CH * VECS / 256;  // vectors each thread moves per chunk
-  static_assert(PER * 256 == 2 * CH * VECS, "chunk must split evenly over the workgroup");
+  constexpr int PER = 2 * CH * VECS / kPrefillThreads;  // vectors each thread moves per chunk
+  static_assert(PER * kPrefillThreads == 2 * CH * VECS, "chunk must split evenly over the workgroup");
   __shared__ __attribute__((aligned(16))) char lds[2][BUF];
 
   // Grid: (query head, sequence, row tile), the row tiles in reverse: the last tiles of the
@@ -281,28 +283,32 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
   // column v % VECS.  Rows in blocks outside the pool are zero, and so are V rows of tokens
   // past t1.
   uint4 pre[PER];
-  // The 256 threads cover 256 / VECS rows per vector k.  When those rows lie in one block
-  // (whole 16-row groups and blocks of at least 16 tokens), the block id is wave-uniform and
-  // each load is a scalar base plus a per-lane offset.
-  constexpr int ROWS_PER_K = 256 / VECS;
-  constexpr bool UNIFORM_ROWS = ROWS_PER_K <= BS && CH % ROWS_PER_K == 0;
+  // The workgroup's threads cover ROWS_PER_K rows per vector k, a wave ROWS_PER_WAVE of
+  // them.  When a wave's rows lie in one block (blocks of at least ROWS_PER_WAVE tokens),
+  // the block id is wave-uniform and each load is a scalar base plus a per-lane offset; when
+  // all the workgroup's rows do, the id is even known at compile time.
+  constexpr int ROWS_PER_K = kPrefillThreads / VECS;
+  constexpr int ROWS_PER_WAVE = 64 / VECS;
+  constexpr bool UNIFORM_K = ROWS_PER_K <= BS && CH % ROWS_PER_K == 0;
+  constexpr bool UNIFORM_ROWS = ROWS_PER_WAVE <= BS && CH % ROWS_PER_WAVE == 0;
   auto fetch = [&](int cs, const int (&ids)[NB]) {
     const bool tail = cs + CH > t1;  // wave-uniform: some row of the chunk is past t1
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int v = tid + 256 * k;
+      const int v = tid + kPrefillThreads * k;
       const int row = v / VECS, col = v % VECS;
       const int off = row % CH;
       const uint32_t lane_off = uint32_t((off % BS) * D * 2 + col * 16);
       if constexpr (UNIFORM_ROWS) {
-        // One block for the vector's rows, all K or all V: a scalar base plus the lane's
+        // One block for the wave's rows, all K or all V: a scalar base plus the lane's
         // offset.  A block outside the pool is read as block 0 and zeroed.  Rows past t1
         // inside a real block are read (they lie in the pool): their keys get -inf scores
         // in the masked tile update, and their values are zeroed, since 0 * garbage may be
         // NaN.  Both zeroings are rare and sit behind a branch, so the usual chunk issues
         // its loads and nothing else.
-        const bool is_v = ROWS_PER_K * k >= CH;
-        const int id = ids[((ROWS_PER_K * k) % CH) / BS];
+        const int row0 = UNIFORM_K ? ROWS_PER_K * k : (64 * wave + kPrefillThreads * k) / VECS;
+        const bool is_v = row0 >= CH;
+        const int id = UNIFORM_K ? ids[(row0 % CH) / BS] : id_of(ids, row0 % CH);
         const bool valid = (unsigned)id < (unsigned)a.num_blocks;
         pre[k] = load_cached((is_v ? vb : kb) + size_t(valid ? id : 0) * blk_bytes + lane_off);
         if (!valid || (is_v && tail && cs + off >= t1)) pre[k] = make_uint4(0, 0, 0, 0);
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(256) void prefill_mfma(DecodeArgs a) {
     constexpr bool F16PV = decltype(f16pv)::value;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int v = tid + 256 * k;
+      const int v = tid + kPrefillThreads * k;
       const int row = v / VECS, col = v % VECS;
       const int off = row < CH ? row * PK : VBASE + (row - CH) * PV;
       uint4 w = pre[k];
@@ -561,10 +567,10 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   const dim3 grid{unsigned(num_q_heads), unsigned(num_seqs),
                   unsigned((max_query_len + kPrefillRows - 1) / kPrefillRows)};
   clear_stale_error();
-  hipLaunchKernelGGL(k.first, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(k.first, grid, dim3(kPrefillThreads), 0, static_cast<hipStream_t>(stream), a);
   if (launch_status("paged_attention_prefill") != PKV_OK) return PKV_ERR_HIP;
   if (k.second) {
-    hipLaunchKernelGGL(k.second, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+    hipLaunchKernelGGL(k.second, grid, dim3(kPrefillThreads), 0, static_cast<hipStream_t>(stream), a);
     return launch_status("paged_attention_prefill (exact fix-up)");
   }
   return PKV_OK;
