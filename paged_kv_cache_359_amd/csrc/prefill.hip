@@ -414,10 +414,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
       // without columns computes on zero queries and is never stored), and in the masked
       // loop a tile whose columns all precede the chunk gets -inf for every key, which
       // leaves its state unchanged.  All score products are issued first, so that the
-      // matrix cores work on the later tiles while the earlier tiles' softmax runs.
+      // matrix cores work on the later tiles while the earlier tiles' softmax runs.  The
+      // wave raises its priority while it issues them, so that it gets the issue slots
+      // ahead of the other wave on the SIMD, whose softmax can then run beside these
+      // products (measured: 4% on long walks, no change on short ones).
       float4_t sc[NT][2];
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int t = 0; t < NT; ++t) tile_scores<M>(ck, qop[t], sc[t]);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         tile_update<M, MASKED, F16PV>(ck, cs, g4, c_abs, sc[t], st[t], lim[t], okbits);
