@@ -226,9 +226,13 @@ def cpu_baseline(w, budget_s):
     c = w.cfg
     q_bits = oracle.bits_of(w.q[0].cpu(), c.dtype)
 
+    built = {}
+
     def build(nseq):
-        nb = sum(-(-int(w.lengths[b]) // c.block_size) for b in range(nseq)) + 1
+        # One spare block per sequence, for the append step timed below.
+        nb = sum(-(-int(w.lengths[b]) // c.block_size) for b in range(nseq)) + 1 + nseq
         a = oracle.OracleAllocator(nb, c.block_size)
+        built["alloc"] = a
         kp = oracle.new_pool(nb, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
         vp = oracle.new_pool(nb, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
         for b in range(nseq):
@@ -262,12 +266,37 @@ def cpu_baseline(w, budget_s):
     tokens = int(np.sum(w.lengths[:nseq]))
     kv_bytes = 2 * c.num_kv_heads * c.head_dim * c.dsize * tokens
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(kv_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "seconds_per_run": round(dt, 3), "runs": len(times),
-            "tokens_per_s": round(nseq / dt, 3),
-            "sample": f"fp64 oracle decode (gather + two-pass softmax) of the first {nseq} of "
-                      f"{w.batch} sequences at the first step ({tokens} context tokens, "
-                      f"{c.num_q_heads} heads), median of {len(times)} runs"}
+    res = {"value": round(kv_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+           "kind": "oracle", "seconds_per_run": round(dt, 3), "runs": len(times),
+           "tokens_per_s": round(nseq / dt, 3),
+           "sample": f"fp64 oracle decode (gather + two-pass softmax) of the first {nseq} of "
+                     f"{w.batch} sequences at the first step ({tokens} context tokens, "
+                     f"{c.num_q_heads} heads), median of {len(times)} runs"}
+    if c.steps >= 2:
+        # The next step's host side on the same sample: the oracle allocator appends one token
+        # per sequence (slot, new block or copy-on-write), then its block copies and cache
+        # write store the new tokens' K/V.
+        kp, vp = args[0], args[1]
+        nxt = [w.token_kv(b, int(w.lengths[b]), int(w.lengths[b]) + 1) for b in range(nseq)]
+        kb = oracle.bits_of(torch_cat([k for k, _ in nxt]).cpu(), c.dtype)
+        vb = oracle.bits_of(torch_cat([v for _, v in nxt]).cpu(), c.dtype)
+        t = time.perf_counter()
+        slots, pairs = built["alloc"].append(range(nseq))
+        if pairs:
+            oracle.copy_blocks(kp, pairs)
+            oracle.copy_blocks(vp, pairs)
+        oracle.cache_write(kp, kb, slots)
+        oracle.cache_write(vp, vb, slots)
+        dt_app = time.perf_counter() - t
+        res["append_step"] = {"seconds": round(dt_app, 6), "tokens_per_s": round(nseq / dt_app, 1),
+                              "sample": f"oracle append + block copies + cache write of one new "
+                                        f"token for each of the {nseq} sequences"}
+    return res
+
+
+def torch_cat(ts):
+    import torch
+    return torch.cat(ts)
 
 
 def _grow_sample(build, run, limit, budget_s, start=1):
@@ -298,9 +327,13 @@ def cpu_baseline_prefill(w, budget_s):
     qs = w.query_start
     q_bits = oracle.bits_of(w.q.cpu(), c.dtype)
 
+    built = {}
+
     def build(nseq):
-        nb = sum(-(-int(w.lengths[b]) // c.block_size) for b in range(nseq)) + 1
+        # One spare block per sequence, for the append step timed below.
+        nb = sum(-(-int(w.lengths[b]) // c.block_size) for b in range(nseq)) + 1 + nseq
         a = oracle.OracleAllocator(nb, c.block_size)
+        built["alloc"] = a
         kp = oracle.new_pool(nb, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
         vp = oracle.new_pool(nb, c.num_kv_heads, c.block_size, c.head_dim, c.dtype)
         for b in range(nseq):
