@@ -229,3 +229,16 @@ def test_device_table_updates_track_the_allocator(name, overrides):
         th, lh = g.alloc.pkv_get_block_tables(list(range(B)), mb)
         assert np.array_equal(tables.cpu().numpy(), th)
         assert np.array_equal(lens.cpu().numpy(), lh)
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("gqa_long", dict(batch=2, lengths=("fixed", (4100, 999)), num_blocks=400)),
+    ("llama7b", dict(batch=2, lengths=("fixed", (4300, 77)), num_blocks=400, num_q_heads=4,
+                     num_kv_heads=4)),
+])
+def test_merge_over_many_partitions(name, overrides):
+    """More partitions than the merge stages at once (256): 16-token partitions of a
+    4100-token context give 257 (m, l, o) triples per (sequence, head), merged in two passes."""
+    w, g, o = both(name, **overrides)
+    check_structures(w, g, o)
+    check_decode(w, g, o, [16, 32, 512])
