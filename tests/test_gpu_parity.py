@@ -81,7 +81,7 @@ for dtype in ("f32", "f16", "bf16"):
 for dtype in ("f16", "bf16"):
     for d in (64, 128):
         for bs in (4, 8, 16, 32):
-            for hq, hkv in ((8, 4), (8, 1), (16, 2), (32, 1)):
+            for hq, hkv in ((8, 4), (8, 1), (16, 2), (32, 1), (12, 4)):
                 SHAPES.append((dtype, d, bs, hq, hkv))
 SHAPES += [("f32", 128, 16, 8, 2), ("f32", 8, 4, 4, 1)]
 

@@ -58,7 +58,7 @@ SHAPES = []
 for dtype in ("f16", "bf16"):
     for d in (64, 128):
         for bs in (8, 16, 32):
-            for hq, hkv in ((4, 4), (8, 2), (16, 1)):
+            for hq, hkv in ((4, 4), (8, 2), (16, 1), (6, 2)):
                 SHAPES.append((dtype, d, bs, hq, hkv))
 
 
