@@ -242,3 +242,27 @@ def test_merge_over_many_partitions(name, overrides):
     w, g, o = both(name, **overrides)
     check_structures(w, g, o)
     check_decode(w, g, o, [16, 32, 512])
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("gqa_long", dict(batch=3, lengths=("fixed", (2100, 999, 37)), num_blocks=300)),
+    ("llama7b", dict(batch=4, num_blocks=700, num_q_heads=4, num_kv_heads=4)),
+])
+def test_max_context_len_bound(name, overrides):
+    """max_context_len is an upper bound that sizes the launch: a loose bound (the automatic
+    split then plans for longer contexts) gives the same attention; a bound below some
+    lengths clamps those sequences to their first max_context_len tokens."""
+    w, g, o = both(name, **overrides)
+    dt = w.cfg.dtype
+    tables, lens = o.tables()
+    ref = o.decode()
+    for p in (-1, 0, 64):
+        out = g.decode(partition_size=p, max_ctx=4 * int(lens.max())).double().cpu().numpy()
+        check(out, ref, dt, f"loose bound, partition {p}")
+    cut = int(np.sort(lens)[len(lens) // 2])
+    lens_cut = np.minimum(lens, cut).astype(np.int32)
+    ref_cut = oracle.decode(oracle.bits_of(w.q[0].cpu(), dt), o.k_pool, o.v_pool, tables,
+                            lens_cut, w.cfg.scale, dt)
+    for p in (-1, 0, 64):
+        out = g.decode(partition_size=p, max_ctx=cut).double().cpu().numpy()
+        check(out, ref_cut, dt, f"bound {cut} below some lengths, partition {p}")
