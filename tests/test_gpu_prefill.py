@@ -189,3 +189,16 @@ def test_prefill_full_size_sampled(name):
         err = check(out[qs[b] + i, h].double().cpu().numpy(), ref, dt, f"b={b} i={i} h={h}")
         worst = max(worst, err)
     print(f"  worst sampled max abs err {worst:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("bound", [1, 4, 40])
+def test_prefill_loose_query_bound(bound):
+    """max_query_len only sizes the launch: a bound above the longest chunk adds row tiles
+    (numbered from the end, so the real tiles move to other workgroups) and changes
+    nothing."""
+    w, g, o = both("prefill_chunked_gqa", batch=3, lengths=("fixed", (40, 513, 600)),
+                   new_tokens=("fixed", 33), num_blocks=160)
+    ref = o.prefill()
+    mq = int(np.max(np.diff(w.query_start)))
+    out = g.prefill(max_query_len=bound * mq + (bound > 1)).double().cpu().numpy()
+    check(out, ref, w.cfg.dtype, f"max_query_len {bound} x")
