@@ -1,18 +1,16 @@
 """Paged decode attention benchmark on one MI355X.
 
-One step = one pass of the whole paged decode path over the batch:
+One step = one pass of the whole paged decode path over the batch
+(``paged_kv_cache_359_amd.step.DecodeStep``):
   host: every sequence appends one token (C++ allocator: slot, new block or copy-on-write)
-  H2D:  slot mapping, block tables and context lengths (pinned, asynchronous)
-  GPU:  copy-on-write block copies (when any), reshape_and_cache of the new K/V, paged
-        decode attention, partition merge.
-Inputs (queries, the new tokens' K/V, the existing cache) are resident in HBM before timing.
-Each step runs on one stream; the device keeps the block tables and lengths, and a step
-uploads only one small packed buffer (the new slots, the positions they extend and the
-shared-prefix hint) that pkv_update_block_tables applies.  --overlap instead uploads whole
-tables on a second stream during the previous decode (four buffer sets); on some MI355X
-boxes the cross-stream waits stall for milliseconds, so it is not the default.  --check
-saves every step's output and afterwards re-decodes each step from the final tables on one
-stream, requiring bit-identical results.
+        into pinned buffers (slots, positions), plus the shared-prefix hint
+  GPU:  copy-on-write block copies (when any); pkv_append_and_cache, which reads the pinned
+        slots and positions in place, writes the new K/V into their slots and updates the
+        block tables and lengths kept on the device; paged decode attention and, when
+        contexts are split, the partition merge.
+Inputs (queries, the new tokens' K/V, the existing cache) are resident in HBM before timing;
+each step runs on one stream.  --check saves every step's output and afterwards re-decodes
+each step from the final tables, requiring bit-identical results.
 
 Prints one JSON line.  ``value`` is the whole step's logical KV throughput (bytes of K and V
 that the batch attends to, per second); ``roofline`` rates the decode kernels alone, timed
@@ -20,8 +18,11 @@ with HIP events on the stream they run on, and ``roofline.measured_read`` also a
 read rates a plain probe kernel reaches over a 4 GiB buffer on the same device (in address
 order, and in random order at one KV head's block slice); ``kernel_protocol`` times the decode call
 alone on the final state (10 warm-up and 100 timed calls, each between its own events, 1 GiB
-written and another 1 GiB read between calls to clear the caches; median); ``cpu_baseline`` times the fp64 CPU
-oracle on a bounded sample of the same batch.
+written and another 1 GiB read between calls to clear the caches; median); ``kv_memory``
+reports the allocator's use of the pool against a contiguous per-sequence reservation.  The
+CPU leg (skipped by --no-cpu-baseline) is the only part that runs the fp64 CPU oracle: it
+times it on a bounded sample of the same batch (``cpu_baseline``) and checks sampled
+sequences of the last timed step against it (``parity``).
 """
 from __future__ import annotations
 
@@ -165,9 +166,6 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cache-hint", action="store_true",
                     help="stream every block (no cached_blocks hint for shared prefixes)")
-    ap.add_argument("--overlap", action="store_true",
-                    help="run each step's uploads and cache write on a second stream during the "
-                         "previous step's decode (whole tables uploaded per step)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measured read ceilings and the kernel timing protocol that "
                          "follow the timed steps (profiling runs count the steps' launches only)")
@@ -219,6 +217,85 @@ def workload_desc(cfg, lengths):
     }
 
 
+def device_info(dev):
+    """The device the run measured: name, architecture, compute units, HBM size."""
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": int(p.multi_processor_count), "hbm_bytes": int(p.total_memory)}
+
+
+def seed_info(cfg):
+    return {"seed_sequence": 1000 + cfg.cfg_id,
+            "streams": "SeedSequence(seed_sequence).spawn(5): lengths, placement, q, k, v"}
+
+
+def kv_memory(alloc, ids, max_blocks, bs):
+    """How the allocator uses the block pool for the batch as it stands: tokens stored per
+    allocated slot (pkv_usage; a token of a shared block counts once per sequence that holds
+    it), the slots of referenced blocks that hold no token (each block counted once, filled
+    as far as its longest holder reaches), and the same tokens under contiguous
+    per-sequence reservation of the longest sequence's length (rounded up to a block), the
+    scheme paging replaces ("PagedAttention 与 vLLM 推理加速", §2.2 and §2.4)."""
+    tokens, slots = alloc.pkv_usage()
+    tables, lens = alloc.pkv_get_block_tables(ids, max_blocks)
+    cols = np.arange(tables.shape[1])[None, :]
+    used = np.clip(lens[:, None].astype(np.int64) - cols * bs, 0, bs)
+    held = used > 0
+    filled = np.zeros(int(tables[held].max()) + 1 if held.any() else 1, dtype=np.int64)
+    np.maximum.at(filled, tables[held], used[held])
+    unique = int(filled.sum())
+    prealloc = int(-(-int(lens.max()) // bs) * bs) if len(lens) else 0
+    contiguous = len(ids) * prealloc
+    return {"tokens_stored": int(tokens), "slots_allocated": int(slots),
+            "tokens_per_slot": round(tokens / max(slots, 1), 5),
+            "distinct_tokens": unique, "empty_slots": int(slots - unique),
+            "empty_frac": round((slots - unique) / max(slots, 1), 5),
+            "contiguous": {"slots_per_sequence": prealloc, "slots": contiguous,
+                           "tokens_per_slot": round(tokens / max(contiguous, 1), 5)}}
+
+
+def oracle_parity(w, out, step, token_budget=200_000, max_seqs=16):
+    """Sampled sequences (every head) of the GPU output of decode step ``step`` against the
+    oracle's definition: fp64 attention of the query over the sequence's contiguous K/V
+    tokens 0 .. len-1 as the workload drew them (no table, no pool: the GPU's result went
+    through both).  The shortest and the longest sequence, then seeded random ones while the
+    sampled context stays within ``token_budget`` tokens."""
+    import oracle
+    from oracle import tolerance as T
+    c = w.cfg
+    lens = w.lengths + step
+    order = np.argsort(lens, kind="stable")
+    pick = [int(order[0])] + ([int(order[-1])] if w.batch > 1 else [])
+    rng = np.random.default_rng(0)
+    for b in rng.permutation(w.batch):
+        if len(pick) >= max_seqs or sum(int(lens[p]) for p in pick) + int(lens[b]) > token_budget:
+            break
+        if int(b) not in pick:
+            pick.append(int(b))
+    q = oracle.to_f64(oracle.bits_of(w.q[step].cpu(), c.dtype), c.dtype)
+    got = out.double().cpu().numpy()
+    refs, outs = [], []
+    for b in pick:
+        k, v = w.token_kv(b, 0, int(lens[b]))
+        for g in range(c.num_kv_heads):
+            kk = oracle.to_f64(oracle.bits_of(k[:, g].cpu(), c.dtype), c.dtype)
+            vv = oracle.to_f64(oracle.bits_of(v[:, g].cpu(), c.dtype), c.dtype)
+            for h in range(g * c.group, (g + 1) * c.group):
+                refs.append(oracle.attention_contiguous(q[b, h], kk, vv, c.scale))
+                outs.append(got[b, h])
+    summ = T.summary(np.array(outs), np.array(refs), c.dtype)
+    summ.update({"step": int(step), "sequences": sorted(pick), "rows_checked": len(refs),
+                 "reference": "fp64 oracle: attention over each sampled sequence's contiguous "
+                              "K/V, every query head",
+                 "pass": bool(summ["excess"] <= 0.0)})
+    return summ
+
+
+def _cores():
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, budget_s):
     """The oracle, untouched, on the first sequences of the batch at the first step."""
     import oracle
@@ -266,7 +343,8 @@ def cpu_baseline(w, budget_s):
     tokens = int(np.sum(w.lengths[:nseq]))
     kv_bytes = 2 * c.num_kv_heads * c.head_dim * c.dsize * tokens
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    res = {"value": round(kv_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+    res = {"value": round(kv_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": _cores(),
+           "blas_threads": int(threads), "python_threads": 1,
            "kind": "oracle", "seconds_per_run": round(dt, 3), "runs": len(times),
            "tokens_per_s": round(nseq / dt, 3),
            "sample": f"fp64 oracle decode (gather + two-pass softmax) of the first {nseq} of "
@@ -353,7 +431,7 @@ def cpu_baseline_prefill(w, budget_s):
 
     nseq, dt, runs = _grow_sample(build, run, w.batch, budget_s)
     flops = prefill_flops(c, w.lengths[:nseq], w.n_new[:nseq])
-    return {"value": round(flops / dt / 1e12, 9), "unit": "TFLOP/s", "cores": _threads(),
+    return {"value": round(flops / dt / 1e12, 9), "unit": "TFLOP/s", "cores": _cores(), "blas_threads": _threads(),
             "kind": "oracle", "seconds_per_run": round(dt, 3), "runs": runs,
             "sample": f"fp64 oracle causal prefill (row by row) of the first {nseq} of {w.batch} "
                       f"sequences ({int(qs[nseq])} new tokens, {c.num_q_heads} heads), median of "
@@ -397,7 +475,7 @@ def cpu_baseline_swap(w, victims, budget_s):
     nv, dt, runs = _grow_sample(build, run, len(victims), budget_s)
     nblk = sum(-(-(int(w.lengths[v]) - 1) // bs) for v in victims[:nv])
     moved = 2 * nblk * c.num_kv_heads * bs * c.head_dim * c.dsize
-    return {"value": round(2 * moved / dt / 1e9, 6), "unit": "GB/s", "cores": _threads(),
+    return {"value": round(2 * moved / dt / 1e9, 6), "unit": "GB/s", "cores": _cores(), "blas_threads": _threads(),
             "kind": "oracle", "seconds_per_run": round(dt, 3), "runs": runs,
             "sample": f"oracle allocator swap-out/in with whole-block bit copies (NumPy) of the "
                       f"first {nv} of {len(victims)} victims ({nblk} blocks, {moved / 1e6:.1f} MB "
@@ -439,7 +517,7 @@ def cpu_baseline_admission(ps, budget_s):
 
     nr, dt, runs = _grow_sample(build, run, R, budget_s, start=2)
     tokens = int(sum(t.size for t in toks[:nr]))
-    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": _threads(),
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": _cores(), "blas_threads": _threads(),
             "kind": "oracle", "seconds_per_run": round(dt, 3), "runs": runs,
             "sample": f"fp64 oracle admission (add_tokens, cache write, row-by-row causal prefill "
                       f"of the uncached tokens) of the first {nr} of {R} requests ({tokens} prompt "
@@ -604,69 +682,6 @@ def build_resident(w, dev):
     return alloc, k_cache, v_cache
 
 
-def overlapped_steps(args, alloc, ids, B, max_blocks, NBUF, k_cache, v_cache, k_new, v_new, q,
-                     out, workspace, max_len_final, c, stream, ev, host_s, saved, use_hint, dev):
-    """The --overlap step: step s's uploads, copy-on-write copies and cache write run on a
-    second stream into device set s % NBUF while step s - 1 decodes from another set.  Step
-    s's writes touch only its new slots and fresh copy-on-write blocks, none of which the
-    decode of step s - 1 reads."""
-    import torch
-    import paged_kv_cache_359_amd as pkv
-    stage = [dict(slots=torch.empty(B, dtype=torch.int64, pin_memory=True),
-                  pairs=torch.empty(2 * B, dtype=torch.int32, pin_memory=True),
-                  tables=torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True),
-                  lens=torch.empty(B, dtype=torch.int32, pin_memory=True),
-                  cached=torch.empty(B, dtype=torch.int32, pin_memory=True),
-                  done=torch.cuda.Event()) for _ in range(NBUF)]
-    for st in stage:
-        st["done"].record()
-    dset = [dict(slots=torch.empty(B, dtype=torch.int64, device=dev),
-                 pairs=torch.empty((B, 2), dtype=torch.int32, device=dev),
-                 tables=torch.empty((B, max_blocks), dtype=torch.int32, device=dev),
-                 lens=torch.empty(B, dtype=torch.int32, device=dev),
-                 cached=torch.empty(B, dtype=torch.int32, device=dev) if use_hint else None,
-                 read=torch.cuda.Event(), ready=torch.cuda.Event()) for _ in range(NBUF)]
-    side = torch.cuda.Stream(dev)
-    last = [None]
-
-    def step(s):
-        st, ds = stage[s % NBUF], dset[s % NBUF]
-        st["done"].synchronize()  # the uploads that last read this staging set are finished
-        h0 = time.perf_counter()
-        sl, pr = st["slots"].numpy(), st["pairs"].numpy()
-        ncow = alloc.pkv_seq_append_into(ids, sl, pr)
-        alloc.pkv_get_block_tables(ids, max_blocks, st["tables"].numpy(), st["lens"].numpy())
-        if ds["cached"] is not None:
-            alloc.pkv_shared_prefix_blocks(ids, st["cached"].numpy())
-        host_s[0] += time.perf_counter() - h0
-        with torch.cuda.stream(side):
-            side.wait_event(ds["read"])  # the decode that last read this device set is done
-            ds["slots"].copy_(st["slots"], non_blocking=True)
-            ds["tables"].copy_(st["tables"], non_blocking=True)
-            ds["lens"].copy_(st["lens"], non_blocking=True)
-            if ds["cached"] is not None:
-                ds["cached"].copy_(st["cached"], non_blocking=True)
-            if ncow:
-                ds["pairs"].view(-1)[: 2 * ncow].copy_(st["pairs"][: 2 * ncow], non_blocking=True)
-            st["done"].record(side)
-            if ncow:
-                pkv.pkv_copy_blocks(k_cache, v_cache, ds["pairs"][:ncow])
-            pkv.pkv_reshape_and_cache(k_new[s], v_new[s], ds["slots"], k_cache, v_cache)
-            ds["ready"].record(side)
-        stream.wait_event(ds["ready"])
-        ev[s][0].record(stream)
-        pkv.pkv_paged_attention_decode(out, q[s], k_cache, v_cache, ds["tables"], ds["lens"],
-                                       max_len_final, c.scale, args.partition, workspace,
-                                       ds["cached"])
-        ev[s][1].record(stream)
-        ds["read"].record(stream)
-        last[0] = ds["tables"]
-        if saved is not None:
-            saved.append(out.clone())
-
-    return step, (lambda: last[0])
-
-
 def main_swap(args):
     """One step = one swap cycle of the victims (every --swap-every-th sequence of the batch).
     Swap-out: the allocator releases each victim's blocks and pkv_gather_blocks copies them
@@ -805,10 +820,10 @@ def main_swap(args):
 def main_cascade(args):
     """One step = one decode of the whole batch of a shared-prefix workload (default
     shared_prefix_bs16: 128 sequences whose first 1024 tokens are one shared set of blocks),
-    done three ways on the same resident cache and tables: cascade decode (the shared
-    prefix read once per group of 16 queries on matrix cores, each sequence's own tokens by
-    the decode kernels, log-sum-exp merge), plain decode with the shared-block hint, and
-    plain decode without it.  All three compute the same outputs (checked within the
+    done three ways on the same resident cache and tables: cascade decode (one kernel: per
+    KV head and 16 (sequence, query head) columns, the shared prefix read once for all 16 on
+    matrix cores, then each sequence's own tokens for its columns only), plain decode with
+    the shared-block hint, and plain decode without it.  All three compute the same outputs (checked within the
     attention bar of each other).  ``value`` is the logical K/V bytes (each sequence's whole
     context) per second of the cascade; ``unique`` bytes count the shared blocks once."""
     import torch
@@ -841,9 +856,9 @@ def main_cascade(args):
     hint = torch.from_numpy(alloc.pkv_shared_prefix_blocks(ids)).to(dev)
     gsz = int(np.max(np.diff(starts)))
     q = w.q[0]
-    ws_c = torch.empty(max(16, pkv.pkv_cascade_workspace_bytes(B, c.num_q_heads, c.num_kv_heads,
-                                                               c.head_dim, bs, max_ctx, c.dtype, -1)),
-                       dtype=torch.uint8, device=dev)
+    ws_n = pkv.pkv_cascade_workspace_bytes(B, c.num_q_heads, c.num_kv_heads, c.head_dim, bs,
+                                           max_ctx, c.dtype, -1)
+    ws_c = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
     ws_d = torch.empty(max(16, pkv.pkv_decode_workspace_bytes(B, c.num_q_heads, c.num_kv_heads,
                                                               c.head_dim, bs, max_ctx, c.dtype, -1)),
                        dtype=torch.uint8, device=dev)
@@ -900,7 +915,7 @@ def main_cascade(args):
         "roofline": {"bound": "hbm", "achieved": gbs(unique, ms), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(unique / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
                      "traffic": None,
-                     "kernel": "paged_attention_cascade (prefix pass + decode + merge), unique bytes",
+                     "kernel": "paged_attention_cascade (one kernel), unique bytes",
                      "bytes_per_launch": unique},
         "cpu_baseline": (None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)),
     }
@@ -1238,6 +1253,7 @@ def main():
     import torch
     import workloads as W
     import paged_kv_cache_359_amd as pkv
+    from paged_kv_cache_359_amd.step import DecodeStep
 
     if W.get_config(args.config).new_tokens is not None:
         return main_prefill(args, W.get_config(args.config))
@@ -1260,76 +1276,26 @@ def main():
     v_new = w.v_tok.index_select(0, step_idx.reshape(-1)).view(total_steps, B, c.num_kv_heads, c.head_dim)
     q = w.q
     max_len_final = int(w.lengths.max()) + total_steps - 1
-    max_blocks = -(-max_len_final // bs)
-    ws_bytes = pkv.pkv_decode_workspace_bytes(B, c.num_q_heads, c.num_kv_heads, c.head_dim, bs,
-                                              max_len_final, c.dtype, args.partition)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, c.num_q_heads, c.head_dim), dtype=c.torch_dtype, device=dev)
     ids = np.arange(B, dtype=np.int64)
-    stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(total_steps)]
     kv_per_token = 2 * c.num_kv_heads * c.head_dim * c.dsize
     step_bytes = [kv_per_token * int(np.sum(w.lengths + s)) for s in range(total_steps)]
-    host_s = [0.0]
     saved = [] if args.check else None
     use_hint = not args.no_cache_hint
-    NBUF = 4 if args.overlap else 2
+    # One stream; the device keeps the block tables and lengths, and the append kernel reads
+    # each step's slots and positions from pinned host memory in place.
+    stepper = DecodeStep(alloc, ids, k_cache, v_cache, c.num_q_heads, max_len_final, c.scale,
+                         args.partition, cache_hint=use_hint)
+    workspace = stepper.workspace
 
-    if args.overlap:
-        step, final_tables = overlapped_steps(args, alloc, ids, B, max_blocks, NBUF, k_cache, v_cache,
-                                              k_new, v_new, q, out, workspace, max_len_final, c,
-                                              stream, ev, host_s, saved, use_hint, dev)
-    else:
-        # One stream.  The device keeps the block tables and lengths: each step uploads one
-        # small packed buffer (the slots, the positions they extend and the hint) and
-        # pkv_update_block_tables applies them, instead of re-sending whole tables.
-        t_host, l_host = alloc.pkv_get_block_tables(ids, max_blocks)
-        tables_d = torch.from_numpy(t_host).to(dev)
-        lens_d = torch.from_numpy(l_host).to(dev)
-        lens_h = l_host.astype(np.int32).copy()
-        rows_d = torch.arange(B, dtype=torch.int32, device=dev)
-        nbytes = 8 * B + 4 * B + 4 * B + 8 * B  # slots | positions | hint | cow pairs
-        pk_h = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(NBUF)]
-        pk_done = [torch.cuda.Event() for _ in range(NBUF)]
-        for e in pk_done:
-            e.record(stream)
-        pk_d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        slots_d = pk_d[: 8 * B].view(torch.int64)
-        pos_d = pk_d[8 * B: 12 * B].view(torch.int32)
-        hint_d = pk_d[12 * B: 16 * B].view(torch.int32)
-        pairs_d = pk_d[16 * B:].view(torch.int32).view(B, 2)
+    def step(s):
+        stepper(k_new[s], v_new[s], q[s], out, ev[s])
+        if saved is not None:
+            saved.append(out.clone())
 
-        def step(s):
-            i = s % NBUF
-            pk_done[i].synchronize()  # the upload that last read this staging buffer is done
-            h0 = time.perf_counter()
-            buf = pk_h[i].numpy()
-            sl = buf[: 8 * B].view(np.int64)
-            ps = buf[8 * B: 12 * B].view(np.int32)
-            hint = buf[12 * B: 16 * B].view(np.int32)
-            pr = buf[16 * B:].view(np.int32)
-            ps[:] = lens_h                                                    # positions
-            ncow = alloc.pkv_seq_append_into(ids, sl, pr)                     # a1
-            lens_h[:] += 1
-            if use_hint:  # leading blocks shared with other sequences: read cached
-                alloc.pkv_shared_prefix_blocks(ids, hint)
-            host_s[0] += time.perf_counter() - h0
-            pk_d.copy_(pk_h[i], non_blocking=True)                            # a2
-            pk_done[i].record(stream)
-            if ncow:                                                          # a3
-                pkv.pkv_copy_blocks(k_cache, v_cache, pairs_d[:ncow])
-            pkv.pkv_update_block_tables(tables_d, lens_d, rows_d, pos_d, slots_d, bs, c.num_blocks)
-            pkv.pkv_reshape_and_cache(k_new[s], v_new[s], slots_d, k_cache, v_cache)  # a4
-            ev[s][0].record(stream)
-            pkv.pkv_paged_attention_decode(out, q[s], k_cache, v_cache, tables_d, lens_d,  # a5, a6
-                                           max_len_final, c.scale, args.partition, workspace,
-                                           hint_d if use_hint else None)
-            ev[s][1].record(stream)
-            if saved is not None:
-                saved.append(out.clone())
-
-        final_tables = lambda: tables_d
+    final_tables = lambda: stepper.tables  # noqa: E731
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -1341,8 +1307,10 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    host_s[0] = 0.0
+    stepper.host_seconds = 0.0
     elapsed = run_timed(step, args.warmup, total_steps, torch.cuda.synchronize)
+    out_last = out.clone()  # the last timed step's output, for the parity check
+    host_ms = stepper.host_seconds * 1e3 / args.steps
     print(f"[bench] timed {args.steps} steps", file=sys.stderr, flush=True)
     if saved is not None:
         # During the timed steps tables only grow, so the final tables with each step's
@@ -1387,10 +1355,16 @@ def main():
         print(f"[bench] kernel protocol median {protocol['median_ms']} ms; read ceiling "
               f"{ceiling}", file=sys.stderr, flush=True)
 
-    cpu = None
+    memory = kv_memory(alloc, ids, stepper.max_blocks, bs)
+    cpu = parity = None
     if not args.no_cpu_baseline:
+        # The CPU leg, the only part of this program that runs the oracle: its timing on a
+        # sample of the batch, and the parity check of the last timed step.
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, args.cpu_seconds)
+        parity = oracle_parity(w, out_last, total_steps - 1)
+        print(f"[bench] parity of step {total_steps - 1}: {parity['rows_checked']} rows, max abs err "
+              f"{parity['max_abs_err']:.3g}, pass {parity['pass']}", file=sys.stderr, flush=True)
 
     traffic = counted_traffic(c.name)
     res = {
@@ -1405,9 +1379,13 @@ def main():
         "decode_kernel_tokens_per_s": round(B / (kern_avg_ms * 1e-3), 1),
         "partition_size": args.partition,
         "cache_hint": not args.no_cache_hint,
-        "step_overlap": bool(args.overlap),
         "checked": bool(args.check),
-        "host_ms_per_step": round(host_s[0] * 1e3 / K, 4),
+        "host_ms_per_step": round(host_ms, 4),
+        "cow_copies": stepper.cow_copies,
+        "device": device_info(dev),
+        "seed": seed_info(c),
+        "kv_memory": memory,
+        "parity": parity,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],

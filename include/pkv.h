@@ -7,9 +7,11 @@
  *  - a host block allocator (pkv_alloc_*, pkv_seq_*): the KV Cache Manager of a paged
  *    inference engine.  It owns the free pool of physical blocks, one block table per
  *    sequence, reference counts for shared blocks, and copy-on-write on append.
- *  - device operations (pkv_reshape_and_cache, pkv_copy_blocks,
- *    pkv_paged_attention_decode): HIP kernels, enqueued asynchronously on the caller's
- *    stream; the library never synchronises inside a call.
+ *  - device operations (pkv_reshape_and_cache, pkv_append_and_cache, pkv_copy_blocks,
+ *    pkv_update_block_tables, pkv_gather_blocks / pkv_scatter_blocks,
+ *    pkv_paged_attention_decode / _cascade / _prefill, pkv_read_probe): HIP kernels,
+ *    enqueued asynchronously on the caller's stream; the library never synchronises inside
+ *    a call.
  *
  * Passages followed (page title, section):
  *  - "vLLM + PagedAttention：打造高并发LLM推理引擎", the numbered steps under
@@ -81,7 +83,10 @@ int32_t pkv_version(void);
  * Host block allocator
  * ====================================================================================== */
 
-/* Create an allocator over num_blocks physical blocks of block_size token slots.
+/* Create an allocator over num_blocks physical blocks of block_size token slots: the pool
+ * of fixed-size blocks every request draws from ("PagedAttention 与 vLLM 推理加速", §2.2; "LLM
+ * Systems 24: Efficient LLM Inference with PagedAttention and vLLM", §2.1.3: the KV Cache
+ * Manager allocates and frees physical blocks).
  * free_order (nullable, host, num_blocks entries): a permutation of 0..num_blocks-1 giving
  * the order in which blocks are first handed out (NULL = 0, 1, 2, ...).  The pool is a
  * stack: blocks freed later are handed out before untouched ones, the most recently freed
@@ -90,11 +95,14 @@ int32_t pkv_version(void);
 pkv_status pkv_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
                             pkv_alloc** out);
 
-/* Destroy an allocator (NULL is ignored). */
+/* Destroy an allocator and its whole state (NULL is ignored); the caller's device pools are
+ * untouched (same passages as pkv_alloc_create). */
 void pkv_alloc_destroy(pkv_alloc* a);
 
-/* Add sequence seq_id holding num_tokens (>= 0) tokens: takes ceil(num_tokens/block_size)
- * blocks, in logical order, and writes the tokens' slots to slots_out (host, num_tokens
+/* Add sequence seq_id holding num_tokens (>= 0) tokens ("vLLM + PagedAttention：打造高并发LLM
+ * 推理引擎", step 1 under "它是怎么工作的？": blocks are taken on demand; "PagedAttention 与 vLLM
+ * 推理加速", §2.3: 7 tokens in 4-token blocks take two blocks, the last with one free slot):
+ * takes ceil(num_tokens/block_size) blocks, in logical order, and writes the tokens' slots to slots_out (host, num_tokens
  * entries; may be NULL only when num_tokens == 0).
  * DUPLICATE_SEQ if seq_id exists; OUT_OF_BLOCKS if the pool is short. */
 pkv_status pkv_seq_add(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t* slots_out);
@@ -117,12 +125,17 @@ pkv_status pkv_seq_add(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t
 pkv_status pkv_seq_add_tokens(pkv_alloc* a, int64_t seq_id, const int32_t* tokens,
                               int32_t num_tokens, int64_t* slots_out, int32_t* n_cached_out);
 
-/* Create child_id sharing every block of parent_id (each block gains one reference).
+/* Create child_id sharing every block of parent_id (each block gains one reference):
+ * requests with a common prefix point at one physical copy ("PagedAttention 与 vLLM 推理加速",
+ * §3.2 (3); "LLM Systems 24", §3 Conclusion: reference counts with copy-on-write).
  * UNKNOWN_SEQ if the parent is missing; DUPLICATE_SEQ if the child exists. */
 pkv_status pkv_seq_fork(pkv_alloc* a, int64_t parent_id, int64_t child_id);
 
 /* Append one token to each of the n sequences seq_ids (host), in order; the ids must be
- * distinct (else INVALID_ARG).  For each sequence: a length that is a multiple of
+ * distinct (else INVALID_ARG).  ("vLLM + PagedAttention", steps 1–2 under "它是怎么工作的？": a
+ * new block only when the last one is full; "PagedAttention 与 vLLM 推理加速", §2.4: only a
+ * sequence's last block is partly filled, and §3.2 (3): a shared block is copied only when a
+ * sharer writes to it.)  For each sequence: a length that is a multiple of
  * block_size takes a fresh block; otherwise a last block shared with another sequence is
  * replaced by a fresh block and the pair (old, new) is reported for the caller to copy
  * (copy-on-write) before writing; an unshared last block is written in place.
@@ -133,7 +146,8 @@ pkv_status pkv_seq_append(pkv_alloc* a, const int64_t* seq_ids, int32_t n, int64
                           int32_t* cow_pairs_out, int32_t* n_cow_out);
 
 /* Append n >= 0 tokens to one sequence (a prefill chunk): the same as n calls of
- * pkv_seq_append with seq_id alone.  slots_out (host, n int64): the new tokens' slots in
+ * pkv_seq_append with seq_id alone (same passages; the chunk's tokens then attend causally,
+ * "PagedAttention 与 vLLM 推理加速", §1).  slots_out (host, n int64): the new tokens' slots in
  * order.  cow_pairs_out (host, 2 int32): at most one (src, dst) copy-on-write pair, for the
  * first token when the last block is shared and partly filled; *n_cow_out = 0 or 1.
  * All-or-nothing: OUT_OF_BLOCKS leaves everything unchanged. */
@@ -141,7 +155,9 @@ pkv_status pkv_seq_extend(pkv_alloc* a, int64_t seq_id, int32_t n, int64_t* slot
                           int32_t* cow_pairs_out, int32_t* n_cow_out);
 
 /* End a sequence: each of its blocks loses a reference; blocks with none left return to
- * the pool in logical order (so its last block is the next one handed out). */
+ * the pool in logical order (so its last block is the next one handed out).  ("vLLM +
+ * PagedAttention", step 4 under "它是怎么工作的？": a finished request's blocks go back to the
+ * pool; "LLM Systems 24", §3 Conclusion: a shared block is freed with its last reference.) */
 pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id);
 
 /* Preemption by swapping ("LLM Systems 24: Efficient LLM Inference with PagedAttention and
@@ -161,7 +177,9 @@ pkv_status pkv_seq_swap_out(pkv_alloc* a, int64_t seq_id, int32_t max_blocks, in
 pkv_status pkv_seq_swap_in(pkv_alloc* a, int64_t seq_id, int32_t max_blocks, int32_t* blocks_out,
                            int32_t* n_blocks_out);
 
-/* Copy the block tables of n sequences into tables_out (host, n * max_blocks int32,
+/* The page tables ("vLLM + PagedAttention", step 2 under "它是怎么工作的？": each request maps
+ * token positions to blocks; "PagedAttention 与 vLLM 推理加速", §2.3; "LLM Systems 24", §2.1.3:
+ * the logical-to-physical block mapping).  Copy the block tables of n sequences into tables_out (host, n * max_blocks int32,
  * row-major, padded with -1) and their lengths into lens_out (host, n int32; nullable).
  * INVALID_ARG if a sequence holds more than max_blocks blocks. */
 pkv_status pkv_get_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
@@ -189,22 +207,37 @@ pkv_status pkv_prefix_groups(const pkv_alloc* a, const int64_t* seq_ids, int32_t
                              int32_t* group_start_out, int32_t* shared_blocks_out,
                              int32_t* n_groups_out);
 
-/* Length (tokens) of one sequence. */
+/* Length (tokens) of one sequence: its page table covers positions 0 .. length - 1 ("vLLM +
+ * PagedAttention", step 2 under "它是怎么工作的？"). */
 pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out);
 
+/* Lengths (tokens) of the n sequences seq_ids (host) into lens_out (host, n int32): before
+ * pkv_seq_append, the positions the appended tokens will take (each request's page table
+ * maps token positions to blocks: "vLLM + PagedAttention", step 2 under "它是怎么工作的？").
+ * UNKNOWN_SEQ if an id is not resident (lens_out untouched). */
+pkv_status pkv_seq_lengths(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
+                           int32_t* lens_out);
+
 /* Number of blocks a call can take: free ones plus evictable cached ones (-1 for a null
- * handle). */
+ * handle).  A scheduler checks it before admitting or growing requests, and preempts when
+ * it runs out ("LLM Systems 24", §3 Conclusion). */
 int32_t pkv_num_free_blocks(const pkv_alloc* a);
 
 /* Number of blocks registered in the prefix cache and not yet evicted, held or evictable
- * (-1 for a null handle). */
+ * (-1 for a null handle) ("PagedAttention 与 vLLM 推理加速", §3.2 (3): one copy of a shared
+ * system prompt's blocks). */
 int32_t pkv_num_cached_blocks(const pkv_alloc* a);
 
-/* Reference count of a physical block (-1 if out of range or a null handle). */
+/* Reference count of a physical block: the number of sequences whose table holds it (-1 if
+ * out of range or a null handle) ("LLM Systems 24", §3 Conclusion: reference counts decide
+ * copy-on-write and freeing). */
 int32_t pkv_block_refcount(const pkv_alloc* a, int32_t block);
 
-/* tokens_stored: sum of all sequence lengths (a shared token counts once per sequence);
- * slots_allocated: block_size times the number of blocks referenced at least once. */
+/* Memory use of the pool ("PagedAttention 与 vLLM 推理加速", §2.4: only the last block of a
+ * sequence wastes slots, under 4% in all; §3.2 (1): utilisation near 96% against ~30% for
+ * contiguous reservation).  tokens_stored: sum of all sequence lengths (a shared token
+ * counts once per sequence); slots_allocated: block_size times the number of blocks
+ * referenced at least once. */
 pkv_status pkv_usage(const pkv_alloc* a, int64_t* tokens_stored, int64_t* slots_allocated);
 
 /* ======================================================================================
@@ -268,6 +301,31 @@ pkv_status pkv_update_block_tables(int32_t* block_tables, int32_t* context_lens,
                                    int32_t max_blocks_per_seq, int32_t block_size,
                                    int32_t num_blocks, void* stream);
 
+/* The cache write and the table upkeep of one decode step in a single launch: the same
+ * result as pkv_update_block_tables(block_tables, context_lens, rows, positions,
+ * slot_mapping, n, num_rows, max_blocks_per_seq, block_size, num_blocks) followed by
+ * pkv_reshape_and_cache(key, value, slot_mapping, k_cache, v_cache, n, num_kv_heads,
+ * head_dim, block_size, num_blocks, dtype) ("vLLM + PagedAttention", steps 1–2 under
+ * "它是怎么工作的？": the new token goes into the block its table assigns, and the table
+ * records where it lives).
+ * slot_mapping (n int64), positions (n int32) and rows (n int32; NULL = token i updates row
+ * i) may be device memory or pinned host memory mapped into the device's address space,
+ * passed by its device-side address (hipHostGetDevicePointer): a decode loop then uploads
+ * nothing.  They are read once per token with system-coherent loads, so the host may rewrite
+ * such a buffer for a later call once this call has completed.
+ * key, value: device, [n][num_kv_heads][head_dim] contiguous, 16-byte aligned.
+ * block_tables, context_lens: device, both NULL for the cache write alone (rows and
+ * positions are then not read).  Slots and rows must be distinct.  A token whose slot lies
+ * outside [0, num_blocks * block_size) is skipped entirely; a table update whose row,
+ * position or column is out of range is skipped (the cache write still happens).
+ * n == 0 is a no-op. */
+pkv_status pkv_append_and_cache(const void* key, const void* value, const int64_t* slot_mapping,
+                                const int32_t* rows, const int32_t* positions, int32_t n,
+                                void* k_cache, void* v_cache, int32_t* block_tables,
+                                int32_t* context_lens, int32_t num_rows, int32_t max_blocks_per_seq,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, pkv_dtype dtype, void* stream);
+
 /* Bytes of workspace pkv_paged_attention_decode needs for this shape, max_context_len and
  * partition_size (same meanings as for the decode call): num_seqs * num_q_heads * P *
  * (head_dim + 2) floats when contexts are split into P > 1 partitions, else 0. */
@@ -295,7 +353,10 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * max_context_len: an upper bound of context_lens (sizes the launch without reading device
  * memory on the host; larger lengths are clamped to it and to
  * max_blocks_per_seq * block_size).  Table entries outside [0, num_blocks) are treated as
- * empty blocks and never dereferenced.
+ * empty blocks and never dereferenced.  With PKV_DEBUG=1 in the environment the call first
+ * waits for the stream, reads context_lens and block_tables back and returns
+ * PKV_ERR_INVALID_ARG (message in pkv_last_error, nothing enqueued) if a length lies outside
+ * [0, that clamp] or a table entry a length covers lies outside [0, num_blocks).
  * cached_blocks (nullable, device, num_seqs int32): a cache-policy hint.  K/V blocks are
  * streamed with non-temporal loads, which is fastest for data read once; the first
  * cached_blocks[b] table entries of sequence b (for example a prefix shared with other
@@ -320,25 +381,33 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
 
 /* Cascade decode: the same result as pkv_paged_attention_decode (plain attention of each
  * sequence's query over its whole context, up to fp32 rounding order), computed with the
- * shared prefix of each group of sequences read once per group.  Cascade attention is named
- * among the kernels a runtime picks per batch ("LLM Systems 24: Efficient LLM Inference
- * with PagedAttention and vLLM", §2.2.1.3); requests sharing a system prompt share its
- * blocks ("PagedAttention 与 vLLM 推理加速", §3.2 (3)).  Three launches on `stream`:
- *   1. per (KV head, group, 16 columns): the group's members' queries (every query head of
- *      the KV head) attend to the shared blocks, read once, on matrix cores;
- *   2. per sequence: the decode kernels attend to the rest of its context;
- *   3. the two parts are merged by their log-sum-exp.
- * group_start (device, num_groups + 1 int32) and shared_blocks (device, num_seqs int32)
- * are pkv_prefix_groups's output for the batch rows in order (any grouping with the same
- * guarantees works: the rows of group g are group_start[g] .. group_start[g+1] - 1, all
- * share their first shared_blocks[row] table entries (the same count for the group), and
- * those blocks lie within every member's context; shared_blocks[row] = 0 for a row alone).
- * max_group_size: an upper bound of the group sizes (sizes the launch).
- * workspace: at least pkv_cascade_workspace_bytes(...) bytes, 16-byte aligned.
- * Other arguments as for pkv_paged_attention_decode (no cache hint: the prefix pass reads
- * shared blocks through the caches, the per-sequence pass streams the rest).
+ * shared prefix of each group of sequences read once per 16 queries instead of once per
+ * sequence.  Cascade attention is named among the kernels a runtime picks per batch ("LLM
+ * Systems 24: Efficient LLM Inference with PagedAttention and vLLM", §2.2.1.3); requests
+ * sharing a system prompt share its blocks ("PagedAttention 与 vLLM 推理加速", §3.2 (3)).
+ * One launch on `stream`: per (KV head, group, tile of 16 (member, query head) columns), a
+ * workgroup walks the group's shared blocks once for all its columns (on matrix cores,
+ * through the caches), then each member's own blocks for that member's columns only (streamed),
+ * and writes the outputs; no partial results leave the workgroup.
+ * group_start (device, num_groups + 1 int32, non-decreasing): group g is the rows
+ * group_start[g] .. group_start[g+1] - 1; every row must lie in exactly one group
+ * (group_start[0] = 0, group_start[num_groups] = num_seqs), and a row outside every group is
+ * not written.  shared_blocks (device, num_seqs int32): the group's shared count is its
+ * first row's entry, clamped to [0, that row's full blocks]; every member shares that many
+ * leading table entries, or its own full blocks if fewer (a member's other entries of
+ * shared_blocks are not read).  pkv_prefix_groups's output for the batch rows in order
+ * meets all of this; a grouping whose members' tables differ within the shared count gives
+ * those members attention over the first row's blocks there.
+ * max_group_size: sizes the launch (ceil(max_group_size * query heads per KV head / 16)
+ * workgroups per group and KV head); a workgroup also takes every later tile at that stride,
+ * so groups larger than the bound are still covered in full.
+ * workspace: the kernels need none (pkv_cascade_workspace_bytes returns 0); it may be NULL.
+ * partition_size: validated as for pkv_paged_attention_decode; each workgroup walks its
+ * columns' whole contexts, so it does not change the work.
+ * Other arguments as for pkv_paged_attention_decode (no cache hint: the shared blocks are
+ * read through the caches, the rest streamed).
  * Supported: fp16 and bf16, head_dim 64 or 128, block_size 8, 16 or 32; otherwise
- * PKV_ERR_UNSUPPORTED (use pkv_paged_attention_decode). */
+ * PKV_ERR_UNSUPPORTED (use pkv_paged_attention_decode).  num_groups == 0 is a no-op. */
 size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                    pkv_dtype dtype, int32_t partition_size);

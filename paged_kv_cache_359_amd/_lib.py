@@ -27,6 +27,7 @@ SIGNATURES = {
     "pkv_seq_swap_in": (c_i32, [c_vp, c_i64, c_i32, P_i32, P_i32]),
     "pkv_get_block_tables": (c_i32, [c_vp, P_i64, c_i32, c_i32, P_i32, P_i32]),
     "pkv_seq_length": (c_i32, [c_vp, c_i64, P_i32]),
+    "pkv_seq_lengths": (c_i32, [c_vp, P_i64, c_i32, P_i32]),
     "pkv_prefix_groups": (c_i32, [c_vp, P_i64, c_i32, P_i32, P_i32, P_i32]),
     "pkv_shared_prefix_blocks": (c_i32, [c_vp, P_i64, c_i32, P_i32]),
     "pkv_num_free_blocks": (c_i32, [c_vp]),
@@ -42,6 +43,8 @@ SIGNATURES = {
                                    c_i32, c_vp]),
     "pkv_update_block_tables": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                         c_i32, c_vp]),
+    "pkv_append_and_cache": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                     c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pkv_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_attention_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,

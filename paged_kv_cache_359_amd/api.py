@@ -155,6 +155,16 @@ class PkvAlloc:
                "pkv_get_block_tables")
         return tables, lens
 
+    def pkv_seq_lengths(self, seq_ids, out=None) -> np.ndarray:
+        """Lengths of the sequences seq_ids (int32), into ``out`` when given."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64).reshape(-1)
+        n = ids.size
+        res = out if out is not None else np.empty(n, np.int32)
+        _check(self._lib.pkv_seq_lengths(self._h, _ptr(ids, ctypes.c_int64) if n else None, n,
+                                         _ptr(res, ctypes.c_int32) if n else None),
+               "pkv_seq_lengths")
+        return res
+
     def pkv_shared_prefix_blocks(self, seq_ids, out=None) -> np.ndarray:
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64).reshape(-1)
         n = ids.size
@@ -276,11 +286,13 @@ def _mapped(t):
         _HIP.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
                                                  ctypes.c_uint]
         _HIP.hipHostGetDevicePointer.restype = ctypes.c_int
+    # The runtime maps whole allocations: map the storage's start and add the view's offset.
+    base = t.untyped_storage().data_ptr()
     ptr = ctypes.c_void_p()
-    err = _HIP.hipHostGetDevicePointer(ctypes.byref(ptr), ctypes.c_void_p(t.data_ptr()), 0)
+    err = _HIP.hipHostGetDevicePointer(ctypes.byref(ptr), ctypes.c_void_p(base), 0)
     if err != 0 or not ptr.value:
         raise ValueError(f"pinned buffer is not mapped for the device (hip error {err})")
-    return ptr.value
+    return ptr.value + (t.data_ptr() - base)
 
 
 def _move_blocks(fn, name, cache_k, cache_v, blocks, buf_k, buf_v):
@@ -333,6 +345,46 @@ def pkv_update_block_tables(block_tables, context_lens, rows, positions, slot_ma
         _dev(block_tables), _dev(context_lens), _dev(rows), _dev(positions), _dev(slot_mapping),
         n, block_tables.shape[0], block_tables.shape[1], int(block_size), int(num_blocks),
         _stream(block_tables)), "pkv_update_block_tables")
+
+
+def pkv_append_and_cache(key, value, slot_mapping, k_cache, v_cache, block_tables=None,
+                         context_lens=None, positions=None, rows=None):
+    """key/value [n, Hkv, D] (GPU); slot_mapping [n] int64, positions [n] int32 and rows [n]
+    int32 (GPU tensors or pinned host tensors, read in place); caches [N, Hkv, bs, D];
+    block_tables [B, max_blocks] and context_lens [B] int32 (GPU, updated in place), or both
+    None for the cache write alone."""
+    import torch
+    n, hkv, bs, d = k_cache.shape
+    t = key.shape[0]
+    if key.shape != (t, hkv, d) or value.shape != key.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if not (key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != t:
+        raise ValueError("slot_mapping must be int64 [n]")
+    upkeep = block_tables is not None or context_lens is not None
+    num_rows = max_blocks = 0
+    if upkeep:
+        if block_tables is None or context_lens is None or positions is None:
+            raise ValueError("block_tables, context_lens and positions go together")
+        if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+            raise TypeError("block_tables and context_lens must be int32")
+        if block_tables.dim() != 2 or context_lens.shape != (block_tables.shape[0],):
+            raise ValueError("table shape")
+        if positions.dtype != torch.int32 or positions.numel() != t:
+            raise ValueError("positions must be int32 [n]")
+        if rows is not None and (rows.dtype != torch.int32 or rows.numel() != t):
+            raise ValueError("rows must be int32 [n]")
+        num_rows, max_blocks = block_tables.shape
+    if t == 0:
+        return
+    _check(_lib.load().pkv_append_and_cache(
+        _dev(key), _dev(value), _mapped(slot_mapping),
+        _mapped(rows) if upkeep and rows is not None else None,
+        _mapped(positions) if upkeep else None, t, _dev(k_cache), _dev(v_cache),
+        _dev(block_tables) if upkeep else None, _dev(context_lens) if upkeep else None,
+        num_rows, max_blocks, hkv, d, bs, n, _dtype_code(k_cache), _stream(k_cache)),
+        "pkv_append_and_cache")
 
 
 def pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -392,10 +444,10 @@ def pkv_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, b
 
 def pkv_paged_attention_cascade(out, q, k_cache, v_cache, block_tables, context_lens, group_start,
                                 shared_blocks, max_group_size: int, max_context_len: int,
-                                scale: float, workspace, partition_size: int = -1):
+                                scale: float, workspace=None, partition_size: int = -1):
     """As pkv_paged_attention_decode; group_start [G + 1] and shared_blocks [B] are int32
-    device tensors (pkv_prefix_groups's output); workspace: a uint8 device tensor of at least
-    pkv_cascade_workspace_bytes(...) bytes."""
+    device tensors (pkv_prefix_groups's output); workspace: None or a uint8 device tensor of
+    at least pkv_cascade_workspace_bytes(...) bytes."""
     import torch
     nb, hq, d = q.shape
     n, hkv, bs, d2 = k_cache.shape
@@ -417,7 +469,8 @@ def pkv_paged_attention_cascade(out, q, k_cache, v_cache, block_tables, context_
         _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
         _dev(group_start), _dev(shared_blocks), ng, int(max_group_size), nb, hq, hkv, d, bs, n,
         block_tables.shape[1], int(max_context_len), float(scale), _dtype_code(k_cache),
-        int(partition_size), _dev(workspace), workspace.numel() * workspace.element_size(),
+        int(partition_size), _dev(workspace) if workspace is not None and workspace.numel() else None,
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(q)), "pkv_paged_attention_cascade")
     return out
 

@@ -485,6 +485,21 @@ pkv_status pkv_seq_length(const pkv_alloc* a, int64_t seq_id, int32_t* len_out) 
   return PKV_OK;
 }
 
+pkv_status pkv_seq_lengths(const pkv_alloc* a, const int64_t* seq_ids, int32_t n,
+                           int32_t* lens_out) {
+  if (!a || n < 0) return PKV_ERR_INVALID_ARG;
+  if (n > 0 && (!seq_ids || !lens_out)) return PKV_ERR_INVALID_ARG;
+  // Resolve every id first, so that an unknown one leaves lens_out untouched.
+  std::vector<int32_t> lens(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    lens[i] = it->second.len;
+  }
+  std::copy(lens.begin(), lens.end(), lens_out);
+  return PKV_OK;
+}
+
 int32_t pkv_num_free_blocks(const pkv_alloc* a) {
   return a ? int32_t(a->available()) : -1;
 }

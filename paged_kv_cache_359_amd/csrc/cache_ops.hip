@@ -62,6 +62,55 @@ __global__ __launch_bounds__(256) void update_tables_kernel(int32_t* __restrict_
   lens[r] = p + 1;
 }
 
+// A decode step's host-produced arrays (slots, rows, positions) may sit in pinned host memory
+// that the host rewrites for a later step, so they are read with system-coherent loads,
+// which never return a line the GPU caches kept from an earlier read of the same address.
+__device__ __forceinline__ int64_t load_sys(const int64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ int32_t load_sys(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// One workgroup per appended token t: thread 0 reads the token's slot (and, with tables, its
+// row and position) once and records the table entry and length as update_tables_kernel
+// does; then the workgroup copies the token's K and V rows of every head into the slot, 16
+// bytes per thread per step, as reshape_and_cache_kernel does.
+__global__ __launch_bounds__(256) void append_and_cache_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value,
+    const int64_t* __restrict__ slots, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ pos, uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+    int32_t* __restrict__ tables, int32_t* __restrict__ lens, int32_t heads, int32_t row_vecs,
+    int32_t block_size, int64_t num_slots, int32_t num_rows, int32_t max_blocks) {
+  __shared__ int64_t s_slot;
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const int64_t s = load_sys(slots + t);
+    s_slot = s;
+    if (tables && s >= 0 && s < num_slots) {
+      const int32_t r = rows ? load_sys(rows + t) : int32_t(t);
+      const int32_t p = load_sys(pos + t);
+      if ((unsigned)r < (unsigned)num_rows && p >= 0 && p / block_size < max_blocks) {
+        tables[int64_t(r) * max_blocks + p / block_size] = int32_t(s / block_size);
+        lens[r] = p + 1;
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t s = s_slot;
+  if (s < 0 || s >= num_slots) return;
+  const int64_t blk = s / block_size;
+  const int64_t off = s - blk * block_size;
+  const int32_t hv = heads * row_vecs;
+  for (int32_t i = threadIdx.x; i < hv; i += blockDim.x) {
+    const int32_t h = i / row_vecs;
+    const int32_t c = i - h * row_vecs;
+    const int64_t dst = ((blk * heads + h) * block_size + off) * row_vecs + c;
+    k_cache[dst] = key[t * hv + i];
+    v_cache[dst] = value[t * hv + i];
+  }
+}
+
 // Whole-block moves between the pools and a contiguous buffer (swap preemption): with
 // OUT, dst[i] = pool[blocks[i]]; otherwise pool[blocks[i]] = src[i].  Ids outside
 // [0, num_blocks) are skipped.
@@ -213,6 +262,37 @@ pkv_status pkv_update_block_tables(int32_t* block_tables, int32_t* context_lens,
                      slot_mapping, n, num_rows, max_blocks_per_seq, block_size,
                      int64_t(num_blocks) * block_size);
   return launch_status("update_block_tables");
+}
+
+pkv_status pkv_append_and_cache(const void* key, const void* value, const int64_t* slot_mapping,
+                                const int32_t* rows, const int32_t* positions, int32_t n,
+                                void* k_cache, void* v_cache, int32_t* block_tables,
+                                int32_t* context_lens, int32_t num_rows, int32_t max_blocks_per_seq,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, pkv_dtype dtype, void* stream) {
+  if (n < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(dtype)) return PKV_ERR_INVALID_ARG;
+  if ((int64_t(head_dim) * dtype_size(dtype)) % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  const bool upkeep = block_tables || context_lens;
+  if (upkeep && (!block_tables || !context_lens || !positions || num_rows < 0 ||
+                 max_blocks_per_seq <= 0))
+    return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_INVALID_ARG;
+  const int32_t row_vecs = head_dim * dtype_size(dtype) / 16;
+  if (int64_t(num_kv_heads) * row_vecs > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+  clear_stale_error();
+  hipLaunchKernelGGL(append_and_cache_kernel, dim3(unsigned(n)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(key),
+                     static_cast<const uint4*>(value), slot_mapping, upkeep ? rows : nullptr,
+                     upkeep ? positions : nullptr, static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), upkeep ? block_tables : nullptr,
+                     upkeep ? context_lens : nullptr, num_kv_heads, row_vecs, block_size,
+                     int64_t(num_blocks) * block_size, num_rows, max_blocks_per_seq);
+  return launch_status("append_and_cache");
 }
 
 }  // extern "C"

@@ -7,6 +7,9 @@
 // Two inner loops: VALU (any head layout; DPP row reductions) and MFMA (grouped-query heads
 // sharing one K/V tile form the columns of small matrix products).  One workgroup per
 // (sequence, head or head group, partition); reduce_partitions merges partitions.
+#include <cstdlib>
+#include <vector>
+
 #include "device.h"
 #include "host.h"
 #include "mfma_tile.h"
@@ -153,13 +156,11 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
   const int h = blockIdx.x;
   const int part = blockIdx.y;
   const int b = blockIdx.z;
-  const int ctx_all = clamp_ctx(a, b);
-  const int sk = skipped_blocks(a, b, ctx_all, BS);
-  const int ctx = ctx_all - sk * BS;  // attended here: tokens sk * BS .. ctx_all - 1
+  const int ctx = clamp_ctx(a, b);
   const int tid = threadIdx.x;
   const size_t out_row = (size_t(b) * a.num_q_heads + h) * D;
   if (ctx == 0) {
-    if (part == 0 && !a.partials_only)
+    if (part == 0)
       for (int d = tid; d < D; d += NW * 64) store_elt<DT>(a.out, out_row + d, 0.f);
     return;
   }
@@ -173,14 +174,14 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
   const int row = lane / V::LPT;
   const int col = lane % V::LPT;
   const int kvh = h / a.group;
-  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks + sk;
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
   const size_t lane_off = (size_t(kvh) * BS * D + size_t(col) * V::VEC) * V::ES;
   const char* kb = static_cast<const char*>(a.k_cache) + lane_off;
   const char* vb = static_cast<const char*>(a.v_cache) + lane_off;
   const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * V::ES;
   const uint4 qv = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
                                                     (out_row + size_t(col) * V::VEC) * V::ES);
-  const int ncached = cached_blocks(a, b) - sk;
+  const int ncached = cached_blocks(a, b);
   typename V::State st;
   V::init(st);
   const int nchunks = (t1 - t0 + V::CT - 1) / V::CT;
@@ -212,10 +213,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu(DecodeArgs a) {
         O += s_o[r][d] * w;
       }
     }
-    if (nparts == 1 && !a.partials_only) {
+    if (nparts == 1) {
       store_elt<DT>(a.out, out_row + d, L > 0.f ? O / L : 0.f);
     } else {
-      const size_t pi = (size_t(b) * a.num_q_heads + h) * a.max_parts + a.part_base + part;
+      const size_t pi = (size_t(b) * a.num_q_heads + h) * a.max_parts + part;
       a.part_o[pi * D + d] = O;
       if (d == 0) {
         a.part_m[pi] = M;
@@ -232,7 +233,7 @@ template <int DT, int D, int BS>
 __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   using M = Mfma<DT, D, BS>;
   constexpr int NW = 4;
-  __shared__ __attribute__((aligned(16))) float smem[NW * 16 * (D + 2)];
+  __shared__ __attribute__((aligned(16))) float smem[M::kMergeFloats];
 
   const int nhg = (a.group + 15) / 16;
   const int kvh = blockIdx.x / nhg;
@@ -241,13 +242,11 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   const int b = blockIdx.z;
   const int h0 = kvh * a.group + hg * 16;             // first query head of this workgroup
   const int nh = min(16, a.group - hg * 16);          // query heads in this workgroup
-  const int ctx_all = clamp_ctx(a, b);
-  const int sk = skipped_blocks(a, b, ctx_all, BS);
-  const int ctx = ctx_all - sk * BS;  // attended here: tokens sk * BS .. ctx_all - 1
+  const int ctx = clamp_ctx(a, b);
   const int tid = threadIdx.x;
   const size_t q_row0 = size_t(b) * a.num_q_heads + h0;
   if (ctx == 0) {
-    if (part == 0 && !a.partials_only)
+    if (part == 0)
       for (int i = tid; i < nh * D; i += NW * 64) store_elt<DT>(a.out, q_row0 * D + i, 0.f);
     return;
   }
@@ -258,8 +257,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int n16 = lane & 15, g4 = lane >> 4;
-  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks + sk;
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
   const size_t head_off = size_t(kvh) * BS * D * 2;
   const char* kb = static_cast<const char*>(a.k_cache) + head_off;
   const char* vb = static_cast<const char*>(a.v_cache) + head_off;
@@ -267,7 +265,7 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
 
   typename M::vec8 qop[M::KK];
   M::load_q(a, q_row0, nh, lane, qop);
-  const int ncached = cached_blocks(a, b) - sk;
+  const int ncached = cached_blocks(a, b);
   typename M::State st;
   M::init(st);
   const int nchunks = (t1 - t0 + kMfmaChunk - 1) / kMfmaChunk;
@@ -277,17 +275,10 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
   }
   st.l = xor_sum_16_32(st.l);  // m already agrees across the four lane groups
 
-  float* mo = smem;                       // [NW][16][D]
-  float* mm = mo + NW * 16 * D;           // [NW][16]
+  float* mo = smem;                       // [NW][16][MP]
+  float* mm = mo + NW * 16 * M::MP;       // [NW][16]
   float* ml = mm + NW * 16;               // [NW][16]
-#pragma unroll
-  for (int r = 0; r < M::E; ++r)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) mo[(wave * 16 + n16) * D + M::out_d(g4, v, r)] = st.acc[r][v];
-  if (g4 == 0) {
-    mm[wave * 16 + n16] = st.m;
-    ml[wave * 16 + n16] = st.l;
-  }
+  M::merge_store(mo, mm, ml, wave, lane, st);
   __syncthreads();
   for (int i = tid; i < nh * D; i += NW * 64) {
     const int hh = i / D, d = i % D;
@@ -300,13 +291,13 @@ __global__ __launch_bounds__(256) void decode_mfma(DecodeArgs a) {
       for (int w = 0; w < NW; ++w) {
         const float sc = exp2_hw(mm[w * 16 + hh] - Mx);
         L += ml[w * 16 + hh] * sc;
-        O += mo[(w * 16 + hh) * D + d] * sc;
+        O += mo[(w * 16 + hh) * M::MP + M::mcol(d)] * sc;
       }
     }
-    if (nparts == 1 && !a.partials_only) {
+    if (nparts == 1) {
       store_elt<DT>(a.out, (q_row0 + hh) * D + d, L > 0.f ? O / L : 0.f);
     } else {
-      const size_t pi = ((size_t(b) * a.num_q_heads + h0 + hh) * a.max_parts + a.part_base + part);
+      const size_t pi = ((size_t(b) * a.num_q_heads + h0 + hh) * a.max_parts + part);
       a.part_o[pi * D + d] = O;
       if (d == 0) {
         a.part_m[pi] = Mx;
@@ -335,14 +326,10 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partitions(DecodeArgs a
   __shared__ float s_max[kReduceThreads / 64];
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int ctx_all = clamp_ctx(a, b);
-  const int sk = skipped_blocks(a, b, ctx_all, a.block_size);
-  const int ctx = ctx_all - sk * a.block_size;
-  // Slots part_base .. part_base + nparts - 1 hold this call's partitions; in a cascade,
-  // slot 0 holds the shared prefix's partial when the sequence has one.
-  const int p0 = sk > 0 ? 0 : a.part_base;
-  const int p1 = a.part_base + (ctx + a.part_size - 1) / a.part_size;
-  if (!a.partials_only && p1 - p0 <= 1) return;  // a single partition wrote the output itself
+  const int ctx = clamp_ctx(a, b);
+  const int p0 = 0;
+  const int p1 = (ctx + a.part_size - 1) / a.part_size;
+  if (p1 <= 1) return;  // a single partition wrote the output itself
   const size_t base = (size_t(b) * a.num_q_heads + h) * a.max_parts;
   float M = kNegInf;
   for (int p = p0 + tid; p < p1; p += kReduceThreads) M = fmaxf(M, a.part_m[base + p]);
@@ -375,91 +362,217 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partitions(DecodeArgs a
 }
 
 // =========================================================================================
-// Cascade decode, shared-prefix pass: one workgroup of 4 waves per (KV head, tile of 16
-// columns, group).  The columns are the group's (member row, query head of this KV head)
-// pairs, so the group's shared prefix blocks are read once per tile for up to 16 queries
-// instead of once per sequence; the tile's chunks are dealt to the waves in turn and merged
-// through LDS, and the result goes to partial slot 0 of each column's (row, head).
+// Cascade decode: one workgroup of NW waves per (KV head, tile of 16 columns, group).  The
+// columns are (member row, query head of this KV head) pairs of the group.  The workgroup
+// walks one list of 32-token chunks: first the group's shared prefix (the first row's table,
+// read through the caches, since every tile of the group reads it), for all 16 columns at
+// once, then each member's own tokens after the prefix (streamed), with only that member's
+// columns taking part (the others' scores are masked, so their state does not change).  So
+// each column's online softmax sees exactly its own context, the prefix is read once per
+// tile instead of once per sequence, and the waves' states merge through LDS into the
+// output: no partial results leave the workgroup.  The waves take the chunks in turn.
+//
+// Tiles of one group run side by side, so the longest tile sets the time.  When every tile
+// holds whole members (16 a multiple of the group size) and the group has at most
+// kCascadeRankMax members, members are dealt to tiles by the length of their own part:
+// sorted longest first and dealt back and forth (tile 0, 1, .., T-1, T-1, .., 0, 0, ..), so
+// the tiles' totals differ by about one member's length.  Otherwise a tile takes 16
+// consecutive columns.  Either way the assignment depends only on the lengths.
 // =========================================================================================
-template <int DT, int D, int BS>
-__global__ __launch_bounds__(256) void cascade_prefix(DecodeArgs a) {
+constexpr int kCascadeRankMax = 512;
+
+template <int DT, int D, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) void cascade_decode(DecodeArgs a) {
   using M = Mfma<DT, D, BS>;
-  constexpr int NW = 4;
-  __shared__ __attribute__((aligned(16))) float smem[NW * 16 * (D + 2)];
+  constexpr int kMergeFloats = NW * 16 * (M::MP + 2);
+  static_assert(kMergeFloats >= kCascadeRankMax, "the rank keys share the merge buffer");
+  __shared__ __attribute__((aligned(16))) float smem[kMergeFloats];
+  __shared__ int s_seg[18];   // chunk offsets: [0] = 0, [1] = prefix end, [k + 2] = slot k end
+  __shared__ int s_mem[16];   // member (row - first row of the group) in slot k of the tile
+  __shared__ int s_ctx[16];   // its context length
+  __shared__ int s_sk[16];    // its shared blocks (walked in the prefix part)
 
   const int kvh = blockIdx.x;
   const int g = blockIdx.z;
   const int m0 = min(max(a.group_start[g], 0), a.num_seqs);       // first row of the group
   const int m1 = min(max(a.group_start[g + 1], m0), a.num_seqs);  // one past its last row
-  const int cols = (m1 - m0) * a.group;
-  const int c0 = blockIdx.y * 16;
-  if (m1 - m0 < 1 || c0 >= cols) return;
-  const int sk = skipped_blocks(a, m0, clamp_ctx(a, m0), BS);  // shared blocks of the group
-  if (sk == 0) return;
-  const int nc = min(16, cols - c0);
-  const int t1 = sk * BS;
+  const int nmem = m1 - m0;
+  const int cols = nmem * a.group;
+  const int ntiles = (cols + 15) / 16;
+  if (int(blockIdx.y) >= ntiles) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int n16 = lane & 15, g4 = lane >> 4;
-
-  // Q^T operand: column n16 is (row m0 + c / group, head kvh * group + c % group), c = c0 + n16.
-  typename M::vec8 qop[M::KK];
-  {
-    const int c = c0 + (n16 < nc ? n16 : 0);
-    const size_t qrow = size_t(m0 + c / a.group) * a.num_q_heads + kvh * a.group + c % a.group;
-    const char* qp = static_cast<const char*>(a.q) + qrow * D * 2;
-#pragma unroll
-    for (int kk = 0; kk < M::KK; ++kk) {
-      const uint4 w = n16 < nc ? *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2)
-                               : make_uint4(0, 0, 0, 0);
-      qop[kk] = __builtin_bit_cast(typename M::vec8, w);
-    }
-  }
-  const int32_t* tbl = a.tables + size_t(m0) * a.max_blocks;  // every member's first sk entries
+  // The group's shared blocks: the first row's count, at most that row's full blocks.  A
+  // member whose context ends earlier shares only its own full blocks of them.
+  const int ctx_first = clamp_ctx(a, m0);
+  const int skg = min(max(uniform(a.skip[m0]), 0), ctx_first / BS);
   const size_t head_off = size_t(kvh) * BS * D * 2;
   const char* kb = static_cast<const char*>(a.k_cache) + head_off;
   const char* vb = static_cast<const char*>(a.v_cache) + head_off;
   const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
-  typename M::State st;
-  M::init(st);
-  const int nchunks = (t1 + kMfmaChunk - 1) / kMfmaChunk;
-  for (int c = wave; c < nchunks; c += NW)  // the prefix is re-read by every tile: cached loads
-    M::chunk(a, tbl, kb, vb, blk_bytes, c * kMfmaChunk, t1, true, lane, qop, st);
-  st.l = xor_sum_16_32(st.l);
+  const int32_t* tbl_first = a.tables + size_t(m0) * a.max_blocks;
+  auto own_chunks = [&](int ctx) { return (ctx - min(skg, ctx / BS) * BS + kMfmaChunk - 1) / kMfmaChunk; };
 
-  float* mo = smem;              // [NW][16][D]
-  float* mm = mo + NW * 16 * D;  // [NW][16]
-  float* ml = mm + NW * 16;      // [NW][16]
-#pragma unroll
-  for (int r = 0; r < M::E; ++r)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) mo[(wave * 16 + n16) * D + M::out_d(g4, v, r)] = st.acc[r][v];
-  if (g4 == 0) {
-    mm[wave * 16 + n16] = st.m;
-    ml[wave * 16 + n16] = st.l;
+  const bool dealt = 16 % a.group == 0 && ntiles > 1 && nmem <= kCascadeRankMax;
+  int* s_key = reinterpret_cast<int*>(smem);  // [nmem] own chunks per member (dealt tiles)
+  if (dealt) {
+    for (int j = tid; j < nmem; j += NW * 64) s_key[j] = own_chunks(clamp_ctx(a, m0 + j));
+    __syncthreads();
   }
-  __syncthreads();
-  for (int i = tid; i < nc * D; i += NW * 64) {
-    const int cc = i / D, d = i % D;
-    float Mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, mm[w * 16 + cc]);
-    float L = 0.f, O = 0.f;
-    if (Mx != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float sc = exp2_hw(mm[w * 16 + cc] - Mx);
-        L += ml[w * 16 + cc] * sc;
-        O += mo[(w * 16 + cc) * D + d] * sc;
+
+  for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {  // every tile, whatever the grid
+    // Members of the tile, in slots 0 .. nm - 1; column n16 of a dealt tile is slot
+    // n16 / group, head n16 % group; of a consecutive tile, column c0 + n16 of the group.
+    int nm, c0 = 0, mf = 0;
+    if (dealt) {
+      const int rounds = nmem / ntiles, rem = nmem % ntiles;
+      nm = rounds + ((rounds & 1) ? ti >= ntiles - rem : ti < rem);
+      // rank of member j: the members before it in the order (longer first, then by row).
+      // Four adjacent threads count a quarter of the keys each.
+      for (int base = 0; base < nmem; base += NW * 16) {
+        const int j = base + tid / 4, part = tid & 3;
+        const int kj = j < nmem ? s_key[j] : 0;
+        int rank = 0;
+        for (int k = part; k < nmem; k += 4) {
+          const int kk = s_key[k];
+          rank += kk > kj || (kk == kj && k < j);
+        }
+        rank += __shfl_xor(rank, 1, 64);
+        rank += __shfl_xor(rank, 2, 64);
+        const int round = rank / ntiles, pos = rank % ntiles;
+        if (j < nmem && part == 0 && ((round & 1) ? ntiles - 1 - pos : pos) == ti) s_mem[round] = j;
+      }
+    } else {
+      c0 = ti * 16;
+      mf = c0 / a.group;
+      nm = (min(c0 + 16, cols) - 1) / a.group - mf + 1;
+      if (tid < nm) s_mem[tid] = mf + tid;
+    }
+    __syncthreads();
+    if (tid < nm) {
+      const int ctx = clamp_ctx(a, m0 + s_mem[tid]);
+      s_ctx[tid] = ctx;
+      s_sk[tid] = min(skg, ctx / BS);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int off = (skg * BS + kMfmaChunk - 1) / kMfmaChunk;
+      s_seg[0] = 0;
+      s_seg[1] = off;
+      for (int k = 0; k < nm; ++k) {
+        off += (s_ctx[k] - s_sk[k] * BS + kMfmaChunk - 1) / kMfmaChunk;
+        s_seg[k + 2] = off;
       }
     }
-    const int c = c0 + cc;
-    const size_t pi = (size_t(m0 + c / a.group) * a.num_q_heads + kvh * a.group + c % a.group) * a.max_parts;
-    a.part_o[pi * D + d] = O;
-    if (d == 0) {
-      a.part_m[pi] = Mx;
-      a.part_l[pi] = L;
+    __syncthreads();
+
+    // This lane's column: tile slot jm, query head kvh * group + hq.
+    int jm, hq;
+    if (dealt) {
+      jm = n16 / a.group;
+      hq = n16 % a.group;
+      if (jm >= nm) jm = -1;
+    } else {
+      const int c = c0 + n16;
+      jm = c < cols ? c / a.group - mf : -1;
+      hq = c % a.group;
+    }
+    const bool cv = jm >= 0;
+    const int pre_lim = cv ? s_sk[jm] * BS - 1 : -1;  // the prefix keys this column sees
+    int pre_min = pre_lim;                            // the least of them (wave-uniform)
+#pragma unroll
+    for (int sh = 1; sh < 16; sh <<= 1) pre_min = min(pre_min, __shfl_xor(pre_min, sh, 64));
+    typename M::vec8 qop[M::KK];
+    {
+      const size_t qrow = size_t(m0 + s_mem[cv ? jm : 0]) * a.num_q_heads + kvh * a.group + (cv ? hq : 0);
+      const char* qp = static_cast<const char*>(a.q) + qrow * D * 2;
+#pragma unroll
+      for (int kk = 0; kk < M::KK; ++kk) {
+        const uint4 w = cv ? *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2)
+                           : make_uint4(0, 0, 0, 0);
+        qop[kk] = __builtin_bit_cast(typename M::vec8, w);
+      }
+    }
+    typename M::State st;
+    M::init(st);
+    const int total = s_seg[nm + 1];
+    const int npre = s_seg[1];
+    // The tile's tables, one entry per lane, read back with wave-uniform lane reads: the
+    // chunk loop then touches no LDS.
+    const int seg_l = s_seg[lane < nm + 2 ? lane : 0];
+    const int row_l = lane < nm ? m0 + s_mem[lane] : m0;
+    const int ctx_l = lane < nm ? s_ctx[lane] : 0;
+    const int sk_l = lane < nm ? s_sk[lane] : 0;
+    int kcur = 0;  // slot of the last member chunk looked up (chunks come in increasing order)
+    // Chunk ch: of the shared prefix (every column, through the caches), or of slot k's own
+    // tokens (only its columns, streamed).  All of it is wave-uniform but the column limit.
+    struct Work {
+      const int32_t* tbl;
+      int cs, t1, lim, lim_min;
+      bool pre;
+    };
+    auto lane_val = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };
+    // The prefix chunks (cache hits after the first tile's read) are spread evenly over the
+    // list, so that while some waves read them the others keep the memory stream going:
+    // position ch holds prefix chunk floor(ch * npre / total) when that value steps up
+    // between ch and ch + 1, and otherwise own chunk ch - floor((ch + 1) * npre / total).
+    auto work = [&](int ch) {
+      const int p0 = int((int64_t(ch) * npre) / total), p1 = int((int64_t(ch + 1) * npre) / total);
+      Work w{tbl_first, p0 * kMfmaChunk, skg * BS, pre_lim, pre_min, p1 > p0};
+      if (!w.pre) {
+        const int sc = ch - p1 + npre;  // own chunks before this one, plus npre
+        int k = kcur;
+        while (sc >= lane_val(seg_l, k + 2)) ++k;
+        kcur = k;
+        const int skk = lane_val(sk_l, k);
+        w.tbl = a.tables + size_t(lane_val(row_l, k)) * a.max_blocks + skk;
+        w.cs = (sc - lane_val(seg_l, k + 1)) * kMfmaChunk;
+        w.t1 = lane_val(ctx_l, k) - skk * BS;
+        w.lim = jm == k ? INT_MAX : -1;
+        w.lim_min = -1;
+      }
+      return w;
+    };
+    for (int ch = wave; ch < total; ch += NW) {
+      const Work w = work(ch);
+      typename M::Chunk ck;
+      M::load(a, w.tbl, kb, vb, blk_bytes, w.cs, w.t1, w.pre, lane, ck);
+      M::template compute<true>(a, ck, w.cs, lane, qop, st, w.lim, w.lim_min);
+    }
+    st.l = xor_sum_16_32(st.l);  // m already agrees across the four lane groups
+
+    __syncthreads();  // the rank keys in smem have been read
+    float* mo = smem;                   // [NW][16][MP]
+    float* mm = mo + NW * 16 * M::MP;   // [NW][16]
+    float* ml = mm + NW * 16;           // [NW][16]
+    M::merge_store(mo, mm, ml, wave, lane, st);
+    __syncthreads();
+    const int nc = dealt ? nm * a.group : min(16, cols - c0);
+    for (int i = tid; i < nc * D; i += NW * 64) {
+      const int cc = i / D, d = i % D;
+      float Mx = kNegInf;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, mm[w * 16 + cc]);
+      float L = 0.f, O = 0.f;
+      if (Mx != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float sc = exp2_hw(mm[w * 16 + cc] - Mx);
+          L += ml[w * 16 + cc] * sc;
+          O += mo[(w * 16 + cc) * M::MP + M::mcol(d)] * sc;
+        }
+      }
+      const int slot = dealt ? cc / a.group : (c0 + cc) / a.group - mf;
+      const int head = dealt ? cc % a.group : (c0 + cc) % a.group;
+      const size_t orow = size_t(m0 + s_mem[slot]) * a.num_q_heads + kvh * a.group + head;
+      store_elt<DT>(a.out, orow * D + d, L > 0.f ? O / L : 0.f);
+    }
+    __syncthreads();  // the next tile reuses the LDS
+    if (dealt) {  // the merge overwrote the rank keys
+      for (int j = tid; j < nmem; j += NW * 64) s_key[j] = own_chunks(clamp_ctx(a, m0 + j));
+      __syncthreads();
     }
   }
 }
@@ -564,12 +677,18 @@ kernel_fn pick_reduce(pkv_dtype dt, int d) {
          : dt == PKV_F16 ? pick_reduce<DT_F16>(d) : pick_reduce<DT_BF16>(d);
 }
 
+// Waves per cascade workgroup.  A batch sharing one prefix has few (KV head, column tile)
+// workgroups (256 for 128 sequences of 32 heads), so each carries several waves to keep
+// loads in flight.  Measured on the shared-prefix batch: 8 waves 0.114 ms, 4 waves 0.128 ms;
+// at 16 the register budget (128 per lane) forces spills (0.17 ms).
+constexpr int kCascadeWaves = 8;
+
 template <int DT, int D>
 kernel_fn pick_cascade_bs(int bs) {
   switch (bs) {
-    case 8: return cascade_prefix<DT, D, 8>;
-    case 16: return cascade_prefix<DT, D, 16>;
-    case 32: return cascade_prefix<DT, D, 32>;
+    case 8: return cascade_decode<DT, D, 8, kCascadeWaves>;
+    case 16: return cascade_decode<DT, D, 16, kCascadeWaves>;
+    case 32: return cascade_decode<DT, D, 32, kCascadeWaves>;
   }
   return nullptr;
 }
@@ -581,11 +700,42 @@ kernel_fn pick_cascade(pkv_dtype dt, int d, int bs) {
   return nullptr;
 }
 
-// Partitions of the per-sequence (suffix) pass of a cascade decode, plus slot 0 for the
-// shared prefix.
-int64_t cascade_slots(int32_t partition_size, int32_t max_context_len, int64_t rows) {
-  const int p = resolve_partition(partition_size, max_context_len, rows);
-  return 1 + (int64_t(max_context_len) + p - 1) / p;
+// PKV_DEBUG=1 in the environment: before a decode is enqueued, wait for the stream, read
+// the lengths and tables back and check them; a violation fails the call with
+// PKV_ERR_INVALID_ARG (and a message in pkv_last_error) before anything is enqueued.  Off by
+// default: the check synchronises and copies every call.
+bool debug_checks() {
+  const char* e = getenv("PKV_DEBUG");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+pkv_status debug_check_tables(const int32_t* tables_d, const int32_t* lens_d, int32_t num_seqs,
+                              int32_t max_blocks, int32_t block_size, int32_t num_blocks,
+                              int32_t ctx_limit, hipStream_t stream) {
+  std::vector<int32_t> lens(num_seqs), tables(size_t(num_seqs) * max_blocks);
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(lens.data(), lens_d, lens.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(tables.data(), tables_d, tables.size() * 4, hipMemcpyDeviceToHost) != hipSuccess) {
+    snprintf(g_last_error, sizeof(g_last_error), "PKV_DEBUG: %s", hipGetErrorString(hipGetLastError()));
+    return PKV_ERR_HIP;
+  }
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t n = lens[b];
+    if (n < 0 || n > ctx_limit) {
+      snprintf(g_last_error, sizeof(g_last_error),
+               "PKV_DEBUG: context_lens[%d] = %d outside [0, %d]", b, n, ctx_limit);
+      return PKV_ERR_INVALID_ARG;
+    }
+    for (int32_t t = 0; t < (n + block_size - 1) / block_size; ++t) {
+      const int32_t id = tables[size_t(b) * max_blocks + t];
+      if (id < 0 || id >= num_blocks) {
+        snprintf(g_last_error, sizeof(g_last_error),
+                 "PKV_DEBUG: block_tables[%d][%d] = %d outside [0, %d)", b, t, id, num_blocks);
+        return PKV_ERR_INVALID_ARG;
+      }
+    }
+  }
+  return PKV_OK;
 }
 
 }  // namespace
@@ -678,6 +828,12 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
   if (!k || !r) return PKV_ERR_UNSUPPORTED;
   const dim3 grid{unsigned(rows), unsigned(max_parts), unsigned(num_seqs)};
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    const pkv_status ds = debug_check_tables(block_tables, context_lens, num_seqs,
+                                             max_blocks_per_seq, block_size, num_blocks,
+                                             ctx_limit, st);
+    if (ds != PKV_OK) return ds;
+  }
   clear_stale_error();
   hipLaunchKernelGGL(k, grid, dim3(mfma ? 256 : 64 * kValuWaves), 0, st, a);
   if (launch_status("paged_attention_decode") != PKV_OK) return PKV_ERR_HIP;
@@ -691,14 +847,11 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
 size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                    pkv_dtype dtype, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      block_size <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads != 0 ||
-      !valid_dtype(dtype) || partition_size < -1)
-    return 0;
-  const int64_t rows = rows_per_seq(dtype, num_q_heads, num_kv_heads, head_dim, block_size);
-  const int64_t slots = cascade_slots(partition_size, max_context_len > 0 ? max_context_len : 1,
-                                      int64_t(num_seqs) * rows);
-  return size_t(num_seqs) * num_q_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
+  // Every workgroup of the cascade kernel merges its waves in LDS and writes the output
+  // itself: no partial results, no workspace.
+  (void)num_seqs, (void)num_q_heads, (void)num_kv_heads, (void)head_dim, (void)block_size;
+  (void)max_context_len, (void)dtype, (void)partition_size;
+  return 0;
 }
 
 pkv_status pkv_paged_attention_cascade(void* out, const void* q, const void* k_cache,
@@ -711,6 +864,7 @@ pkv_status pkv_paged_attention_cascade(void* out, const void* q, const void* k_c
                                        int32_t max_blocks_per_seq, int32_t max_context_len,
                                        float scale, pkv_dtype dtype, int32_t partition_size,
                                        void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace, (void)workspace_bytes;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0 || num_groups < 0 || max_group_size < 0)
     return PKV_ERR_INVALID_ARG;
@@ -720,26 +874,21 @@ pkv_status pkv_paged_attention_cascade(void* out, const void* q, const void* k_c
   if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
     return PKV_ERR_INVALID_ARG;
   if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
-  kernel_fn pk = pick_cascade(dtype, head_dim, block_size);
-  if (!pk) return PKV_ERR_UNSUPPORTED;  // the shared-prefix pass runs on matrix cores
-  if (num_seqs == 0) return PKV_OK;
+  kernel_fn k = pick_cascade(dtype, head_dim, block_size);
+  if (!k) return PKV_ERR_UNSUPPORTED;  // the cascade kernel runs on matrix cores
+  if (num_seqs == 0 || num_groups == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !shared_blocks ||
-      (num_groups > 0 && !group_start))
+      !group_start)
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_ERR_INVALID_ARG;
+  if (num_groups > 65535) return PKV_ERR_UNSUPPORTED;
   const int64_t cap = int64_t(max_blocks_per_seq) * block_size;
   const int group = num_q_heads / num_kv_heads;
-  const bool mfma = use_mfma(dtype, head_dim, block_size, group);
-  const int64_t rows = rows_per_seq(dtype, num_q_heads, num_kv_heads, head_dim, block_size);
-  const int mc = max_context_len > 0 ? max_context_len : 1;
-  const int part = resolve_partition(partition_size, mc, int64_t(num_seqs) * rows);
-  const int64_t slots = cascade_slots(partition_size, mc, int64_t(num_seqs) * rows);
-  const int64_t tiles = (int64_t(max_group_size) * group + 15) / 16;
-  if (slots > 65535 || num_seqs > 65535 || num_groups > 65535 || tiles > 65535)
-    return PKV_ERR_UNSUPPORTED;
-  const size_t need = size_t(num_seqs) * num_q_heads * slots * (size_t(head_dim) + 2) * sizeof(float);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
+  // Column tiles per group: enough for max_group_size members; a workgroup also takes every
+  // gridDim.y-th tile after its own, so a larger group is still covered in full.
+  int64_t tiles = (int64_t(max_group_size) * group + 15) / 16;
+  tiles = tiles < 1 ? 1 : (tiles > 65535 ? 65535 : tiles);
 
   DecodeArgs a = {};
   a.out = out;
@@ -754,34 +903,15 @@ pkv_status pkv_paged_attention_cascade(void* out, const void* q, const void* k_c
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks_per_seq;
   a.ctx_limit = int32_t(max_context_len < cap ? max_context_len : cap);
-  a.part_size = part;
-  a.max_parts = int(slots);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.skip = shared_blocks;
   a.group_start = group_start;
   a.num_seqs = num_seqs;
   a.block_size = block_size;
-  a.part_base = 1;
-  a.partials_only = 1;
-  float* w = static_cast<float*>(workspace);
-  a.part_o = w;
-  a.part_m = w + size_t(num_seqs) * num_q_heads * slots * head_dim;
-  a.part_l = a.part_m + size_t(num_seqs) * num_q_heads * slots;
-  kernel_fn k = pick_decode(dtype, head_dim, block_size, mfma);
-  kernel_fn r = pick_reduce(dtype, head_dim);
-  if (!k || !r) return PKV_ERR_UNSUPPORTED;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   clear_stale_error();
-  if (num_groups > 0 && tiles > 0) {
-    hipLaunchKernelGGL(pk, dim3(unsigned(num_kv_heads), unsigned(tiles), unsigned(num_groups)),
-                       dim3(256), 0, st, a);
-    if (launch_status("cascade_prefix") != PKV_OK) return PKV_ERR_HIP;
-  }
-  hipLaunchKernelGGL(k, dim3(unsigned(rows), unsigned(slots - 1), unsigned(num_seqs)),
-                     dim3(mfma ? 256 : 64 * kValuWaves), 0, st, a);
-  if (launch_status("paged_attention_decode") != PKV_OK) return PKV_ERR_HIP;
-  hipLaunchKernelGGL(r, dim3(unsigned(num_q_heads), unsigned(num_seqs)), dim3(kReduceThreads), 0, st, a);
-  return launch_status("reduce_partitions");
+  hipLaunchKernelGGL(k, dim3(unsigned(num_kv_heads), unsigned(tiles), unsigned(num_groups)),
+                     dim3(64 * kCascadeWaves), 0, static_cast<hipStream_t>(stream), a);
+  return launch_status("paged_attention_cascade");
 }
 
 }  // extern "C"

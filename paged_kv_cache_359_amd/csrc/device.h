@@ -214,16 +214,12 @@ struct DecodeArgs {
   int32_t part_size;  // tokens per partition (multiple of 16 and of block_size)
   int32_t max_parts;
   float scale_log2;   // scale * log2(e): scores are kept in the log2 domain
-  // Cascade decode.  skip (nullable): leading table entries of sequence b attended by the
-  // group's prefix pass, not here.  group_start: [G + 1] rows of each group.  Partials of
-  // this call's partitions go to slots part_base + p; partials_only: write partials even
-  // for a single partition (the merge writes the output).
+  // Cascade decode.  skip: leading table entries of each row that its group shares (the
+  // group's first row's count is used); group_start: [G + 1] rows of each group.
   const int32_t* skip;
   const int32_t* group_start;
   int32_t num_seqs;
   int32_t block_size;
-  int32_t part_base;
-  int32_t partials_only;
 };
 
 // Number of leading table entries of sequence b to read through the caches (wave-uniform).
@@ -237,12 +233,5 @@ __device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, int b) {
   return n < a.ctx_limit ? n : a.ctx_limit;
 }
 
-// Leading blocks of sequence b that another pass attends (0 without a skip array), at most
-// the full blocks of its context ctx (wave-uniform).
-__device__ __forceinline__ int skipped_blocks(const DecodeArgs& a, int b, int ctx, int bs) {
-  if (!a.skip) return 0;
-  const int k = uniform(a.skip[b]);
-  return k < 0 ? 0 : min(k, ctx / bs);
-}
 
 }  // namespace pkv

@@ -80,11 +80,20 @@ struct Mfma {
     bool need_mask;  // wave-uniform: some row of this chunk does not exist
   };
 
-  // kb / vb: pool base plus this KV head's offset.  cs: a multiple of 16.  cached: read this
-  // chunk through the caches (wave-uniform).
-  __device__ static void load(const DecodeArgs& a, const int32_t* tbl, const char* kb,
-                              const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
-                              int lane, Chunk& ck) {
+  // A chunk's loads as issued, before the V^T operands are formed.
+  struct Raw {
+    uint4 kr[2][KK];
+    uint32_t vr[2][4][E / 2];
+    bool vok[2][4];
+    bool need_mask;  // wave-uniform: some row of this chunk does not exist
+  };
+
+  // Issues the loads of the chunk starting at token cs (tokens >= t1 are masked).  kb / vb:
+  // pool base plus this KV head's offset.  cs: a multiple of 16.  cached: read this chunk
+  // through the caches (wave-uniform).
+  __device__ static void issue(const DecodeArgs& a, const int32_t* tbl, const char* kb,
+                               const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
+                               int lane, Raw& r) {
     const int n16 = lane & 15, g4 = lane >> 4;
     bool need_mask = cs + kMfmaChunk > t1;  // wave-uniform
     int ids[2][NBH];
@@ -109,24 +118,23 @@ struct Mfma {
         const int tv = cs + 16 * hf + 4 * g4 + i;
         const int idv = ids[hf][NBH > 1 ? (4 * g4 + i) / BS : 0];
         const bool vv = (unsigned)idv < (unsigned)a.num_blocks;
-        ck.vok[hf][i] = vv && tv < t1;
+        r.vok[hf][i] = vv && tv < t1;
         vp[hf][i] = vb + size_t(vv ? idv : 0) * blk_bytes + size_t(tv % BS) * D * 2 + E * n16 * 2;
       }
     }
-    uint32_t vr[2][4][E / 2];
     if (cached) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) ck.kr[hf][kk] = load_cached(kp[hf] + 32 * kk * 2);
+        for (int kk = 0; kk < KK; ++kk) r.kr[hf][kk] = load_cached(kp[hf] + 32 * kk * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (E == 8) {
             const uint4 w = load_cached(vp[hf][i]);
-            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
+            r.vr[hf][i][0] = w.x, r.vr[hf][i][1] = w.y, r.vr[hf][i][2] = w.z, r.vr[hf][i][3] = w.w;
           } else {
             const uint2 w = load_cached8(vp[hf][i]);
-            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
+            r.vr[hf][i][0] = w.x, r.vr[hf][i][1] = w.y;
           }
         }
       }
@@ -134,30 +142,52 @@ struct Mfma {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) ck.kr[hf][kk] = load_stream(kp[hf] + 32 * kk * 2);
+        for (int kk = 0; kk < KK; ++kk) r.kr[hf][kk] = load_stream(kp[hf] + 32 * kk * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (E == 8) {
             const uint4 w = load_stream(vp[hf][i]);
-            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y, vr[hf][i][2] = w.z, vr[hf][i][3] = w.w;
+            r.vr[hf][i][0] = w.x, r.vr[hf][i][1] = w.y, r.vr[hf][i][2] = w.z, r.vr[hf][i][3] = w.w;
           } else {
             const uint2 w = load_stream8(vp[hf][i]);
-            vr[hf][i][0] = w.x, vr[hf][i][1] = w.y;
+            r.vr[hf][i][0] = w.x, r.vr[hf][i][1] = w.y;
           }
         }
       }
     }
-    ck.need_mask = need_mask;
-    if (need_mask) {
+    r.need_mask = need_mask;
+  }
+
+  // Forms the chunk from its issued loads: rows of tokens that do not exist are zeroed (unused
+  // slots may hold anything) and V is transposed into the operands of the product.
+  __device__ static void finish(Raw& r, Chunk& ck) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) ck.kr[hf][kk] = r.kr[hf][kk];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ck.vok[hf][i] = r.vok[hf][i];
+    ck.need_mask = r.need_mask;
+    if (r.need_mask) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (!ck.vok[hf][i])
+          if (!r.vok[hf][i])
 #pragma unroll
-            for (int q = 0; q < E / 2; ++q) vr[hf][i][q] = 0u;  // unused slots may hold anything
+            for (int q = 0; q < E / 2; ++q) r.vr[hf][i][q] = 0u;
     }
-    make_vop(vr, ck);
+    make_vop(r.vr, ck);
+  }
+
+  __device__ static void load(const DecodeArgs& a, const int32_t* tbl, const char* kb,
+                              const char* vb, size_t blk_bytes, int cs, int t1, bool cached,
+                              int lane, Chunk& ck) {
+    Raw r;
+    issue(a, tbl, kb, vb, blk_bytes, cs, t1, cached, lane, r);
+    finish(r, ck);
   }
 
   // V^T operand of output tile r: element r of each of the lane's eight token rows.
@@ -280,6 +310,29 @@ struct Mfma {
 
   // Output d of element (r, v) of the lane's accumulators: E * (4 * (lane / 16) + v) + r.
   __device__ static int out_d(int g4, int v, int r) { return E * (4 * g4 + v) + r; }
+
+  // Cross-wave merge buffer in LDS: one row of MP floats per (wave, column), output d at
+  // row offset mcol(d).  One store instruction of the merge writes element (v, r) of all 64
+  // lanes: 16 rows times 4 column groups 4E apart.  The pitch and the one-float shift per
+  // 32 columns put those 64 floats in distinct banks of a 64-bank LDS (two per bank, the
+  // least possible, with 32 banks); unpadded rows of D floats put all 16 rows in one bank.
+  static constexpr int MP = D == 128 ? D + 4 : D + 1;
+  __device__ static int mcol(int d) { return D == 128 ? d + (d >> 5) : d; }
+  static constexpr int kMergeFloats = 4 * 16 * (MP + 2);  // four waves: rows, then m and l
+
+  // Stores this wave's state for the merge: mo rows, then mm and ml ([NW][16] each).
+  __device__ static void merge_store(float* mo, float* mm, float* ml, int wave, int lane,
+                                     const State& st) {
+    const int n16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < E; ++r)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mo[(wave * 16 + n16) * MP + mcol(out_d(g4, v, r))] = st.acc[r][v];
+    if (g4 == 0) {
+      mm[wave * 16 + n16] = st.m;
+      ml[wave * 16 + n16] = st.l;
+    }
+  }
 };
 
 }  // namespace pkv

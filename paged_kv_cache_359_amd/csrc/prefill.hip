@@ -155,10 +155,14 @@ constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kPrefillRows = kPrefillWaves * 16 * kPrefillTiles;  // new tokens per workgroup
 
 // Kernel forms.  kExact: P.V in the cache's type (bf16 with P split into two products).
-// kFast (bf16 only): V staged in LDS as fp16 (round to nearest: exact for bf16 values below
-// 2^16 in magnitude; larger ones become inf) and P.V as one fp16 product.  An inf in any V
+// kFast (bf16 only): V staged in LDS as fp16 (round to nearest) and P.V as one fp16
+// product.  The conversion is exact for bf16 magnitudes in fp16's normal range [2^-14,
+// 2^16) (8 significant bits fit in 11).  Below 2^-14 fp16 subnormals keep fewer bits and
+// magnitudes below 2^-25 become 0: an absolute error of at most 2^-25 per element, which
+// moves an output by at most 2^-25 as well (it is a convex combination of the rows).  From
+// 2^16 up a value becomes inf.  An inf in any V
 // row the walk stages makes an accumulator of every column it meets inf or NaN (0 * inf is
-// NaN), so when every column of the workgroup ends finite the fp16 staging was exact and
+// NaN), so when every column of the workgroup ends finite no value overflowed and
 // the outputs are stored; otherwise the workgroup stores only a NaN in element 0 of its
 // first row.  kFixup (bf16 only, launched after kFast over the same grid): a workgroup
 // whose element 0 of its first row is finite returns at once; any other walks its keys in
@@ -320,8 +324,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
       }
     }
   };
-  // F16PV: V rows go to LDS as fp16 (round to nearest; exact for bf16 values below 2^16
-  // in magnitude, and larger ones become inf).
+  // F16PV: V rows go to LDS as fp16 (round to nearest: exact for bf16 magnitudes in
+  // [2^-14, 2^16), off by at most 2^-25 below that range, inf from 2^16 up).
   auto stash = [&](int buf, auto f16pv) {
     constexpr bool F16PV = decltype(f16pv)::value;
 #pragma unroll

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import paged_kv_cache_359_amd as pkv
@@ -291,22 +292,66 @@ def cascade(**kw):
     (dict(shared=None), 1),
     (dict(gs=None), 1),                # groups given but no group_start
     (dict(q=MIS), 1),
-    (dict(), 6),                       # the cascade always needs a workspace
-    (dict(ws=FAKE, wsb=100), 6),
-    (dict(ws=MIS, wsb=1 << 20), 6),    # misaligned workspace
+    (dict(tables=None), 1),
+    (dict(ng=70000), 5),               # grid limit
     (dict(nseq=0), 0),                 # nothing to do
+    (dict(ng=0, gs=None), 0),          # no groups: nothing to do
 ])
 def test_cascade_validation(kw, status):
     assert cascade(**kw) == status
 
 
 def test_cascade_workspace_bytes():
+    # Each workgroup merges its waves in LDS and writes the output: no workspace.
     f = pkv.pkv_cascade_workspace_bytes
-    # Slot 0 (shared prefix) plus the per-sequence partitions, each (m, l, o).
-    assert f(2, 4, 4, 128, 16, 512, "f16", 512) == 2 * 4 * 2 * 130 * 4
-    assert f(2, 4, 4, 128, 16, 4096, "f16", 512) == 2 * 4 * 9 * 130 * 4
-    assert f(0, 4, 4, 128, 16, 512, "f16", 512) == 0
-    assert f(2, 6, 4, 128, 16, 512, "f16", 512) == 0
+    assert f(2, 4, 4, 128, 16, 512, "f16", 512) == 0
+    assert f(128, 32, 32, 128, 16, 4096, "f16", -1) == 0
+
+
+def append(**kw):
+    args = dict(key=FAKE, value=FAKE, slots=FAKE, rows=None, pos=FAKE, n=3, kc=FAKE, vc=FAKE,
+                tables=FAKE, lens=FAKE, nrows=4, maxb=8, hkv=4, d=128, bs=16, nblocks=100,
+                dtype=1, stream=None)
+    args.update(kw)
+    a = args
+    return lib().pkv_append_and_cache(a["key"], a["value"], a["slots"], a["rows"], a["pos"], a["n"],
+                                      a["kc"], a["vc"], a["tables"], a["lens"], a["nrows"],
+                                      a["maxb"], a["hkv"], a["d"], a["bs"], a["nblocks"],
+                                      a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), 0),                    # nothing to write
+    (dict(n=0, key=None, slots=None), 0),
+    (dict(n=-1), 1),
+    (dict(key=None), 1),
+    (dict(slots=None), 1),
+    (dict(kc=MIS), 1),                 # misaligned pool
+    (dict(lens=None), 1),              # tables without lengths
+    (dict(pos=None), 1),               # tables without positions
+    (dict(maxb=0), 1),
+    (dict(nrows=-1), 1),
+    (dict(hkv=0), 1),
+    (dict(nblocks=0), 1),
+    (dict(dtype=9), 1),
+    (dict(d=4), 5),                    # 8-byte fp16 rows: not whole 16-byte vectors
+])
+def test_append_and_cache_validation(kw, status):
+    assert append(**kw) == status
+
+
+def test_seq_lengths():
+    a = pkv.PkvAlloc(16, 4)
+    a.pkv_seq_add(7, 9)
+    a.pkv_seq_add(3, 0)
+    a.pkv_seq_append([7, 3])
+    assert a.pkv_seq_lengths([3, 7]).tolist() == [1, 10]
+    out = np.full(2, -5, np.int32)
+    with pytest.raises(pkv.PkvError) as e:
+        a.pkv_seq_lengths([7, 11], out)
+    assert e.value.name == "PKV_ERR_UNKNOWN_SEQ" and out.tolist() == [-5, -5]
+    assert a.pkv_seq_lengths([]).size == 0
+    assert lib().pkv_seq_lengths(None, None, 0, None) == 1
 
 
 @pytest.mark.parametrize("args,status", [

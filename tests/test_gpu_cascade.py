@@ -1,10 +1,10 @@
 """Cascade decode on the GPU against the oracle's plain attention.
 
-The cascade reads each group's shared prefix once (matrix cores, the group's queries as
-columns), attends each sequence's remaining context with the decode kernels, and merges the
-two by log-sum-exp.  It computes the same quantity as plain paged decode, so the bar is the
-attention bar against the fp64 oracle (and the plain decode must meet it too).  Groups come
-from pkv_prefix_groups on the library's allocator.
+The cascade reads each group's shared prefix once per 16 (member, query head) columns on
+matrix cores, then each member's own blocks with only that member's columns taking part.  It
+computes the same quantity as plain paged decode, so the bar is the attention bar against
+the fp64 oracle (and the plain decode must meet it too).  Groups come from
+pkv_prefix_groups on the library's allocator.
 """
 import numpy as np
 import pytest
@@ -20,7 +20,8 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def cascade(alloc, rows, q, k_cache, v_cache, scale, partition_size=-1):
+def cascade(alloc, rows, q, k_cache, v_cache, scale, partition_size=-1, max_group_size=None,
+            shared_override=None):
     """Runs the cascade for batch rows ``rows`` (in that order) and returns (out, groups)."""
     n, hkv, bs, d = k_cache.shape
     starts, shared = alloc.pkv_prefix_groups(rows)
@@ -29,13 +30,16 @@ def cascade(alloc, rows, q, k_cache, v_cache, scale, partition_size=-1):
     mc = int(lens.max())
     nb, hq, _ = q.shape
     ws_n = pkv.pkv_cascade_workspace_bytes(nb, hq, hkv, d, bs, mc, q.dtype, partition_size)
-    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
     out = torch.empty_like(q)
     gsz = int(np.max(np.diff(starts))) if starts.size > 1 else 0
+    if max_group_size is not None:
+        gsz = max_group_size
+    sh = shared if shared_override is None else shared_override
     pkv.pkv_paged_attention_cascade(out, q, k_cache, v_cache, torch.from_numpy(tables).cuda(),
                                     torch.from_numpy(lens).cuda(), torch.from_numpy(starts).cuda(),
-                                    torch.from_numpy(shared).cuda(), gsz, mc, scale, ws,
-                                    partition_size)
+                                    torch.from_numpy(np.ascontiguousarray(sh)).cuda(), gsz, mc,
+                                    scale, ws, partition_size)
     return out, (starts, shared)
 
 
@@ -137,3 +141,29 @@ def test_cascade_two_groups_singleton_and_short_member():
     ref = oracle.decode(oracle.bits_of(q.cpu(), "f16"), kp, vp, tab, lens, scale, "f16")
     err = check(out.double().cpu().numpy(), ref, "f16", "cascade, two groups")
     print(f"  max abs err {err:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("shared_prefix_bs16_cow", dict(batch=6, num_blocks=512)),
+    ("shared_prefix_bs16_cow", dict(batch=5, num_blocks=512, num_q_heads=32, num_kv_heads=4,
+                                    dtype="bf16")),
+])
+def test_cascade_launch_bound_and_member_counts(name, overrides):
+    """max_group_size only sizes the launch: a bound of 1 (one column tile per group and KV
+    head) covers every tile by striding and gives bit-identical output.  The group's shared
+    count is its first row's: other members' shared_blocks entries are not read."""
+    cfg = W.get_config(name, **overrides)
+    w = W.make_workload(cfg, device="cuda")
+    g = gpu_side.build(w)
+    rows = list(range(w.batch))
+    ref, (starts, shared) = cascade(g.alloc, rows, w.q[0], g.k_cache, g.v_cache, cfg.scale)
+    assert starts.tolist() == [0, w.batch]
+    small, _ = cascade(g.alloc, rows, w.q[0], g.k_cache, g.v_cache, cfg.scale, max_group_size=1)
+    assert torch.equal(small, ref)
+    big, _ = cascade(g.alloc, rows, w.q[0], g.k_cache, g.v_cache, cfg.scale,
+                     max_group_size=4 * w.batch)
+    assert torch.equal(big, ref)
+    odd = shared.copy()
+    odd[1:] = np.arange(1, w.batch) * 1000 - 3  # nonsense in every member but the first
+    other, _ = cascade(g.alloc, rows, w.q[0], g.k_cache, g.v_cache, cfg.scale, shared_override=odd)
+    assert torch.equal(other, ref)

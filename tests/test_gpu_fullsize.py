@@ -20,7 +20,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 FULL = ["llama7b", "llama13b", "gqa_long", "shared_prefix_bs8_cow", "shared_prefix_bs16_cow",
-        "shared_prefix_bs32_cow", "shared_prefix_bs16"]
+        "shared_prefix_bs32_cow", "shared_prefix_bs8", "shared_prefix_bs16", "shared_prefix_bs32"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -143,6 +143,38 @@ def test_prefill_bf16_values_beyond_fp16_range():
     print(f"  max abs err {err:.3g}", flush=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_tiny_values(dtype):
+    """V magnitudes across [2^-33, 2^-12]: below fp16's normal range, where the bf16 kernels'
+    fp16 staging of V keeps fewer bits or flushes to zero.  That moves each output by at most
+    2^-25 (the outputs are convex combinations of the rows).  On top of it come the fp16
+    probabilities (2^-11 relative each), fp32 sums and the output's rounding (2^-9 relative),
+    all bounded by 2^-8 times A = sum_t p_t |v_t|, the oracle's attention over |V|.  The bar
+    here is 2^-25 + 2^-8 A per element, far tighter than 5e-3 at these magnitudes."""
+    cfg = W.get_config("prefill_chunked_gqa", batch=2, lengths=("fixed", (300, 700)),
+                       new_tokens=("fixed", 140), num_blocks=80, dtype=dtype)
+    w = W.make_workload(cfg, device="cuda")
+    # Scale token t's values by 2^-(12 + t % 19): exact in bf16 (and in fp16 down to its
+    # subnormal range); the same stored values reach the oracle.
+    scale = torch.exp2(-(12 + torch.arange(w.v_tok.shape[0], device="cuda") % 19).float())
+    w.v_tok.copy_((w.v_tok.float() * scale[:, None, None]).to(w.v_tok.dtype))
+    g = gpu_side.build(w)
+    o = oracle_side.build(gpu_side.to_cpu(w), fill=gpu_side.SENTINEL_BITS[dtype])
+    out = g.prefill().double().cpu().numpy()
+    ref = o.prefill()
+    tables, lens = o.tables()
+    v_abs = o.v_pool & np.uint16(0x7FFF)  # |v|: the sign bit cleared (fp16 and bf16)
+    a = oracle.prefill(oracle.bits_of(o.w.q, dtype), o.k_pool, v_abs, tables, lens,
+                       w.query_start, cfg.scale, dtype)
+    err = np.abs(out - ref)
+    bound = 2.0 ** -25 + 2.0 ** -8 * a
+    assert np.all(np.isfinite(out))
+    assert np.all(err <= bound), f"max excess {float(np.max(err - bound)):.3g}"
+    assert float(np.abs(ref).max()) > 2.0 ** -16  # the outputs are not all below the bound
+    print(f"  max abs err {float(err.max()):.3g} with |ref| up to {float(np.abs(ref).max()):.3g}",
+          flush=True)
+
+
 def test_prefill_matches_decode_kernel_on_the_last_row():
     """The newest row of a prefill and a decode of that sequence read the same keys."""
     w, g, o = both("prefill_chunked_gqa", batch=2, lengths=("fixed", (300, 77)), num_blocks=80)
