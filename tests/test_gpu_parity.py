@@ -290,7 +290,7 @@ def test_debug_table_check(monkeypatch):
         with pytest.raises(pkv.PkvError) as e:
             pkv.pkv_paged_attention_decode(out, w.q[0], g.k_cache, g.v_cache,
                                            torch.from_numpy(t).cuda(), torch.from_numpy(l).cuda(),
-                                           int(l.max()), w.cfg.scale)
+                                           int(l.max()), w.cfg.scale, 0)  # unsplit: no workspace
         assert e.value.name == "PKV_ERR_INVALID_ARG"
         assert bool((out == 7.0).all())  # nothing was enqueued
     monkeypatch.delenv("PKV_DEBUG")
