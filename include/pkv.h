@@ -379,6 +379,30 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
                                       float scale, pkv_dtype dtype, int32_t partition_size,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): pkv_paged_attention_decode with the same
+ * arguments and result, minus the workspace.  When contexts are split, the partials go to a
+ * scratch array of PKV_DECODE_SCRATCH_BYTES bytes inside the library, one per GPU, reserved
+ * when the library's code is loaded onto the device and held until the process ends; its
+ * device address is looked up once per device (with that device current) on the first call.
+ * The call allocates nothing.  The current device must be the stream's.  A shape whose
+ * partials need more than PKV_DECODE_SCRATCH_BYTES (pkv_decode_workspace_bytes says how
+ * many) fails with PKV_ERR_WORKSPACE before anything is enqueued.  All calls on one GPU
+ * share its array: calls that overlap in time on one GPU (different streams, or several
+ * host threads) race and give undefined results; calls on one stream are safe.  Nothing in
+ * the array needs clearing between calls (every partial is written before it is read). */
+#define PKV_DECODE_SCRATCH_BYTES (64u << 20)
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                              const void* v_cache, const int32_t* block_tables,
+                                              const int32_t* context_lens,
+                                              const int32_t* cached_blocks, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                                              int32_t max_context_len, float scale,
+                                              pkv_dtype dtype, int32_t partition_size,
+                                              void* stream);
+
 /* Cascade decode: the same result as pkv_paged_attention_decode (plain attention of each
  * sequence's query over its whole context, up to fp32 rounding order), computed with the
  * shared prefix of each group of sequences read once per 16 queries instead of once per

@@ -49,6 +49,9 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,
                                            c_i32, c_i32, c_vp, c_sz, c_vp]),
+    "pkv_paged_attention_decode_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                   c_i32, c_f32, c_i32, c_i32, c_vp]),
     "pkv_cascade_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_attention_cascade": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                             c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,

@@ -432,6 +432,40 @@ def pkv_paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_l
     return out
 
 
+PKV_DECODE_SCRATCH_BYTES = 64 << 20  # include/pkv.h
+
+
+def pkv_paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens,
+                                       max_context_len: int, scale: float,
+                                       partition_size: int = -1, cached_blocks=None):
+    """pkv_paged_attention_decode without a workspace: split-K partials go to the library's
+    per-GPU scratch array (at most PKV_DECODE_SCRATCH_BYTES); allocates nothing."""
+    import torch
+    nb, hq, d = q.shape
+    n, hkv, bs, d2 = k_cache.shape
+    if d2 != d or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == out.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("dtype mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != nb or context_lens.shape != (nb,):
+        raise ValueError("table shape")
+    cached_ptr = None
+    if cached_blocks is not None:
+        if cached_blocks.dtype != torch.int32 or cached_blocks.shape != (nb,):
+            raise ValueError("cached_blocks must be int32 [num_seqs]")
+        cached_ptr = _dev(cached_blocks) if nb else None
+    if nb == 0:
+        return out
+    _check(_lib.load().pkv_paged_attention_decode_noalloc(
+        _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), _dev(context_lens),
+        cached_ptr, nb, hq, hkv, d, bs, n, block_tables.shape[1], int(max_context_len),
+        float(scale), _dtype_code(k_cache), int(partition_size), _stream(q)),
+        "pkv_paged_attention_decode_noalloc")
+    return out
+
+
 def pkv_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_context_len, dtype, partition_size=-1) -> int:
     """dtype: "f32" | "f16" | "bf16" or a torch dtype."""

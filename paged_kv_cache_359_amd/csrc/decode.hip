@@ -8,6 +8,7 @@
 // sharing one K/V tile form the columns of small matrix products).  One workgroup per
 // (sequence, head or head group, partition); reduce_partitions merges partitions.
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "device.h"
@@ -700,6 +701,41 @@ kernel_fn pick_cascade(pkv_dtype dt, int d, int bs) {
   return nullptr;
 }
 
+// Split-K partials of pkv_paged_attention_decode_noalloc, for callers that cannot allocate:
+// a fixed device array, one copy per GPU, held for the life of the process.  In host code
+// `scratch` names only a host-side stand-in; kernels get the device address that
+// hipGetSymbolAddress reports, fetched once per device with that device current.  Calls that
+// overlap on one GPU share the array and race.  The partials are written before they are
+// read, so nothing needs clearing between calls.
+constexpr size_t kScratchBytes = size_t(PKV_DECODE_SCRATCH_BYTES);
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+pkv_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    snprintf(g_last_error, sizeof(g_last_error), "decode_noalloc: hipGetDevice: %s (device %d)",
+             hipGetErrorString(ge), dev);
+    return PKV_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      snprintf(g_last_error, sizeof(g_last_error), "decode_noalloc: hipGetSymbolAddress: %s",
+               hipGetErrorString(e));
+      return PKV_ERR_HIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return PKV_OK;
+}
+
 // PKV_DEBUG=1 in the environment: before a decode is enqueued, wait for the stream, read
 // the lengths and tables back and check them; a violation fails the call with
 // PKV_ERR_INVALID_ARG (and a message in pkv_last_error) before anything is enqueued.  Off by
@@ -756,15 +792,19 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
   return size_t(num_seqs) * num_q_heads * max_parts * (size_t(head_dim) + 2) * sizeof(float);
 }
 
-pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
-                                      const void* v_cache, const int32_t* block_tables,
-                                      const int32_t* context_lens, const int32_t* cached_blocks,
-                                      int32_t num_seqs,
-                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                      int32_t block_size, int32_t num_blocks,
-                                      int32_t max_blocks_per_seq, int32_t max_context_len,
-                                      float scale, pkv_dtype dtype, int32_t partition_size,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode call.  from_scratch: the split-K partials go to this device's copy of the
+// library's scratch array instead of the caller's workspace.
+pkv_status decode_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       const int32_t* cached_blocks, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       float scale, pkv_dtype dtype, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, bool from_scratch, void* stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0)
     return PKV_ERR_INVALID_ARG;
@@ -817,6 +857,17 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
   if (max_parts > 1) {
     const size_t need =
         size_t(num_seqs) * num_q_heads * max_parts * (size_t(head_dim) + 2) * sizeof(float);
+    if (from_scratch) {
+      if (need > kScratchBytes) {
+        snprintf(g_last_error, sizeof(g_last_error),
+                 "decode_noalloc: the split-K partials need %zu bytes, the scratch holds %zu",
+                 need, kScratchBytes);
+        return PKV_ERR_WORKSPACE;
+      }
+      const pkv_status ss = scratch_of_current_device(&workspace);
+      if (ss != PKV_OK) return ss;
+      workspace_bytes = kScratchBytes;
+    }
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
     float* w = static_cast<float*>(workspace);
     a.part_o = w;
@@ -842,6 +893,41 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
     return launch_status("reduce_partitions");
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, const int32_t* cached_blocks,
+                                      int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      float scale, pkv_dtype dtype, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call(out, q, k_cache, v_cache, block_tables, context_lens, cached_blocks,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, dtype, partition_size,
+                     workspace, workspace_bytes, false, stream);
+}
+
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                              const void* v_cache, const int32_t* block_tables,
+                                              const int32_t* context_lens,
+                                              const int32_t* cached_blocks, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                                              int32_t max_context_len, float scale,
+                                              pkv_dtype dtype, int32_t partition_size,
+                                              void* stream) {
+  return decode_call(out, q, k_cache, v_cache, block_tables, context_lens, cached_blocks,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, dtype, partition_size, nullptr,
+                     0, true, stream);
 }
 
 size_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
