@@ -461,7 +461,10 @@ pkv_status pkv_paged_attention_cascade(void* out, const void* q, const void* k_c
  * max_query_len: an upper bound of the n_b (sizes the launch); max_context_len as for
  * decode.  A token whose position would be negative (n_b > context_lens[b]) gets zeros.
  * Supported: fp16 and bf16, head_dim 64 or 128, block_size 8, 16 or 32 (matrix cores);
- * other shapes return PKV_ERR_UNSUPPORTED.  Enqueued on stream; no workspace. */
+ * other shapes return PKV_ERR_UNSUPPORTED, and so do launches of more than 2^31 - 1
+ * workgroups (8 * ceil(num_seqs * num_kv_heads / 8) * (num_q_heads / num_kv_heads) *
+ * ceil(max_query_len / 128)) and K/V blocks of 2^32 bytes or more.  Enqueued on stream; no
+ * workspace. */
 pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
                                        const void* v_cache, const int32_t* block_tables,
                                        const int32_t* context_lens, const int32_t* query_start,

@@ -220,6 +220,7 @@ struct DecodeArgs {
   const int32_t* group_start;
   int32_t num_seqs;
   int32_t block_size;
+  int32_t row_tiles;  // prefill: row tiles per (query head, sequence)
 };
 
 // Number of leading table entries of sequence b to read through the caches (wave-uniform).

@@ -32,6 +32,20 @@ __device__ __forceinline__ uint2 read_tr16(lds_char* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_short4*>(p)));
 }
 
+// A wave-uniform pointer into device memory, moved into scalar registers (global address
+// space, so that loads through it stay global loads).
+typedef __attribute__((address_space(1))) const char gchar;
+__device__ __forceinline__ gchar* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<gchar*>((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ uint4 load_global(gchar* p) {
+  const u32x4_t v = *reinterpret_cast<__attribute__((address_space(1))) const u32x4_t*>(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Four consecutive output elements (8 bytes of 16-bit values).
 template <int DT>
 __device__ __forceinline__ void store4(void* base, size_t idx, const float (&v)[4]) {
@@ -70,14 +84,37 @@ __device__ __forceinline__ void tile_scores(const typename M::Chunk& ck,
   }
 }
 
+// The online-softmax state of one tile (per lane: its column).  m is the running reference
+// (log2 domain, -inf before any key); mu is the offset the scores are taken relative to (m,
+// or 0 while m is -inf) and thr the exponent above which the reference must move (kRescale-
+// Slack, or -inf while m is -inf): both change only with m, so they are kept rather than
+// derived from m on every chunk.
+template <typename M>
+struct TileState {
+  float4_t acc[M::E];
+  float m, l, mu, thr;
+};
+
+template <typename M>
+__device__ __forceinline__ void tile_init(TileState<M>& st) {
+#pragma unroll
+  for (int r = 0; r < M::E; ++r) st.acc[r] = float4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = kNegInf;
+  st.l = 0.f;
+  st.mu = 0.f;
+  st.thr = kNegInf;
+}
+
 // F16PV (bf16 only): the chunk's V rows were staged in LDS as fp16, and the probabilities go
-// into an fp16 product as well (11 significant bits, no remainder product).
+// into an fp16 product as well (11 significant bits, no remainder product).  The row sum l
+// then adds up the same fp16 probabilities, with dot products against (1, 1) that
+// accumulate in fp32, so that the weights of the output are exactly those of the product.
 template <typename M, bool MASKED, bool F16PV>
 __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs, int g4, float c,
-                                            const float4_t (&s)[2], typename M::State& st, int lim,
+                                            const float4_t (&s)[2], TileState<M>& st, int lim,
                                             uint32_t okbits) {
   // e = exponent of each probability relative to the current reference: s * c - mu.
-  const float mu = st.m == kNegInf ? 0.f : st.m;
+  const float mu = st.mu;
   float e[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -93,8 +130,7 @@ __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs,
   // still -inf (no key seen) and a finite score arrives.  The maximum is taken over the
   // exponents, which are already rounded results, so no extra instruction readies the
   // matrix-core outputs for the comparison.
-  const float thr = st.m == kNegInf ? kNegInf : kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(lm > thr)) {
+  if (__builtin_amdgcn_ballot_w64(lm > st.thr)) {
     const float cm = xor_max_16_32(lm) + mu;  // column maximum, absolute
     const bool grow = cm > st.m + kRescaleSlack;
     const float mn = grow ? cm : st.m;
@@ -103,24 +139,32 @@ __device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs,
 #pragma unroll
     for (int r = 0; r < M::E; ++r) st.acc[r] *= alpha;
     st.m = mn;
-    const float shift = (mn == kNegInf ? 0.f : mn) - mu;
+    st.mu = mn == kNegInf ? 0.f : mn;
+    st.thr = mn == kNegInf ? kNegInf : kRescaleSlack;
+    const float shift = st.mu - mu;
 #pragma unroll
     for (int j = 0; j < 8; ++j) e[j] -= shift;
   }
   float p[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) p[j] = exp2_hw(e[j]);
-  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   if constexpr (M::SPLIT_P && F16PV) {
     half8_t ph;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ph[j] = _Float16(p[j]);
+    const half2_t one2 = {_Float16(1.f), _Float16(1.f)};
+    float l = st.l;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      l = __builtin_amdgcn_fdot2(half2_t{ph[2 * q], ph[2 * q + 1]}, one2, l, false);
+    st.l = l;
 #pragma unroll
     for (int r = 0; r < M::E; ++r)
       st.acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ck.vop[r]), ph,
                                                           st.acc[r], 0, 0, 0);
     return;
   }
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   typename M::vec8 phi, plo;
   if constexpr (M::SPLIT_P) {
     // Pairs: one packed conversion gives both high parts; each reads back as fp32 by a
@@ -171,6 +215,35 @@ constexpr int kPrefillRows = kPrefillWaves * 16 * kPrefillTiles;  // new tokens 
 // after the fast one, it made the usual walk 5% slower.
 enum { kExact = 0, kFast = 1, kFixup = 2 };
 
+// The work of one workgroup: query head h of sequence b, new tokens jw .. jw + 127.
+struct PrefillItem {
+  int h, b, jw;
+};
+
+// Workgroups go to the eight XCDs in turn (workgroup L to XCD L % 8), and each XCD starts
+// its share about in the order of L / 8; every XCD has its own L2.  The query heads and row
+// tiles of one (sequence, KV head) read the same K/V, so they are kept on one XCD: unit
+// u = b * Hkv + kvh runs on XCD u % 8.  An XCD's share lists the row tiles from the last
+// (those walk the most keys, so the short walks fill in behind the long ones), within a row
+// tile its units, within a unit the unit's query heads: the workgroups that read one unit's
+// K/V start together and walk it in step through that L2.  A grid of 8 * ceil(U / 8) * G * T
+// workgroups (U units, G query heads per KV head, T row tiles) covers every item once; the
+// slots of units past U are padding (b = -1).
+__device__ __forceinline__ PrefillItem prefill_item(const DecodeArgs& a, unsigned L) {
+  const int units = a.num_seqs * a.num_kv_heads;
+  const int per_xcd = (units + 7) >> 3;
+  const int per_tile = per_xcd * a.group;
+  const int i = int(L >> 3);
+  const int zr = i / per_tile;  // row tile, counted from the last
+  const int rem = i - zr * per_tile;
+  const int lu = rem / a.group;
+  const int u = lu * 8 + int(L & 7);
+  if (u >= units) return {0, -1, 0};
+  const int b = u / a.num_kv_heads;
+  const int kvh = u - b * a.num_kv_heads;
+  return {kvh * a.group + (rem - lu * a.group), b, (a.row_tiles - 1 - zr) * kPrefillRows};
+}
+
 template <int DT, int D, int BS, int MODE>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   using M = Mfma<DT, D, BS>;
@@ -188,20 +261,21 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   constexpr int VECS = D * 2 / 16;          // 16-byte vectors per row
   constexpr int PER = 2 * CH * VECS / kPrefillThreads;  // vectors each thread moves per chunk
   static_assert(PER * kPrefillThreads == 2 * CH * VECS, "chunk must split evenly over the workgroup");
+  // A thread's vectors k < PER / 2 are K rows, the others V rows (known at compile time).
+  static_assert((CH * VECS) % kPrefillThreads == 0, "K rows fill whole vector steps");
   __shared__ __attribute__((aligned(16))) char lds[2][BUF];
 
-  // Grid: (query head, sequence, row tile), the row tiles in reverse: the last tiles of the
-  // sequences, which walk the most keys, are dispatched first and the short ones fill in
-  // behind them.
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  const PrefillItem it = prefill_item(a, blockIdx.x);
+  if (it.b < 0) return;  // uniform: a padding workgroup
+  const int h = it.h;
+  const int b = it.b;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int n16 = lane & 15, g4 = lane >> 4;
   const int r0 = a.query_start[b];
   const int n = a.query_start[b + 1] - r0;
-  const int jw = int(gridDim.z - 1 - blockIdx.z) * kPrefillRows;  // first new token of the workgroup
+  const int jw = it.jw;  // first new token of the workgroup
   // Uniform over the workgroup, so returning here skips no barrier another wave waits at.
   if (r0 < 0 || n <= 0 || jw >= n || r0 + jw >= a.num_tokens) return;
   const size_t mark = (size_t(r0 + jw) * a.num_q_heads + h) * D;  // element 0 of the first row
@@ -219,7 +293,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   const int nq = max(0, min(16 * NT, jw + nw - j0));   // columns of this wave that have a row
 
   typename M::vec8 qop[NT][M::KK];
-  typename M::State st[NT];
+  TileState<M> st[NT];
   int lim[NT], lim_min[NT], lim_max[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -256,23 +330,31 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   const char* kb = static_cast<const char*>(a.k_cache) + head_off;
   const char* vb = static_cast<const char*>(a.v_cache) + head_off;
   const size_t blk_bytes = size_t(a.num_kv_heads) * BS * D * 2;
+  const uint32_t blk32 = uint32_t(blk_bytes);  // the launch checks that it fits
   const int nch = (t1 + CH - 1) / CH;
 
   // Block ids of a chunk's tokens (wave-uniform; -1 past t1), read two chunks ahead so that
   // no K/V load waits for its table entry.
   constexpr int NB = CH / BS;  // blocks per chunk (block sizes divide the chunk)
   static_assert(NB * BS == CH, "block size must divide the chunk");
-  // The table does not change during the kernel: reading it through the constant address
-  // space makes these scalar loads, which wait on their own counter instead of on every
-  // vector load in flight (the K/V prefetch issued just before).
-  const __attribute__((address_space(4))) int32_t* ctbl =
-      (const __attribute__((address_space(4))) int32_t*)tbl;
-  auto load_ids = [&](int cs, int (&ids)[NB]) {
+  // They are vector loads (the address is forced into vector registers, so that the
+  // compiler does not turn them into scalar loads), issued right after the chunk's K/V
+  // prefetch and read back into scalar registers at the end of the chunk, where the loop
+  // waits for that prefetch anyway.  Scalar loads would share the counter of the LDS reads,
+  // whose completion order they break, and every LDS read would then have to wait for all
+  // of them.
+  auto load_ids = [&](int cs, int (&raw)[NB]) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int tok = cs + k * BS;
-      ids[k] = tok < t1 ? ctbl[tok / BS] : -1;
+      auto p = (__attribute__((address_space(1))) const int32_t*)(tbl + (tok < t1 ? tok / BS : 0));
+      asm volatile("" : "+v"(p));
+      raw[k] = tok < t1 ? *p : -1;
     }
+  };
+  auto to_uniform = [&](int (&ids)[NB]) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) ids[k] = uniform(ids[k]);
   };
   // The id of the block holding token cs + off (0 <= off < CH).
   auto id_of = [&](const int (&ids)[NB], int off) {
@@ -311,11 +393,16 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
         // NaN.  Both zeroings are rare and sit behind a branch, so the usual chunk issues
         // its loads and nothing else.
         const int row0 = UNIFORM_K ? ROWS_PER_K * k : (64 * wave + kPrefillThreads * k) / VECS;
-        const bool is_v = row0 >= CH;
+        const bool is_v = k >= PER / 2;
         const int id = UNIFORM_K ? ids[(row0 % CH) / BS] : id_of(ids, row0 % CH);
         const bool valid = (unsigned)id < (unsigned)a.num_blocks;
-        pre[k] = load_cached((is_v ? vb : kb) + size_t(valid ? id : 0) * blk_bytes + lane_off);
-        if (!valid || (is_v && tail && cs + off >= t1)) pre[k] = make_uint4(0, 0, 0, 0);
+        // The block base is wave-uniform: held in scalar registers, it makes the load a
+        // scalar base plus the lane's 32-bit offset (an unsigned 32 x 32-bit product).
+        const uint32_t uid = valid ? uint32_t(id) : 0u;
+        pre[k] = load_global(uniform_ptr((is_v ? vb : kb) + uint64_t(uid) * blk32) + lane_off);
+        if (!valid || (is_v && tail)) {  // uniform, and rare
+          if (!valid || cs + off >= t1) pre[k] = make_uint4(0, 0, 0, 0);
+        }
       } else {
         const int id = cs + off < t1 ? id_of(ids, off) : -1;
         pre[k] = make_uint4(0, 0, 0, 0);
@@ -332,10 +419,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
     for (int k = 0; k < PER; ++k) {
       const int v = tid + kPrefillThreads * k;
       const int row = v / VECS, col = v % VECS;
-      const int off = row < CH ? row * PK : VBASE + (row - CH) * PV;
+      const bool is_v = k >= PER / 2;
+      const int off = is_v ? VBASE + (row - CH) * PV : row * PK;
       uint4 w = pre[k];
       if constexpr (F16PV) {
-        if (row >= CH) {
+        if (is_v) {
           uint32_t x[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -355,11 +443,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   auto run = [&](auto f16pv) {
   constexpr bool F16PV = decltype(f16pv)::value;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) M::init(st[t]);
-  int ids_cur[NB], ids_next[NB], ids_after[NB];
+  for (int t = 0; t < NT; ++t) tile_init(st[t]);
+  int ids_cur[NB], ids_next[NB], ids_after[NB] = {};
   if (nch > 0) {
     load_ids(0, ids_cur);
     load_ids(CH, ids_next);
+    to_uniform(ids_cur);
+    to_uniform(ids_next);
     fetch(0, ids_cur);
     stash(0, f16pv);
   }
@@ -396,6 +486,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
       }
       // K operands: row cs + 16hf + lane%16, elements 32kk + 8(lane/16) .. + 8.
       const char* kl = lds[c & 1];
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -408,12 +499,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
       // 16r + 4(l%4) .. + 4.
       lds_char* vl = (lds_char*)(lds[c & 1]) + VBASE +
                      (4 * g4 + (n16 >> 2)) * PV + (4 * (lane & 3)) * 2;
-#pragma unroll
-      for (int r = 0; r < M::E; ++r) {
-        const uint2 lo = read_tr16(vl + 32 * r);
-        const uint2 hi = read_tr16(vl + 16 * PV + 32 * r);
-        ck.vop[r] = __builtin_bit_cast(typename M::vec8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      }
       // Every tile of the wave takes part: in the unmasked loop all are active (a tile
       // without columns computes on zero queries and is never stored), and in the masked
       // loop a tile whose columns all precede the chunk gets -inf for every key, which
@@ -423,10 +508,27 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
       // ahead of the other wave on the SIMD, whose softmax can then run beside these
       // products (measured: 4% on long walks, no change on short ones).
       float4_t sc[NT][2];
-      __builtin_amdgcn_s_setprio(1);
+      uint2 vlo[M::E], vhi[M::E];
 #pragma unroll
       for (int t = 0; t < NT; ++t) tile_scores<M>(ck, qop[t], sc[t]);
+#pragma unroll
+      for (int r = 0; r < M::E; ++r) {
+        vlo[r] = read_tr16(vl + 32 * r);
+        vhi[r] = read_tr16(vl + 16 * PV + 32 * r);
+      }
+      // The products wait only for the K reads: the V^T reads are issued between them, so
+      // their latency runs under the matrix-core work (waiting for all the chunk's reads at
+      // once left the matrix cores idle for the whole read).
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * M::KK, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * M::E; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
       __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int r = 0; r < M::E; ++r)
+        ck.vop[r] = __builtin_bit_cast(typename M::vec8, make_uint4(vlo[r].x, vlo[r].y, vhi[r].x, vhi[r].y));
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         tile_update<M, MASKED, F16PV>(ck, cs, g4, c_abs, sc[t], st[t], lim[t], okbits);
@@ -435,7 +537,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       ids_cur[k] = ids_next[k];
-      ids_next[k] = ids_after[k];
+      ids_next[k] = uniform(ids_after[k]);
     }
     __syncthreads();
   };
@@ -548,10 +650,10 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   if (!valid_dtype(dtype)) return PKV_ERR_INVALID_ARG;
   if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
   const PrefillKernels k = pick_prefill(dtype, head_dim, block_size);
+  if (k.first && int64_t(num_kv_heads) * block_size * head_dim * 2 > int64_t(UINT32_MAX))
+    return PKV_ERR_UNSUPPORTED;  // a block's bytes must fit 32 bits
   if (!k.first) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
-  if (num_seqs > 65535 || (int64_t(max_query_len) + kPrefillRows - 1) / kPrefillRows > 65535)
-    return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -573,8 +675,12 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
   a.max_blocks = max_blocks_per_seq;
   a.ctx_limit = int32_t(max_context_len < cap ? max_context_len : cap);
   a.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid{unsigned(num_q_heads), unsigned(num_seqs),
-                  unsigned((max_query_len + kPrefillRows - 1) / kPrefillRows)};
+  a.num_seqs = num_seqs;
+  a.row_tiles = int32_t((int64_t(max_query_len) + kPrefillRows - 1) / kPrefillRows);
+  const int64_t units = int64_t(num_seqs) * num_kv_heads;
+  const int64_t blocks = 8 * ((units + 7) / 8) * a.group * a.row_tiles;
+  if (blocks > 0x7FFFFFFF) return PKV_ERR_UNSUPPORTED;
+  const dim3 grid{unsigned(blocks)};
   clear_stale_error();
   hipLaunchKernelGGL(k.first, grid, dim3(kPrefillThreads), 0, static_cast<hipStream_t>(stream), a);
   if (launch_status("paged_attention_prefill") != PKV_OK) return PKV_ERR_HIP;

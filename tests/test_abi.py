@@ -193,7 +193,8 @@ def prefill(**kw):
     (dict(scale=float("nan")), 1),
     (dict(qs=None), 1),
     (dict(out=MIS), 1),
-    (dict(nseq=70000), 5),
+    (dict(nseq=70000, maxq=1 << 26), 5),   # more workgroups than one launch takes
+    (dict(hq=2000000, hkv=2000000), 5),    # a block's bytes past 32 bits
     (dict(ntok=0, out=None), 0),       # nothing to do
     (dict(maxq=0, q=None), 0),
 ])
