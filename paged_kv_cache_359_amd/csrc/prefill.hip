@@ -64,13 +64,8 @@ __device__ __forceinline__ void store4(void* base, size_t idx, const float (&v)[
 }
 
 // Online-softmax update of one 16-column tile with the chunk in ck (keys cs .. cs + 31), as
-// the shared tile's compute does, in two forms.  c = |scale| * log2(e); the query operands
-// carry the scale's sign, so c >= 0.  Each score becomes its exponent relative to the
-// running reference in one fused multiply-add.  MASKED = false: every row of the chunk
-// exists and no key is past any column's causal limit.  MASKED = true: the rows whose bit
-// in okbits is clear (bit 4hf + i for the lane's row 16hf + 4(lane/16) + i) and keys past
-// the column's limit lim get -inf exponents.  The chunk loop picks the form per chunk with
-// a uniform branch, so the usual chunk runs no masking instructions at all.
+// the shared tile's compute does, in an unmasked and a masked form; the chunk loop picks the
+// form per chunk with a uniform branch, so the usual chunk runs no masking instructions.
 // S = K . Q^T of one tile for both 16-token halves of the chunk.
 template <typename M>
 __device__ __forceinline__ void tile_scores(const typename M::Chunk& ck,
@@ -105,46 +100,62 @@ __device__ __forceinline__ void tile_init(TileState<M>& st) {
   st.thr = kNegInf;
 }
 
-// F16PV (bf16 only): the chunk's V rows were staged in LDS as fp16, and the probabilities go
-// into an fp16 product as well (11 significant bits, no remainder product).  The row sum l
-// then adds up the same fp16 probabilities, with dot products against (1, 1) that
-// accumulate in fp32, so that the weights of the output are exactly those of the product.
-template <typename M, bool MASKED, bool F16PV>
-__device__ __forceinline__ void tile_update(const typename M::Chunk& ck, int cs, int g4, float c,
-                                            const float4_t (&s)[2], TileState<M>& st, int lim,
-                                            uint32_t okbits) {
-  // e = exponent of each probability relative to the current reference: s * c - mu.
-  const float mu = st.mu;
-  float e[8];
+// The tile update runs in three parts, so that the chunk loop can place the matrix-core work
+// of one part between the vector instructions of another.
+//
+// 1. tile_exps: each score becomes its exponent relative to the tile's offset mu, in one
+//    fused multiply-add (c = |scale| * log2(e); the query operands carry the scale's sign,
+//    so c >= 0).  MASKED = false: every row of the chunk exists and no key is past any
+//    column's causal limit.  MASKED = true: the rows whose bit in okbits is clear (bit
+//    4hf + i for the lane's row 16hf + 4(lane/16) + i) and keys past the column's limit lim
+//    get -inf exponents.  Returns the lane's largest exponent.  The maximum is taken over
+//    the exponents, which are already rounded results, so no extra instruction readies the
+//    matrix-core outputs for the comparison.
+template <typename M, bool MASKED>
+__device__ __forceinline__ float tile_exps(int cs, int g4, float c, const float4_t (&s)[2],
+                                           const TileState<M>& st, int lim, uint32_t okbits,
+                                           float (&e)[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int hf = j >> 2, i = j & 3;
-    e[j] = __builtin_fmaf(s[hf][i], c, -mu);
+    e[j] = __builtin_fmaf(s[hf][i], c, -st.mu);
     if constexpr (MASKED)
       if (!((okbits >> j) & 1u) || cs + 16 * hf + 4 * g4 + i > lim) e[j] = kNegInf;
   }
-  const float lm = fmaxf(fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])),
-                         fmaxf(fmaxf(e[4], e[5]), fmaxf(e[6], e[7])));
-  // Lazy rescaling as in the shared tile: the reference st.m moves (with a cross-lane maximum
-  // and a rescale) only when a score exceeds it by more than kRescaleSlack, or when it is
-  // still -inf (no key seen) and a finite score arrives.  The maximum is taken over the
-  // exponents, which are already rounded results, so no extra instruction readies the
-  // matrix-core outputs for the comparison.
-  if (__builtin_amdgcn_ballot_w64(lm > st.thr)) {
-    const float cm = xor_max_16_32(lm) + mu;  // column maximum, absolute
-    const bool grow = cm > st.m + kRescaleSlack;
-    const float mn = grow ? cm : st.m;
-    const float alpha = exp2_hw(st.m - (mn == kNegInf ? 0.f : mn));
-    st.l *= alpha;
+  return fmaxf(fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])), fmaxf(fmaxf(e[4], e[5]), fmaxf(e[6], e[7])));
+}
+
+// 2. tile_rescale (lazy, as in the shared tile): called when some lane of the wave has an
+//    exponent above its threshold.  The reference st.m moves (with a cross-lane maximum and a
+//    rescale of l and the accumulators) only in columns where a score exceeds it by more
+//    than kRescaleSlack, or where it is still -inf and a finite score arrives; the exponents
+//    are shifted to the new offset.
+template <typename M>
+__device__ __forceinline__ void tile_rescale(TileState<M>& st, float lm, float (&e)[8]) {
+  const float mu = st.mu;
+  const float cm = xor_max_16_32(lm) + mu;  // column maximum, absolute
+  const bool grow = cm > st.m + kRescaleSlack;
+  const float mn = grow ? cm : st.m;
+  const float alpha = exp2_hw(st.m - (mn == kNegInf ? 0.f : mn));
+  st.l *= alpha;
 #pragma unroll
-    for (int r = 0; r < M::E; ++r) st.acc[r] *= alpha;
-    st.m = mn;
-    st.mu = mn == kNegInf ? 0.f : mn;
-    st.thr = mn == kNegInf ? kNegInf : kRescaleSlack;
-    const float shift = st.mu - mu;
+  for (int r = 0; r < M::E; ++r) st.acc[r] *= alpha;
+  st.m = mn;
+  st.mu = mn == kNegInf ? 0.f : mn;
+  st.thr = mn == kNegInf ? kNegInf : kRescaleSlack;
+  const float shift = st.mu - mu;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] -= shift;
-  }
+  for (int j = 0; j < 8; ++j) e[j] -= shift;
+}
+
+// 3. tile_accum: the probabilities, their row sum l and P.V.  F16PV (bf16 only): the chunk's
+//    V rows were staged in LDS as fp16, and the probabilities go into an fp16 product as
+//    well (11 significant bits, no remainder product); l then adds up the same fp16
+//    probabilities, with dot products against (1, 1) that accumulate in fp32, so that the
+//    weights of the output are exactly those of the product.
+template <typename M, bool F16PV>
+__device__ __forceinline__ void tile_accum(const typename M::Chunk& ck, TileState<M>& st,
+                                           const float (&e)[8]) {
   float p[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) p[j] = exp2_hw(e[j]);
@@ -440,47 +451,65 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
 
   // The whole walk over the chunks, with fresh tile states.  F16PV (bf16 only) stages V as
   // fp16 and takes the fp16 product for P.V.
+  //
+  // The walk is software-pipelined over three chunks.  While the waves compute chunk c from
+  // LDS buffer c % 2, they stash chunk c + 1 (loaded while chunk c - 1 was computed) into the
+  // other buffer, and then issue the global loads of chunk c + 2.  Every buffer a chunk
+  // writes was last read one chunk earlier, before the barrier that ends each chunk.  Inside
+  // a chunk the matrix-core products and the vector work of other steps are interleaved:
+  // the score products with the V^T reads and the stash of the next chunk, the P.V products
+  // of one tile with the exponents of the other.
   auto run = [&](auto f16pv) {
   constexpr bool F16PV = decltype(f16pv)::value;
 #pragma unroll
   for (int t = 0; t < NT; ++t) tile_init(st[t]);
-  int ids_cur[NB], ids_next[NB], ids_after[NB] = {};
+  // Block ids of chunks c and c + 1 (wave-uniform) for the loop's chunk c, and in raw those
+  // of chunk c + 2, as loaded during chunk c - 1.  The loaded ids are read back into scalar
+  // registers one chunk after their load, just before the fetch that needs them: the K/V
+  // loads issued before them have been waited for by then (the stash), so reading the ids
+  // never waits for a load in flight.  The next ids are then loaded into the same registers
+  // (a copy of a register with a load in flight would wait for the load).
+  int ids0[NB], ids1[NB], raw[NB];
   if (nch > 0) {
-    load_ids(0, ids_cur);
-    load_ids(CH, ids_next);
-    to_uniform(ids_cur);
-    to_uniform(ids_next);
-    fetch(0, ids_cur);
+    load_ids(0, ids0);
+    load_ids(CH, ids1);
+    load_ids(2 * CH, raw);
+    to_uniform(ids0);
+    to_uniform(ids1);
+    fetch(0, ids0);
     stash(0, f16pv);
+    if (nch > 1) fetch(CH, ids1);
   }
   __syncthreads();
-  // One chunk: prefetch the next chunk's rows and the block ids two ahead, update the tiles
-  // from LDS, stash the prefetched rows.  MASKED selects the tile update's form.
-  auto step = [&](int c, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
+  // KIND 0: an unmasked chunk, for a wave with columns (it computes); KIND 1: an unmasked
+  // chunk, for a wave without columns (it only stages); KIND 2: a masked chunk, where a wave
+  // computes while some tile of it still needs keys from here.  Knowing the first two at
+  // compile time keeps the usual chunk's body one basic block.
+  auto step = [&](int c, auto kind) {
+    constexpr int KIND = decltype(kind)::value;
+    constexpr bool MASKED = KIND == 2;
     const int cs = c * CH;
-    if (c + 1 < nch) {
-      fetch(cs + CH, ids_next);
-      load_ids(cs + 2 * CH, ids_after);
-    }
-    bool busy = false;  // wave-uniform: some tile of this wave still needs keys from here
+    bool busy = KIND == 0;  // wave-uniform
+    if constexpr (KIND == 2) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) busy |= cs <= lim_max[t];
+      for (int t = 0; t < NT; ++t) busy |= cs <= lim_max[t];
+    }
+    typename M::Chunk ck;
+    float e[NT][8], lm[NT];
     if (busy) {
-      typename M::Chunk ck;
       // Rows that do not exist (past t1, or in a block outside the pool) have their bit in
       // okbits cleared; only the masked form reads it.
       uint32_t okbits = 0xFFu;
       if constexpr (MASKED) {
         bool need_mask = cs + CH > t1;
 #pragma unroll
-        for (int k = 0; k < NB; ++k) need_mask |= (unsigned)ids_cur[k] >= (unsigned)a.num_blocks;
+        for (int k = 0; k < NB; ++k) need_mask |= (unsigned)ids0[k] >= (unsigned)a.num_blocks;
         if (need_mask) {
           okbits = 0;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int off = 16 * (j >> 2) + 4 * g4 + (j & 3);
-            if (cs + off < t1 && (unsigned)id_of(ids_cur, off) < (unsigned)a.num_blocks) okbits |= 1u << j;
+            if (cs + off < t1 && (unsigned)id_of(ids0, off) < (unsigned)a.num_blocks) okbits |= 1u << j;
           }
         }
       }
@@ -492,6 +521,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
 #pragma unroll
         for (int kk = 0; kk < M::KK; ++kk)
           ck.kr[hf][kk] = *reinterpret_cast<const uint4*>(kl + (16 * hf + n16) * PK + (32 * kk + 8 * g4) * 2);
+      // All K reads are issued before anything else of the chunk, so that the first product
+      // waits for the first read only.
+      __builtin_amdgcn_sched_barrier(0);
       // V^T operand of output tile r, which here covers head elements 16r .. 16r + 15 (row
       // lane%16 of the tile is element 16r + lane%16): element j of lane l is V of token
       // 16(j/4) + 4(l/16) + j%4, the token the lane's score slot j holds.  One transposed
@@ -502,11 +534,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
       // Every tile of the wave takes part: in the unmasked loop all are active (a tile
       // without columns computes on zero queries and is never stored), and in the masked
       // loop a tile whose columns all precede the chunk gets -inf for every key, which
-      // leaves its state unchanged.  All score products are issued first, so that the
-      // matrix cores work on the later tiles while the earlier tiles' softmax runs.  The
-      // wave raises its priority while it issues them, so that it gets the issue slots
-      // ahead of the other wave on the SIMD, whose softmax can then run beside these
-      // products (measured: 4% on long walks, no change on short ones).
+      // leaves its state unchanged.  The wave raises its priority while it issues the score
+      // products, so that it gets the issue slots ahead of the other wave on the SIMD, whose
+      // vector work can then run beside these products.
       float4_t sc[NT][2];
       uint2 vlo[M::E], vhi[M::E];
 #pragma unroll
@@ -516,14 +546,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
         vlo[r] = read_tr16(vl + 32 * r);
         vhi[r] = read_tr16(vl + 16 * PV + 32 * r);
       }
-      // The products wait only for the K reads: the V^T reads are issued between them, so
-      // their latency runs under the matrix-core work (waiting for all the chunk's reads at
-      // once left the matrix cores idle for the whole read).
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * M::KK, 0);
+      // The stash runs on every chunk, so that it shares the products' basic block: after
+      // the last chunk it writes stale registers into a buffer that nothing reads again.
+      stash((c + 1) & 1, f16pv);
+      // The products wait only for the K reads: the V^T reads and the stash's conversions
+      // and writes are issued between them.
 #pragma unroll
       for (int i = 0; i < 2 * M::E; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       }
       __builtin_amdgcn_s_setprio(0);
 #pragma unroll
@@ -531,13 +564,33 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
         ck.vop[r] = __builtin_bit_cast(typename M::vec8, make_uint4(vlo[r].x, vlo[r].y, vhi[r].x, vhi[r].y));
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        tile_update<M, MASKED, F16PV>(ck, cs, g4, c_abs, sc[t], st[t], lim[t], okbits);
+        lm[t] = tile_exps<M, MASKED>(cs, g4, c_abs, sc[t], st[t], lim[t], okbits, e[t]);
+    } else {
+      stash((c + 1) & 1, f16pv);
     }
-    if (c + 1 < nch) stash((c + 1) & 1, f16pv);
+    int ids2[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) ids2[k] = uniform(raw[k]);
+    if (c + 2 < nch) {
+      fetch(cs + 2 * CH, ids2);
+      load_ids(cs + 3 * CH, raw);
+    }
+    if (busy) {
+      bool up = false;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) up |= lm[t] > st[t].thr;
+      if (__builtin_amdgcn_ballot_w64(up)) {  // rare: a reference moves
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (__builtin_amdgcn_ballot_w64(lm[t] > st[t].thr)) tile_rescale(st[t], lm[t], e[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) tile_accum<M, F16PV>(ck, st[t], e[t]);
+    }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      ids_cur[k] = ids_next[k];
-      ids_next[k] = uniform(ids_after[k]);
+      ids0[k] = ids1[k];
+      ids1[k] = ids2[k];
     }
     __syncthreads();
   };
@@ -546,15 +599,19 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   // table entry is outside the pool; the first such entry ends the unmasked loop.  The rest
   // (the diagonal chunks and the context's tail) take the masked form.
   const int n_plain = min(nch, max(0, (first + jw + 1) / CH));
-  int c = 0;
-  for (; c < n_plain; ++c) {
+  auto plain_bad = [&]() {
     bool bad = false;
 #pragma unroll
-    for (int k = 0; k < NB; ++k) bad |= (unsigned)ids_cur[k] >= (unsigned)a.num_blocks;
-    if (bad) break;
-    step(c, std::false_type{});
+    for (int k = 0; k < NB; ++k) bad |= (unsigned)ids0[k] >= (unsigned)a.num_blocks;
+    return bad;
+  };
+  int c = 0;
+  if (nq > 0) {
+    for (; c < n_plain && !plain_bad(); ++c) step(c, std::integral_constant<int, 0>{});
+  } else {
+    for (; c < n_plain && !plain_bad(); ++c) step(c, std::integral_constant<int, 1>{});
   }
-  for (; c < nch; ++c) step(c, std::true_type{});
+  for (; c < nch; ++c) step(c, std::integral_constant<int, 2>{});
   };
 
   if constexpr (MODE == kFast) {
