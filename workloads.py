@@ -58,6 +58,9 @@ class DecodeConfig:
     # as one chunk and attending causally); None for decode.  ("all",) = a fresh prompt,
     # ("fixed", n) = a chunk of n tokens on top of cached context.
     new_tokens: Optional[tuple] = None
+    # The split-K partition size the workload's description names, if any (timed beside the
+    # automatic split).
+    stated_partition: Optional[int] = None
 
     @property
     def group(self) -> int:
@@ -107,7 +110,7 @@ CONFIGS = {
                              ("lognormal", 512, 1.0, 16, 4096), steps=64),
     # Grouped-query long context: 64 query heads over 8 KV heads, 32k tokens, split-K.
     "gqa_long": DecodeConfig("gqa_long", 4, "bf16", 64, 8, 128, 16, 33792, 16,
-                             ("fixed", (32768,) * 16)),
+                             ("fixed", (32768,) * 16), stated_partition=512),
 }
 for _bs in (8, 16, 32):
     for _cow in (False, True):
