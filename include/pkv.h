@@ -365,7 +365,11 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * depend on it.
  * workspace / workspace_bytes: device scratch of at least pkv_decode_workspace_bytes(...)
  * bytes, 16-byte aligned (may be NULL when that is 0); its contents need no initialisation
- * and are overwritten.
+ * and are overwritten.  After a split call it holds the partials, fp32, with P =
+ * ceil(max_context_len / partition size): o [num_seqs][num_q_heads][P][head_dim], then m and
+ * l [num_seqs][num_q_heads][P] (m in the log2 domain, a reference that need not be the
+ * partition's largest score; o / l is the partition's attention); only the partitions a
+ * sequence's context reaches are written, and none for a sequence with one partition.
  * Supported: dtype f32, f16, bf16; head_dim 8, 64, 128; block_size 4, 8, 16, 32;
  * num_q_heads a multiple of num_kv_heads.  Grouped-query attention with 16-bit elements,
  * head_dim 64 or 128 and block_size >= 8 runs on matrix cores (MFMA). */
