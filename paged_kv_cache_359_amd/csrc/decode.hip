@@ -517,13 +517,15 @@ __global__ __launch_bounds__(NW * 64) void cascade_decode(DecodeArgs a) {
     auto lane_val = [](int v, int l) { return __builtin_amdgcn_readlane(v, l); };
     // The prefix chunks (cache hits after the first tile's read) are spread evenly over the
     // list, so that while some waves read them the others keep the memory stream going:
-    // position ch holds prefix chunk floor(ch * npre / total) when that value steps up
-    // between ch and ch + 1, and otherwise own chunk ch - floor((ch + 1) * npre / total).
-    auto work = [&](int ch) {
-      const int p0 = int((int64_t(ch) * npre) / total), p1 = int((int64_t(ch + 1) * npre) / total);
-      Work w{tbl_first, p0 * kMfmaChunk, skg * BS, pre_lim, pre_min, p1 > p0};
+    // with ch * npre = q * total + r (0 <= r < total), position ch holds prefix chunk q when
+    // (ch + 1) * npre reaches the next multiple of total (r + npre >= total), and otherwise
+    // own chunk ch - q.  q and r are carried from one of the wave's positions to the next
+    // (ch grows by NW), so no chunk pays for a division.
+    int q = (wave * npre) / max(total, 1), r = (wave * npre) - q * max(total, 1);
+    for (int ch = wave; ch < total; ch += NW) {
+      Work w{tbl_first, q * kMfmaChunk, skg * BS, pre_lim, pre_min, r + npre >= total};
       if (!w.pre) {
-        const int sc = ch - p1 + npre;  // own chunks before this one, plus npre
+        const int sc = ch - q + npre;  // own chunks before this one, plus npre
         int k = kcur;
         while (sc >= lane_val(seg_l, k + 2)) ++k;
         kcur = k;
@@ -534,10 +536,11 @@ __global__ __launch_bounds__(NW * 64) void cascade_decode(DecodeArgs a) {
         w.lim = jm == k ? INT_MAX : -1;
         w.lim_min = -1;
       }
-      return w;
-    };
-    for (int ch = wave; ch < total; ch += NW) {
-      const Work w = work(ch);
+      r += NW * npre;
+      while (r >= total) {
+        r -= total;
+        ++q;
+      }
       typename M::Chunk ck;
       M::load(a, w.tbl, kb, vb, blk_bytes, w.cs, w.t1, w.pre, lane, ck);
       M::template compute<true>(a, ck, w.cs, lane, qop, st, w.lim, w.lim_min);
