@@ -651,6 +651,514 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   }
 }
 
+
+// =========================================================================================
+// The pipelined walk, for the fp16 products (bf16 caches with V staged as fp16, and fp16
+// caches).  Same workgroups, tiles, work order and chunk staging as prefill_mfma; the chunk
+// walk is arranged so that one wave keeps the matrix cores and the vector units busy side by
+// side:
+//
+// - iteration c issues the score products of chunk c + 1 between the vector instructions of
+//   chunk c's softmax (exponents, fp16 probabilities, row sums), then chunk c's P.V products
+//   between the instructions that stage chunk c + 2 into LDS.  So a chunk's scores wait one
+//   iteration in registers, and the LDS holds three chunks: c (its V^T read), c + 1 (its K
+//   read) and c + 2 (being written), each iteration ending with one barrier;
+// - the tile's reference moves only when some probability would not fit fp16 (from 65520
+//   up, an exponent near 16 above the reference) or while it is still -inf.  Both show in
+//   the lane's row sum after the chunk: the fp16 probabilities are added into it anyway,
+//   and an fp16 inf makes it inf.  So one comparison per tile and chunk replaces the
+//   per-chunk maximum, which is taken only on the rare path that moves the reference.
+//   Probabilities stay in [0, 65504] and the largest one a column has seen is at least 1
+//   (the reference is set to a column maximum), so fp16 keeps 11 significant bits of each,
+//   as in prefill_mfma's form with its smaller slack.
+// =========================================================================================
+constexpr float kPosInf = __builtin_inff();
+// max(lo, min(x, hi)) of wave-uniform values in scalar registers.  (Written out, the clamp
+// is selected as a vector instruction, and a buffer descriptor built from its result would
+// need a loop over the lanes' values.)
+__device__ __forceinline__ int sclamp(int x, int lo, int hi) {
+  int r;
+  asm volatile("s_min_i32 %0, %1, %2\n\ts_max_i32 %0, %0, %3"
+               : "=&s"(r)
+               : "s"(__builtin_amdgcn_readfirstlane(x)), "s"(hi), "s"(lo)
+               : "scc");
+  return r;
+}
+
+// Word 3 of a raw buffer descriptor on gfx9-family targets (32-bit data format; no swizzle,
+// no stride).
+constexpr int kBufferWord3 = 0x00020000;
+
+template <typename M>
+__device__ __forceinline__ void pipe_scores(const uint4 (&kr)[2][M::KK],
+                                            const typename M::vec8 (&qop)[M::KK], float4_t (&s)[2]) {
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    s[hf] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < M::KK; ++kk)
+      s[hf] = M::mma(__builtin_bit_cast(typename M::vec8, kr[hf][kk]), qop[kk], s[hf]);
+  }
+}
+
+// The exponents of a masked chunk, as tile_exps<M, true> takes them, with the causal limit
+// as one per-lane distance d = lim - cs - 4(lane/16): the key of score slot j,
+// cs + 16(j/4) + 4(lane/16) + j%4, is past the column's limit when 16(j/4) + j%4 > d.
+template <typename M>
+__device__ __forceinline__ void pipe_exps_masked(int d, float c, const float4_t (&s)[2],
+                                                 const TileState<M>& st, uint32_t okbits, float (&e)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int hf = j >> 2, i = j & 3;
+    e[j] = __builtin_fmaf(s[hf][i], c, -st.mu);
+    if (!((okbits >> j) & 1u) || 16 * hf + i > d) e[j] = kNegInf;
+  }
+}
+
+// The fp16 probabilities of one tile and the lane's row sum l with them added (dot products
+// against (1, 1), accumulated in fp32).
+__device__ __forceinline__ float pipe_probs(const float (&e)[8], float l, half8_t& ph) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ph[j] = _Float16(exp2_hw(e[j]));
+  const half2_t one2 = {_Float16(1.f), _Float16(1.f)};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) l = __builtin_amdgcn_fdot2(half2_t{ph[2 * q], ph[2 * q + 1]}, one2, l, false);
+  return l;
+}
+
+// The rare path: the column maximum of the chunk's exponents moves the reference where it
+// exceeds it by more than kRescaleSlack (always where a probability overflowed), rescales l
+// and the accumulators, and shifts the exponents to the new offset.  thr is +inf once the
+// reference is finite; while it is -inf, thr keeps its value.
+template <typename M>
+__device__ __forceinline__ void pipe_rescale(TileState<M>& st, float (&e)[8]) {
+  const float lm = fmaxf(fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])), fmaxf(fmaxf(e[4], e[5]), fmaxf(e[6], e[7])));
+  const float mu = st.mu;
+  const float cm = xor_max_16_32(lm) + mu;  // column maximum, absolute
+  const bool grow = cm > st.m + kRescaleSlack;
+  const float mn = grow ? cm : st.m;
+  const float alpha = exp2_hw(st.m - (mn == kNegInf ? 0.f : mn));
+  st.l *= alpha;
+#pragma unroll
+  for (int r = 0; r < M::E; ++r) st.acc[r] *= alpha;
+  st.m = mn;
+  st.mu = mn == kNegInf ? 0.f : mn;
+  st.thr = mn == kNegInf ? st.thr : kPosInf;
+  const float shift = st.mu - mu;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] -= shift;
+}
+
+template <int DT, int D, int BS>
+__global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_pipe(DecodeArgs a) {
+  using M = Mfma<DT, D, BS>;
+  constexpr bool CONVERT_V = DT == DT_BF16;  // V staged in LDS as fp16 (checked at the end)
+  constexpr int NT = kPrefillTiles;
+  constexpr int CH = kMfmaChunk;
+  constexpr int PK = D * 2 + 32;  // padded LDS rows, as in prefill_mfma
+  constexpr int PV = D * 2 + 32;
+  constexpr int VBASE = CH * PK;
+  constexpr int BUF = CH * PK + CH * PV;
+  constexpr int VECS = D * 2 / 16;
+  constexpr int PER = 2 * CH * VECS / kPrefillThreads;
+  static_assert(PER * kPrefillThreads == 2 * CH * VECS, "chunk must split evenly over the workgroup");
+  static_assert((CH * VECS) % kPrefillThreads == 0, "K rows fill whole vector steps");
+  constexpr int ROWS_PER_K = kPrefillThreads / VECS;
+  constexpr int ROWS_PER_WAVE = 64 / VECS;
+  constexpr bool UNIFORM_K = ROWS_PER_K <= BS && CH % ROWS_PER_K == 0;
+  static_assert(ROWS_PER_WAVE <= BS && CH % ROWS_PER_WAVE == 0, "a wave's rows of one vector step share a block");
+  constexpr int NB = CH / BS;
+  static_assert(NB * BS == CH, "block size must divide the chunk");
+  __shared__ __attribute__((aligned(16))) char lds[3 * BUF];
+
+  const PrefillItem it = prefill_item(a, blockIdx.x);
+  if (it.b < 0) return;  // uniform: a padding workgroup
+  const int h = it.h;
+  const int b = it.b;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int n16 = lane & 15, g4 = lane >> 4;
+  // Per-sequence values are read into scalar registers: the buffer descriptors below are
+  // built from them.
+  const int r0 = uniform(a.query_start[b]);
+  const int n = uniform(a.query_start[b + 1]) - r0;
+  const int jw = it.jw;
+  if (r0 < 0 || n <= 0 || jw >= n || r0 + jw >= a.num_tokens) return;  // uniform
+  const size_t mark = (size_t(r0 + jw) * a.num_q_heads + h) * D;
+  const int nw = min(min(kPrefillRows, n - jw), a.num_tokens - r0 - jw);
+  const int ctx = uniform(clamp_ctx(a, b));
+  const int first = ctx - n;
+  const int t1 = max(0, min(ctx, first + jw + nw));
+  const int j0 = jw + wave * 16 * NT;
+  const int nq = max(0, min(16 * NT, jw + nw - j0));
+
+  // The table row is read through a buffer descriptor with the entry's byte offset in a
+  // scalar register (t1 < 2^31 and BS >= 8, so it fits), which needs no vector address.
+  const int32_t* tbl = a.tables + size_t(b) * a.max_blocks;
+  const __amdgpu_buffer_rsrc_t tbl_rs = __builtin_amdgcn_make_buffer_rsrc((void*)tbl, (short)0, -1, kBufferWord3);
+  // The first four chunks' table entries in one load, issued before the query loads: lane j
+  // reads entry j (entry 0 for blocks past t1).
+  static_assert(4 * NB <= 64, "a wave reads the first four chunks' entries");
+  const int ids0123 = __builtin_amdgcn_raw_buffer_load_b32(
+      tbl_rs, ((lane < 4 * NB ? lane : 0) * BS < t1 ? (lane < 4 * NB ? lane : 0) : 0) * 4, 0, 0);
+
+  typename M::vec8 qop[NT][M::KK];
+  TileState<M> st[NT];
+  int lim[NT], lim_max[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int jt = j0 + 16 * t;
+    const bool col = 16 * t + n16 < nq;
+    lim[t] = col ? first + jt + n16 : -1;
+    lim_max[t] = nq > 16 * t ? first + jt + min(16, nq - 16 * t) - 1 : -1;
+#pragma unroll
+    for (int kk = 0; kk < M::KK; ++kk) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (col) {
+        const char* qp = static_cast<const char*>(a.q) + ((size_t(r0 + jt + n16) * a.num_q_heads + h) * D) * 2;
+        w = *reinterpret_cast<const uint4*>(qp + (32 * kk + 8 * g4) * 2);
+      }
+      if (a.scale_log2 < 0.f) {
+        w.x ^= 0x80008000u, w.y ^= 0x80008000u, w.z ^= 0x80008000u, w.w ^= 0x80008000u;
+      }
+      qop[t][kk] = __builtin_bit_cast(typename M::vec8, w);
+    }
+    tile_init(st[t]);
+    // A lane without a column never moves its reference (its state is never stored).
+    st[t].thr = col ? kNegInf : kPosInf;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int kk = 0; kk < M::KK; ++kk) asm volatile("" ::"v"(__builtin_bit_cast(u32x4_t, qop[t][kk])));
+
+  const float c_abs = fabsf(a.scale_log2);
+  const int kvh = h / a.group;
+  const size_t head_off = size_t(kvh) * BS * D * 2;
+  const char* kb = static_cast<const char*>(a.k_cache) + head_off;
+  const char* vb = static_cast<const char*>(a.v_cache) + head_off;
+  const uint32_t blk32 = uint32_t(size_t(a.num_kv_heads) * BS * D * 2);  // the launch checks that it fits
+  const int nch = (t1 + CH - 1) / CH;
+
+  // Block ids: vector loads (the table entry of each block of the chunk, entry 0 for blocks
+  // past t1) read back into scalar registers one chunk later, as in prefill_mfma; ids_of
+  // gives -1 for blocks past t1.
+  auto load_ids = [&](int cs, int (&raw)[NB]) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int tok = cs + k * BS;
+      raw[k] = __builtin_amdgcn_raw_buffer_load_b32(tbl_rs, 0, (tok < t1 ? tok / BS : 0) * 4, 0);
+    }
+  };
+  auto ids_of = [&](int cs, const int (&raw)[NB], int (&ids)[NB]) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int id = uniform(raw[k]);
+      ids[k] = cs + k * BS < t1 ? id : -1;
+    }
+  };
+  auto id_of = [&](const int (&ids)[NB], int off) {
+    int id = ids[0];
+#pragma unroll
+    for (int k = 1; k < NB; ++k)
+      if (off >= k * BS) id = ids[k];
+    return id;
+  };
+  // Staging geometry: vector k of a thread is chunk row RK * k + lrow (rows 0 .. CH-1 are K,
+  // CH .. 2CH-1 V), 16-byte column lcol.  A wave's rows of one vector step lie in one block.
+  constexpr int RK = kPrefillThreads / VECS;
+  const int lrow = tid / VECS, lcol = tid % VECS;
+  const uint32_t glane = uint32_t((lrow % BS) * D * 2 + lcol * 16);  // byte offset in a block
+  const int llane = lrow * PK + lcol * 16;                           // byte offset in a buffer
+  static_assert(PK == PV, "K and V rows share the LDS row pitch");
+  // The fetch reads each block through a buffer descriptor whose base is the block's slice
+  // for this KV head and whose size covers only the block's rows before t1 (none for a block
+  // outside the pool): the loads of rows outside it return zeros, so blocks outside the pool
+  // and V rows past t1 arrive zeroed with no branch and no extra instruction.  (K rows past t1
+  // are zeroed as well; their keys are masked anyway.)
+  uint4 pre[PER];
+  auto fetch = [&](int cs, const int (&ids)[NB]) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int ck = RK * k;  // first chunk row of the step
+      const bool is_v = ck >= CH;
+      const int c0 = ck % CH;
+      const int brow = UNIFORM_K ? c0 : c0 + ROWS_PER_WAVE * wave;  // a row of the wave's block
+      const int id = UNIFORM_K ? ids[c0 / BS] : id_of(ids, brow);
+      const bool valid = (unsigned)id < (unsigned)a.num_blocks;
+      const int tok0 = cs + brow / BS * BS;
+      const int span = sclamp(t1 - tok0, 0, BS);
+      const int rows = valid ? span : 0;
+      const char* base = (is_v ? vb : kb) + uint64_t(valid ? uint32_t(id) : 0u) * blk32;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rows * D * 2, kBufferWord3);
+      const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rs, glane, (c0 % BS) * D * 2, 0);
+      pre[k] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  };
+  auto stash = [&](int base) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int ck = RK * k;
+      const bool is_v = ck >= CH;
+      const int off = is_v ? VBASE + (ck - CH) * PV : ck * PK;
+      uint4 w = pre[k];
+      if constexpr (CONVERT_V) {
+        if (is_v) {
+          uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const half2_t hv = {_Float16(__builtin_bit_cast(float, x[q] << 16)),
+                                _Float16(__builtin_bit_cast(float, x[q] & 0xFFFF0000u))};
+            x[q] = __builtin_bit_cast(uint32_t, hv);
+          }
+          w = make_uint4(x[0], x[1], x[2], x[3]);
+        }
+      }
+      *reinterpret_cast<uint4*>(&lds[base + llane + off]) = w;
+    }
+  };
+  // K operands of the chunk in the buffer at kbase: rows 16hf + lane%16, elements
+  // 32kk + 8(lane/16) .. + 8.
+  auto read_k = [&](int kbase, uint4 (&kr)[2][M::KK]) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int kk = 0; kk < M::KK; ++kk)
+        kr[hf][kk] = *reinterpret_cast<const uint4*>(&lds[kbase + (16 * hf + n16) * PK + (32 * kk + 8 * g4) * 2]);
+  };
+  // V^T operands (fp16) of the chunk in the buffer at vbase, one transposed read per 16-token
+  // half and output tile, as in prefill_mfma.
+  auto read_vt = [&](int vbase, uint2 (&vlo)[M::E], uint2 (&vhi)[M::E]) {
+    lds_char* vl = (lds_char*)(lds) + vbase + VBASE + (4 * g4 + (n16 >> 2)) * PV + (4 * (lane & 3)) * 2;
+#pragma unroll
+    for (int r = 0; r < M::E; ++r) {
+      vlo[r] = read_tr16(vl + 32 * r);
+      vhi[r] = read_tr16(vl + 16 * PV + 32 * r);
+    }
+  };
+
+  // Chunk ids: idsA of chunk c, idsB of c + 1, idsC of c + 2, raw (loading) of c + 3.
+  int idsA[NB], idsB[NB], idsC[NB], raw[NB];
+  // LDS buffers (byte offsets, wave-uniform): chunk c's, c + 1's and c + 2's.
+  int bufV = 0, bufK = BUF, bufS = 2 * BUF;
+  float4_t sc[NT][2];  // scores of chunk c
+  {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      idsA[k] = k * BS < t1 ? __builtin_amdgcn_readlane(ids0123, k) : -1;
+      idsB[k] = CH + k * BS < t1 ? __builtin_amdgcn_readlane(ids0123, NB + k) : -1;
+      idsC[k] = 2 * CH + k * BS < t1 ? __builtin_amdgcn_readlane(ids0123, 2 * NB + k) : -1;
+      raw[k] = __builtin_amdgcn_readlane(ids0123, 3 * NB + k);
+    }
+  }
+  // Chunks past t1 read nothing (their blocks count no rows), so these need no guard.  The
+  // first two chunks' loads are in flight together.
+  {
+    fetch(0, idsA);
+    uint4 first_rows[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) first_rows[k] = pre[k];
+    fetch(CH, idsB);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const uint4 w = pre[k];
+      pre[k] = first_rows[k];
+      first_rows[k] = w;
+    }
+    stash(0);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) pre[k] = first_rows[k];
+    stash(BUF);
+  }
+  fetch(2 * CH, idsC);
+  __syncthreads();
+  if (nq > 0 && nch > 0) {
+    uint4 kr[2][M::KK];
+    read_k(0, kr);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pipe_scores<M>(kr, qop[t], sc[t]);
+  }
+
+  // One iteration.  KIND 0: chunk c unmasked, for a wave with columns; KIND 2: chunk c
+  // masked (a wave computes the chunks some tile of it still needs).
+  auto iter = [&](int c, auto kind) {
+    constexpr int KIND = decltype(kind)::value;
+    const int cs = c * CH;
+    bool busy_p = KIND == 0, busy_s = KIND == 0;  // wave-uniform
+    if constexpr (KIND == 2) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        busy_p |= cs <= lim_max[t];
+        busy_s |= cs + CH <= lim_max[t];
+      }
+    }
+    // The next chunk's scores.  A wave that skips them here skips that chunk's softmax and
+    // P.V as well, so the value they then carry is never read.
+    float4_t sn[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) sn[t][hf] = __builtin_nondeterministic_value(float4_t{});
+    half8_t ph[NT];
+    {
+      // The K reads first; then the exponents, which free the scores' registers for the next
+      // chunk's; then the next chunk's score products between this chunk's probabilities and
+      // row sums.
+      float e[NT][8], ln[NT];
+      uint4 kr[2][M::KK];
+      if (busy_s) read_k(bufK, kr);
+      if (busy_p) {
+        if constexpr (KIND == 0) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) tile_exps<M, false>(cs, g4, c_abs, sc[t], st[t], lim[t], 0xFFu, e[t]);
+        } else {
+          uint32_t okbits = 0xFFu;
+          bool need_mask = cs + CH > t1;
+#pragma unroll
+          for (int k = 0; k < NB; ++k) need_mask |= (unsigned)idsA[k] >= (unsigned)a.num_blocks;
+          if (need_mask) {
+            okbits = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int off = 16 * (j >> 2) + 4 * g4 + (j & 3);
+              if (cs + off < t1 && (unsigned)id_of(idsA, off) < (unsigned)a.num_blocks) okbits |= 1u << j;
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t) pipe_exps_masked(lim[t] - cs - 4 * g4, c_abs, sc[t], st[t], okbits, e[t]);
+        }
+      }
+      if constexpr (KIND == 0) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      if (busy_s) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) pipe_scores<M>(kr, qop[t], sn[t]);
+      }
+      if (busy_p) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) ln[t] = pipe_probs(e[t], st[t].l, ph[t]);
+      }
+      if constexpr (KIND == 0) {
+#pragma unroll
+        for (int i = 0; i < 2 * M::E; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (busy_p) {
+        bool bad = false;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bad |= !(ln[t] < st[t].thr);
+        if (__builtin_amdgcn_ballot_w64(bad)) {  // rare: a reference moves
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            if (__builtin_amdgcn_ballot_w64(!(ln[t] < st[t].thr))) {
+              pipe_rescale(st[t], e[t]);
+              ln[t] = pipe_probs(e[t], st[t].l, ph[t]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) st[t].l = ln[t];
+      }
+    }
+    // This chunk's V^T reads and P.V products, between the instructions that stage chunk
+    // c + 2.
+    if (busy_p) {
+      uint2 vlo[M::E], vhi[M::E];
+      read_vt(bufV, vlo, vhi);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < M::E; ++r)
+          st[t].acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(half8_t, make_uint4(vlo[r].x, vlo[r].y, vhi[r].x, vhi[r].y)), ph[t],
+              st[t].acc[r], 0, 0, 0);
+    }
+    stash(bufS);
+    if constexpr (KIND == 0) {
+#pragma unroll
+      for (int i = 0; i < 2 * M::E; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 1);
+      }
+    }
+    // The next chunk's loads; past the walk's end they read nothing.
+    int idsD[NB];
+    ids_of(cs + 3 * CH, raw, idsD);
+    fetch(cs + 3 * CH, idsD);
+    load_ids(cs + 4 * CH, raw);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      idsA[k] = idsB[k];
+      idsB[k] = idsC[k];
+      idsC[k] = idsD[k];
+    }
+    const int bv = bufV;
+    bufV = bufK;
+    bufK = bufS;
+    bufS = bv;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      sc[t][0] = sn[t][0];
+      sc[t][1] = sn[t][1];
+    }
+    __syncthreads();
+  };
+  const int n_plain = min(nch, max(0, (first + jw + 1) / CH));
+  auto plain_bad = [&]() {
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) bad |= (unsigned)idsA[k] >= (unsigned)a.num_blocks;
+    return bad;
+  };
+  // A wave without columns takes the masked form throughout: it computes nothing there and
+  // only stages.
+  int c = 0;
+  if (nq > 0)
+    for (; c < n_plain && !plain_bad(); ++c) iter(c, std::integral_constant<int, 0>{});
+  for (; c < nch; ++c) iter(c, std::integral_constant<int, 2>{});
+
+  if constexpr (CONVERT_V) {
+    // An inf in a staged V row (a bf16 value from 2^16 up) leaves some accumulator
+    // non-finite: the workgroup then stores only a NaN in element 0 of its first row, and
+    // the exact fix-up kernel (prefill_mfma, kFixup) redoes it.
+    __shared__ int redo;
+    if (tid == 0) redo = 0;
+    __syncthreads();
+    bool badv = false;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < M::E; ++r)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) badv |= !__builtin_isfinite(st[t].acc[r][v]);
+    if (__builtin_amdgcn_ballot_w64(badv) && lane == 0) redo = 1;
+    __syncthreads();
+    if (redo) {
+      if (tid == 0) static_cast<uint16_t*>(a.out)[mark] = DT == DT_BF16 ? 0x7FC0u : 0x7E00u;
+      return;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    st[t].l = xor_sum_16_32(st[t].l);
+    if (16 * t + n16 < nq) {
+      const float inv = st[t].l > 0.f ? 1.f / st[t].l : 0.f;
+      const size_t row = (size_t(r0 + j0 + 16 * t + n16) * a.num_q_heads + h) * D;
+#pragma unroll
+      for (int r = 0; r < M::E; ++r) {
+        const float v[4] = {st[t].acc[r][0] * inv, st[t].acc[r][1] * inv, st[t].acc[r][2] * inv,
+                            st[t].acc[r][3] * inv};
+        store4<DT>(a.out, row + 16 * r + 4 * g4, v);
+      }
+    }
+  }
+}
+
 }  // namespace pkv
 
 namespace {
@@ -667,8 +1175,8 @@ struct PrefillKernels {
 
 template <int DT, int D, int BS>
 PrefillKernels prefill_pair() {
-  if constexpr (DT == DT_BF16) return {prefill_mfma<DT, D, BS, kFast>, prefill_mfma<DT, D, BS, kFixup>};
-  else return {prefill_mfma<DT, D, BS, kExact>, nullptr};
+  if constexpr (DT == DT_BF16) return {prefill_pipe<DT, D, BS>, prefill_mfma<DT, D, BS, kFixup>};
+  else return {prefill_pipe<DT, D, BS>, nullptr};
 }
 
 template <int DT, int D>
