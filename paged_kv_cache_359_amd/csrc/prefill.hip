@@ -1106,6 +1106,9 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
       sc[t][0] = sn[t][0];
       sc[t][1] = sn[t][1];
     }
+    // Every product is issued before the barrier, so that the matrix cores work through the
+    // wait (the scheduler would otherwise move the last ones past it).
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   };
   const int n_plain = min(nch, max(0, (first + jw + 1) / CH));
