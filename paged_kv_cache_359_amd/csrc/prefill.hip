@@ -16,10 +16,15 @@ namespace pkv {
 // query_start[b] .. query_start[b+1]; with ctx_b tokens cached (the new ones included), new
 // token j sits at position ctx_b - n_b + j and sees keys 0 .. that position.
 // The workgroup walks the keys its rows need in 32-token chunks.  Each chunk's K and V rows
-// are gathered through the block table once per workgroup into LDS (rows padded by 16 bytes
-// so that the waves' row reads spread over the banks), double-buffered: the global loads of
-// chunk c+1 are in flight while the waves compute chunk c from LDS.  Neighbouring workgroups
-// and the query heads of a group read the same K/V, so it is read through the caches.
+// are gathered through the block table once per workgroup into LDS (rows padded by 32 bytes
+// so that the waves' row reads spread over the banks).  Neighbouring workgroups and the
+// query heads of a group read the same K/V, so it is read through the caches.
+//
+// Two kernels share this layout.  prefill_pipe (further below) is the walk every call runs:
+// fp16 products, three LDS buffers, each iteration overlapping one chunk's softmax with the
+// next chunk's score products.  prefill_mfma is the earlier two-buffer walk, kept for the
+// exact bf16 form that the fix-up pass runs for the rare workgroup whose fp16-staged V
+// overflowed.
 // =========================================================================================
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4;
@@ -148,33 +153,14 @@ __device__ __forceinline__ void tile_rescale(TileState<M>& st, float lm, float (
   for (int j = 0; j < 8; ++j) e[j] -= shift;
 }
 
-// 3. tile_accum: the probabilities, their row sum l and P.V.  F16PV (bf16 only): the chunk's
-//    V rows were staged in LDS as fp16, and the probabilities go into an fp16 product as
-//    well (11 significant bits, no remainder product); l then adds up the same fp16
-//    probabilities, with dot products against (1, 1) that accumulate in fp32, so that the
-//    weights of the output are exactly those of the product.
-template <typename M, bool F16PV>
+// 3. tile_accum: the probabilities, their row sum l and P.V in the cache's type (for bf16,
+//    P split into a high part and a remainder, two products).
+template <typename M>
 __device__ __forceinline__ void tile_accum(const typename M::Chunk& ck, TileState<M>& st,
                                            const float (&e)[8]) {
   float p[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) p[j] = exp2_hw(e[j]);
-  if constexpr (M::SPLIT_P && F16PV) {
-    half8_t ph;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ph[j] = _Float16(p[j]);
-    const half2_t one2 = {_Float16(1.f), _Float16(1.f)};
-    float l = st.l;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      l = __builtin_amdgcn_fdot2(half2_t{ph[2 * q], ph[2 * q + 1]}, one2, l, false);
-    st.l = l;
-#pragma unroll
-    for (int r = 0; r < M::E; ++r)
-      st.acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ck.vop[r]), ph,
-                                                          st.acc[r], 0, 0, 0);
-    return;
-  }
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   typename M::vec8 phi, plo;
   if constexpr (M::SPLIT_P) {
@@ -209,22 +195,20 @@ constexpr int kPrefillWaves = 4;  // waves per workgroup
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kPrefillRows = kPrefillWaves * 16 * kPrefillTiles;  // new tokens per workgroup
 
-// Kernel forms.  kExact: P.V in the cache's type (bf16 with P split into two products).
-// kFast (bf16 only): V staged in LDS as fp16 (round to nearest) and P.V as one fp16
-// product.  The conversion is exact for bf16 magnitudes in fp16's normal range [2^-14,
-// 2^16) (8 significant bits fit in 11).  Below 2^-14 fp16 subnormals keep fewer bits and
-// magnitudes below 2^-25 become 0: an absolute error of at most 2^-25 per element, which
-// moves an output by at most 2^-25 as well (it is a convex combination of the rows).  From
-// 2^16 up a value becomes inf.  An inf in any V
-// row the walk stages makes an accumulator of every column it meets inf or NaN (0 * inf is
-// NaN), so when every column of the workgroup ends finite no value overflowed and
-// the outputs are stored; otherwise the workgroup stores only a NaN in element 0 of its
-// first row.  kFixup (bf16 only, launched after kFast over the same grid): a workgroup
-// whose element 0 of its first row is finite returns at once; any other walks its keys in
-// the exact form and stores them (a V that really holds inf or NaN gives the same
-// non-finite result there).  The exact walk lives in a kernel of its own because, inlined
-// after the fast one, it made the usual walk 5% slower.
-enum { kExact = 0, kFast = 1, kFixup = 2 };
+// The exact bf16 fix-up.  prefill_pipe stages bf16 V in LDS as fp16 (round to nearest) and
+// takes one fp16 product.  The conversion is exact for bf16 magnitudes in fp16's normal
+// range [2^-14, 2^16) (8 significant bits fit in 11).  Below 2^-14 fp16 subnormals keep fewer
+// bits and magnitudes below 2^-25 become 0: an absolute error of at most 2^-25 per element,
+// which moves an output by at most 2^-25 as well (it is a convex combination of the rows).
+// From 2^16 up a value becomes inf.  An inf in any V row the walk stages makes an
+// accumulator of every column it meets inf or NaN (0 * inf is NaN), so when every column of
+// a workgroup ends finite no value overflowed and the outputs are stored; otherwise the
+// workgroup stores only a NaN in element 0 of its first row.  prefill_mfma, launched after
+// it over the same grid, returns at once in a workgroup whose element 0 of its first row is
+// finite; any other walks its keys in the exact form (P.V in bf16 with P split into two
+// products) and stores them (a V that really holds inf or NaN gives the same non-finite
+// result there).  The exact walk lives in a kernel of its own because, inlined after the
+// fast one, it made the usual walk 5% slower.
 
 // The work of one workgroup: query head h of sequence b, new tokens jw .. jw + 127.
 struct PrefillItem {
@@ -255,10 +239,10 @@ __device__ __forceinline__ PrefillItem prefill_item(const DecodeArgs& a, unsigne
   return {kvh * a.group + (rem - lu * a.group), b, (a.row_tiles - 1 - zr) * kPrefillRows};
 }
 
-template <int DT, int D, int BS, int MODE>
+template <int DT, int D, int BS>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   using M = Mfma<DT, D, BS>;
-  static_assert(MODE == kExact || DT == DT_BF16, "the fp16 form is for bf16 caches");
+  static_assert(DT == DT_BF16, "the exact fix-up is for bf16 caches");
   constexpr int NT = kPrefillTiles;
   constexpr int CH = kMfmaChunk;
   // LDS bytes per K row and per V row, padded so that the waves' reads spread over the banks
@@ -290,11 +274,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   // Uniform over the workgroup, so returning here skips no barrier another wave waits at.
   if (r0 < 0 || n <= 0 || jw >= n || r0 + jw >= a.num_tokens) return;
   const size_t mark = (size_t(r0 + jw) * a.num_q_heads + h) * D;  // element 0 of the first row
-  if constexpr (MODE == kFixup) {
+  {
     const uint32_t bits = static_cast<const uint16_t*>(a.out)[mark];
-    const float x = DT == DT_BF16 ? __builtin_bit_cast(float, bits << 16)
-                                  : float(__builtin_bit_cast(_Float16, uint16_t(bits)));
-    if (__builtin_isfinite(x)) return;  // same element for every thread: uniform
+    if (__builtin_isfinite(__builtin_bit_cast(float, bits << 16))) return;  // same element for every thread: uniform
   }
   const int nw = min(min(kPrefillRows, n - jw), a.num_tokens - r0 - jw);  // rows of the workgroup
   const int ctx = clamp_ctx(a, b);
@@ -422,35 +404,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
       }
     }
   };
-  // F16PV: V rows go to LDS as fp16 (round to nearest: exact for bf16 magnitudes in
-  // [2^-14, 2^16), off by at most 2^-25 below that range, inf from 2^16 up).
-  auto stash = [&](int buf, auto f16pv) {
-    constexpr bool F16PV = decltype(f16pv)::value;
+  auto stash = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int v = tid + kPrefillThreads * k;
       const int row = v / VECS, col = v % VECS;
       const bool is_v = k >= PER / 2;
       const int off = is_v ? VBASE + (row - CH) * PV : row * PK;
-      uint4 w = pre[k];
-      if constexpr (F16PV) {
-        if (is_v) {
-          uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const half2_t hv = {_Float16(__builtin_bit_cast(float, x[q] << 16)),
-                                _Float16(__builtin_bit_cast(float, x[q] & 0xFFFF0000u))};
-            x[q] = __builtin_bit_cast(uint32_t, hv);
-          }
-          w = make_uint4(x[0], x[1], x[2], x[3]);
-        }
-      }
-      *reinterpret_cast<uint4*>(&lds[buf][off + col * 16]) = w;
+      *reinterpret_cast<uint4*>(&lds[buf][off + col * 16]) = pre[k];
     }
   };
 
-  // The whole walk over the chunks, with fresh tile states.  F16PV (bf16 only) stages V as
-  // fp16 and takes the fp16 product for P.V.
+  // The whole walk over the chunks, with fresh tile states.
   //
   // The walk is software-pipelined over three chunks.  While the waves compute chunk c from
   // LDS buffer c % 2, they stash chunk c + 1 (loaded while chunk c - 1 was computed) into the
@@ -459,8 +424,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   // a chunk the matrix-core products and the vector work of other steps are interleaved:
   // the score products with the V^T reads and the stash of the next chunk, the P.V products
   // of one tile with the exponents of the other.
-  auto run = [&](auto f16pv) {
-  constexpr bool F16PV = decltype(f16pv)::value;
+  auto run = [&]() {
 #pragma unroll
   for (int t = 0; t < NT; ++t) tile_init(st[t]);
   // Block ids of chunks c and c + 1 (wave-uniform) for the loop's chunk c, and in raw those
@@ -477,7 +441,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
     to_uniform(ids0);
     to_uniform(ids1);
     fetch(0, ids0);
-    stash(0, f16pv);
+    stash(0);
     if (nch > 1) fetch(CH, ids1);
   }
   __syncthreads();
@@ -548,7 +512,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
       }
       // The stash runs on every chunk, so that it shares the products' basic block: after
       // the last chunk it writes stale registers into a buffer that nothing reads again.
-      stash((c + 1) & 1, f16pv);
+      stash((c + 1) & 1);
       // The products wait only for the K reads: the V^T reads and the stash's conversions
       // and writes are issued between them.
 #pragma unroll
@@ -566,7 +530,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
       for (int t = 0; t < NT; ++t)
         lm[t] = tile_exps<M, MASKED>(cs, g4, c_abs, sc[t], st[t], lim[t], okbits, e[t]);
     } else {
-      stash((c + 1) & 1, f16pv);
+      stash((c + 1) & 1);
     }
     int ids2[NB];
 #pragma unroll
@@ -585,7 +549,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
           if (__builtin_amdgcn_ballot_w64(lm[t] > st[t].thr)) tile_rescale(st[t], lm[t], e[t]);
       }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) tile_accum<M, F16PV>(ck, st[t], e[t]);
+      for (int t = 0; t < NT; ++t) tile_accum<M>(ck, st[t], e[t]);
     }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
@@ -614,26 +578,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
   for (; c < nch; ++c) step(c, std::integral_constant<int, 2>{});
   };
 
-  if constexpr (MODE == kFast) {
-    __shared__ int redo;
-    if (tid == 0) redo = 0;
-    run(std::true_type{});
-    bool bad = false;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < M::E; ++r)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) bad |= !__builtin_isfinite(st[t].acc[r][v]);
-    if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) redo = 1;
-    __syncthreads();
-    if (redo) {  // uniform: leave the workgroup to the exact form
-      if (tid == 0) static_cast<uint16_t*>(a.out)[mark] = DT == DT_BF16 ? 0x7FC0u : 0x7E00u;
-      return;
-    }
-  } else {
-    run(std::false_type{});
-  }
+  run();
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     st[t].l = xor_sum_16_32(st[t].l);
@@ -1128,7 +1073,7 @@ __global__ __launch_bounds__(kPrefillThreads) __attribute__((amdgpu_waves_per_eu
   if constexpr (CONVERT_V) {
     // An inf in a staged V row (a bf16 value from 2^16 up) leaves some accumulator
     // non-finite: the workgroup then stores only a NaN in element 0 of its first row, and
-    // the exact fix-up kernel (prefill_mfma, kFixup) redoes it.
+    // the exact fix-up kernel (prefill_mfma) redoes it.
     __shared__ int redo;
     if (tid == 0) redo = 0;
     __syncthreads();
@@ -1170,15 +1115,15 @@ using namespace pkv;
 
 typedef void (*kernel_fn)(DecodeArgs);
 
-// The kernels of one call: fp16 caches run kExact alone; bf16 caches run kFast, then
-// kFixup over the same grid.
+// The kernels of one call: prefill_pipe, and for bf16 caches the exact fix-up prefill_mfma
+// over the same grid.
 struct PrefillKernels {
   kernel_fn first = nullptr, second = nullptr;
 };
 
 template <int DT, int D, int BS>
 PrefillKernels prefill_pair() {
-  if constexpr (DT == DT_BF16) return {prefill_pipe<DT, D, BS>, prefill_mfma<DT, D, BS, kFixup>};
+  if constexpr (DT == DT_BF16) return {prefill_pipe<DT, D, BS>, prefill_mfma<DT, D, BS>};
   else return {prefill_pipe<DT, D, BS>, nullptr};
 }
 
