@@ -599,9 +599,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
 
 // =========================================================================================
 // The pipelined walk, for the fp16 products (bf16 caches with V staged as fp16, and fp16
-// caches).  Same workgroups, tiles, work order and chunk staging as prefill_mfma; the chunk
-// walk is arranged so that one wave keeps the matrix cores and the vector units busy side by
-// side:
+// caches).  Same workgroups, tiles and work order as prefill_mfma, with a third LDS buffer
+// and the chunk rows read through buffer descriptors; the chunk walk is arranged so that one
+// wave keeps the matrix cores and the vector units busy side by side:
 //
 // - iteration c issues the score products of chunk c + 1 between the vector instructions of
 //   chunk c's softmax (exponents, fp16 probabilities, row sums), then chunk c's P.V products
@@ -615,7 +615,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_mfma(DecodeArgs a) {
 //   per-chunk maximum, which is taken only on the rare path that moves the reference.
 //   Probabilities stay in [0, 65504] and the largest one a column has seen is at least 1
 //   (the reference is set to a column maximum), so fp16 keeps 11 significant bits of each,
-//   as in prefill_mfma's form with its smaller slack.
+//   as it would with a smaller slack.
 // =========================================================================================
 constexpr float kPosInf = __builtin_inff();
 // max(lo, min(x, hi)) of wave-uniform values in scalar registers.  (Written out, the clamp
