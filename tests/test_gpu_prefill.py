@@ -175,6 +175,33 @@ def test_prefill_tiny_values(dtype):
           flush=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("pattern", ["rising", "sawtooth"])
+def test_prefill_reference_moves_many_times(dtype, pattern):
+    """Scores that climb along the keys, so that a column's running reference has to move
+    again and again during one walk (the kernel moves it only when an fp16 probability
+    overflows, i.e. a score climbs about 16 above it in log2 units, or while it is -inf).
+    Key t of a sequence is (t' / 512) * (1, .., 1), the query 8 * (1, .., 1): the score of
+    key t is 2 t' and its log2-domain exponent 2 t' * scale * log2(e) ~ 0.255 t', about 8
+    more per 32-key chunk.  rising: t' = t, so the reference moves every few chunks and
+    every earlier key's weight underflows; sawtooth: t' = t mod 160, so the score climbs,
+    falls back far below the reference and climbs again."""
+    cfg = W.get_config("prefill_llama7b", batch=2, lengths=("fixed", (300, 900)),
+                       num_blocks=128, dtype=dtype)
+    print(f"[case] reference moves {dtype} {pattern}", flush=True)
+    w = W.make_workload(cfg, device="cuda")
+    qs = [int(x) for x in w.query_start]
+    pos = torch.cat([torch.arange(qs[b + 1] - qs[b]) for b in range(len(qs) - 1)]).to("cuda")
+    tp = pos if pattern == "rising" else pos % 160
+    w.k_tok.copy_((tp.float() / 512.0)[:, None, None].expand_as(w.k_tok).to(w.k_tok.dtype))
+    w.q.fill_(8.0)
+    g = gpu_side.build(w)
+    o = oracle_side.build(gpu_side.to_cpu(w), fill=gpu_side.SENTINEL_BITS[dtype])
+    out = g.prefill().double().cpu().numpy()
+    err = check(out, o.prefill(), dtype, f"reference moves, {pattern}")
+    print(f"  max abs err {err:.3g}", flush=True)
+
+
 def test_prefill_matches_decode_kernel_on_the_last_row():
     """The newest row of a prefill and a decode of that sequence read the same keys."""
     w, g, o = both("prefill_chunked_gqa", batch=2, lengths=("fixed", (300, 77)), num_blocks=80)
