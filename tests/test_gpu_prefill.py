@@ -64,8 +64,8 @@ for dtype in ("f16", "bf16"):
 
 @pytest.mark.parametrize("dtype,d,bs,hq,hkv", SHAPES)
 def test_prefill_shape_sweep(dtype, d, bs, hq, hkv):
-    # Ragged new-token counts around the 16-token column tiles and 64-token workgroup tiles,
-    # fresh prompts and chunks on top of cached context.
+    # Ragged new-token counts around the 16-token column tiles, the 32-token wave tiles and
+    # the 128-token workgroup tiles, fresh prompts and chunks on top of cached context.
     lengths = (1, 15, 16, 17, 64, 65, 130, 200)
     for new in (("all",), ("fixed", 47)):
         cfg = dict(dtype=dtype, head_dim=d, block_size=bs, num_q_heads=hq, num_kv_heads=hkv,
