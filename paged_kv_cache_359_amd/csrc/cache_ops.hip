@@ -75,7 +75,10 @@ __device__ __forceinline__ int32_t load_sys(const int32_t* p) {
 // One workgroup per appended token t: thread 0 reads the token's slot (and, with tables, its
 // row and position) once and records the table entry and length as update_tables_kernel
 // does; then the workgroup copies the token's K and V rows of every head into the slot, 16
-// bytes per thread per step, as reshape_and_cache_kernel does.
+// bytes per thread per step, as reshape_and_cache_kernel does.  The host reads go out
+// together, and each thread's first four vectors of K and of V are loaded before the slot is
+// known, so the new rows' reads overlap the round trip to host memory.
+
 __global__ __launch_bounds__(256) void append_and_cache_kernel(
     const uint4* __restrict__ key, const uint4* __restrict__ value,
     const int64_t* __restrict__ slots, const int32_t* __restrict__ rows,
@@ -84,31 +87,49 @@ __global__ __launch_bounds__(256) void append_and_cache_kernel(
     int32_t block_size, int64_t num_slots, int32_t num_rows, int32_t max_blocks) {
   __shared__ int64_t s_slot;
   const int64_t t = blockIdx.x;
+  const int32_t hv = heads * row_vecs;
+  // Four vectors of K and of V per thread, in named registers (an array indexed in a loop
+  // with an early exit would live in scratch memory), read before anything waits.
+  const int32_t i0 = threadIdx.x, i1 = i0 + blockDim.x, i2 = i1 + blockDim.x, i3 = i2 + blockDim.x;
+  auto at = [&](int32_t i) { return t * hv + min(i, hv - 1); };  // past the rows: read again
+  const uint4 k0 = key[at(i0)], k1 = key[at(i1)], k2 = key[at(i2)], k3 = key[at(i3)];
+  const uint4 v0 = value[at(i0)], v1 = value[at(i1)], v2 = value[at(i2)], v3 = value[at(i3)];
   if (threadIdx.x == 0) {
+    // The three host reads go out together: an absent array is stood in for by the slot's
+    // own address (always readable), and its value is not used.
+    const int32_t* stand_in = reinterpret_cast<const int32_t*>(slots + t);
     const int64_t s = load_sys(slots + t);
-    s_slot = s;
-    if (tables && s >= 0 && s < num_slots) {
-      const int32_t r = rows ? load_sys(rows + t) : int32_t(t);
-      const int32_t p = load_sys(pos + t);
-      if ((unsigned)r < (unsigned)num_rows && p >= 0 && p / block_size < max_blocks) {
+    const int32_t r_in = load_sys(rows ? rows + t : stand_in);
+    const int32_t p = load_sys(tables ? pos + t : stand_in);
+    if (tables) {
+      const int32_t r = rows ? r_in : int32_t(t);
+      if (s >= 0 && s < num_slots && (unsigned)r < (unsigned)num_rows && p >= 0 &&
+          p / block_size < max_blocks) {
         tables[int64_t(r) * max_blocks + p / block_size] = int32_t(s / block_size);
         lens[r] = p + 1;
       }
     }
+    s_slot = s;
   }
   __syncthreads();
   const int64_t s = s_slot;
   if (s < 0 || s >= num_slots) return;
   const int64_t blk = s / block_size;
   const int64_t off = s - blk * block_size;
-  const int32_t hv = heads * row_vecs;
-  for (int32_t i = threadIdx.x; i < hv; i += blockDim.x) {
-    const int32_t h = i / row_vecs;
-    const int32_t c = i - h * row_vecs;
-    const int64_t dst = ((blk * heads + h) * block_size + off) * row_vecs + c;
-    k_cache[dst] = key[t * hv + i];
-    v_cache[dst] = value[t * hv + i];
-  }
+  const int64_t base = (blk * heads * block_size + off) * row_vecs;
+  auto put = [&](int32_t i, const uint4& kv, const uint4& vv) {
+    if (i < hv) {
+      const int32_t h = i / row_vecs;
+      const int64_t d = base + (int64_t(h) * block_size - h) * row_vecs + i;
+      k_cache[d] = kv;
+      v_cache[d] = vv;
+    }
+  };
+  put(i0, k0, v0);
+  put(i1, k1, v1);
+  put(i2, k2, v2);
+  put(i3, k3, v3);
+  for (int32_t i = i3 + blockDim.x; i < hv; i += blockDim.x) put(i, key[t * hv + i], value[t * hv + i]);
 }
 
 // Whole-block moves between the pools and a contiguous buffer (swap preemption): with
