@@ -55,6 +55,75 @@ def decode_source_sha():
     return h.hexdigest()
 
 
+class DeviceEvent:
+    """A HIP timing event created with ``hipEventDisableSystemFence``, for timing work on the
+    device only.  Recording a default event (``torch.cuda.Event``) adds a system-scope fence:
+    the caches are written back and invalidated between the kernels it brackets, a few
+    microseconds that the kernels of a real step do not pay.  Without the fence the event
+    still waits for the work before it, and a host wait on it still returns only once that
+    work is done; what it gives up is making device writes visible to the host, which no
+    caller of it needs.  Same interface as the torch event where the benchmark uses it."""
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            from paged_kv_cache_359_amd import _lib
+            # Through the library's handle, so the symbols come from the HIP runtime that it
+            # and PyTorch share, never from a second copy.
+            hip = _lib.load()
+            vp = ctypes.c_void_p
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [vp, vp]
+            hip.hipEventSynchronize.argtypes = [vp]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            hip.hipEventDestroy.argtypes = [vp]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._e = ctypes.c_void_p()
+        self._check(self._lib().hipEventCreateWithFlags(ctypes.byref(self._e), 0x20000000),
+                    "hipEventCreateWithFlags")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def record(self, stream=None):
+        """On ``stream`` (a torch stream), by default the current one."""
+        import ctypes
+        import torch
+        st = torch.cuda.current_stream() if stream is None else stream
+        self._check(self._hip.hipEventRecord(self._e, ctypes.c_void_p(st.cuda_stream)), "hipEventRecord")
+
+    def synchronize(self):
+        self._check(self._hip.hipEventSynchronize(self._e), "hipEventSynchronize")
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        self._check(self._hip.hipEventElapsedTime(ctypes.byref(ms), self._e, end._e), "hipEventElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self._e:
+            self._hip.hipEventDestroy(self._e)
+
+
+EVENT_KIND = "device"
+
+
+def timing_event():
+    """The event the benchmark times device work with (see DeviceEvent); ``--events torch``
+    takes torch's default event instead."""
+    import torch
+    return DeviceEvent() if EVENT_KIND == "device" else torch.cuda.Event(enable_timing=True)
+
+
 def run_timed(fn, first, last, sync):
     """Runs fn(first) .. fn(last - 1) between two device synchronisations and returns the wall
     time in seconds.  Python's cyclic garbage collector is run before and kept off inside, so
@@ -108,7 +177,7 @@ def read_ceiling(dev, slice_bytes, nbytes=4 << 30, runs=10, warmup=3):
         n = nbytes // chunk
         evs = []
         for _ in range(warmup + runs):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = timing_event(), timing_event()
             e0.record()
             pkv.pkv_read_probe(buf, chunk, cs, order, n)
             e1.record()
@@ -140,7 +209,7 @@ def kernel_protocol(launch, nbytes, dev, warmup=10, runs=100, evict_bytes=1 << 3
     for i in range(warmup + runs):
         scratch.fill_(i & 0xFF)
         clean.sum()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = timing_event(), timing_event()
         e0.record()
         launch()
         e1.record()
@@ -199,6 +268,10 @@ def parse():
                     help="with --summarize-counters: ';'-separated counter lists, one per run")
     ap.add_argument("--trace-args", default="",
                     help="with --summarize-trace: the bench.py arguments the traced run used")
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="bracket the decode call with timing events in every n-th timed step")
+    ap.add_argument("--events", choices=["device", "torch"], default="device",
+                    help="timing events: without the system-scope fence (default), or torch's")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (scales HBM counters)")
     return ap.parse_args()
@@ -582,7 +655,7 @@ def main_prefill(args, cfg):
     max_ctx = int(w.lengths.max())
     stream = torch.cuda.current_stream(dev)
     total_steps = args.warmup + args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev = [(timing_event(), timing_event())
           for _ in range(total_steps)]
 
     def step(s):
@@ -729,7 +802,7 @@ def main_swap(args):
 
     before = decode()
     total = args.warmup + args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
+    ev = [[timing_event() for _ in range(5)] for _ in range(total)]
     host_s = [0.0]
 
     direct = args.swap_mode == "direct"
@@ -877,7 +950,7 @@ def main_cascade(args):
     for key, fn in runs.items():
         for _ in range(args.warmup):
             fn()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ev = [(timing_event(), timing_event())
               for _ in range(args.steps)]
 
         def one(i):
@@ -1014,7 +1087,7 @@ def main_prefix_cache(args):
             slots_d[lo:hi].copy_(slots_h[lo:hi], non_blocking=True)
             alloc.pkv_get_block_tables(bt, max_blocks, th[bi, :len(bt)])
             tab_d[bi, :len(bt)].copy_(tab_h[bi, :len(bt)], non_blocking=True)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e = [timing_event() for _ in range(3)]
             e[0].record(stream)
             pkv.pkv_reshape_and_cache(k_all[lo:hi], v_all[lo:hi], slots_d[lo:hi], k_cache, v_cache)
             e[1].record(stream)
@@ -1208,7 +1281,8 @@ def summarize(config, outdir):
          f"--config {C} --steps 16 --warmup 4 --no-cpu-baseline --no-extras > {rel}/kt_{C}.log",
          f"  python3 bench.py --config {C} --summarize {rel}",
          f"decode_source_sha256: {sha}", "",
-         "bench.py line of the same run (HIP events on the launch stream, 16 timed steps):",
+         "bench.py line of the same run (16 timed steps; HIP events on the launch stream around "
+         f"the decode call of {bj['timing_events']['decode_calls_bracketed']} of them):",
          f"  decode_kernel_ms {bj['decode_kernel_ms']}  roofline.achieved {r0['achieved']} GB/s  "
          f"frac {r0['frac']}  bytes_per_launch {r0['bytes_per_launch']}  step value {bj['value']} GB/s  "
          f"ms_per_step {bj['ms_per_step']}", "",
@@ -1230,7 +1304,9 @@ def summarize(config, outdir):
 
 
 def main():
+    global EVENT_KIND
     args = parse()
+    EVENT_KIND = args.events
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the paged decode path here runs on a single GPU).", file=sys.stderr)
@@ -1278,8 +1354,11 @@ def main():
     max_len_final = int(w.lengths.max()) + total_steps - 1
     out = torch.empty((B, c.num_q_heads, c.head_dim), dtype=c.torch_dtype, device=dev)
     ids = np.arange(B, dtype=np.int64)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(total_steps)]
+    # The decode call is bracketed by events in every time_every-th step (each recorded event
+    # leaves the GPU idle a few microseconds); its time is the mean over those steps.
+    te = max(1, min(args.time_every, args.steps))
+    bracketed = [s for s in range(total_steps) if (s - args.warmup) % te == te - 1]
+    ev = {s: (timing_event(), timing_event()) for s in bracketed}
     kv_per_token = 2 * c.num_kv_heads * c.head_dim * c.dsize
     step_bytes = [kv_per_token * int(np.sum(w.lengths + s)) for s in range(total_steps)]
     saved = [] if args.check else None
@@ -1287,11 +1366,11 @@ def main():
     # One stream; the device keeps the block tables and lengths, and the append kernel reads
     # each step's slots and positions from pinned host memory in place.
     stepper = DecodeStep(alloc, ids, k_cache, v_cache, c.num_q_heads, max_len_final, c.scale,
-                         args.partition, cache_hint=use_hint)
+                         args.partition, cache_hint=use_hint, mark_every=te)
     workspace = stepper.workspace
 
     def step(s):
-        stepper(k_new[s], v_new[s], q[s], out, ev[s])
+        stepper(k_new[s], v_new[s], q[s], out, ev.get(s))
         if saved is not None:
             saved.append(out.clone())
 
@@ -1329,10 +1408,12 @@ def main():
     K = args.steps
     ms_per_step = elapsed * 1e3 / K
     timed = range(args.warmup, total_steps)
-    kern_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in timed]
+    timed_ev = [s for s in timed if s in ev]
+    kern_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in timed_ev]
     kern_avg_ms = float(np.mean(kern_ms))
     bytes_avg = float(np.mean([step_bytes[s] for s in timed]))
-    achieved = bytes_avg / (kern_avg_ms * 1e-3) / 1e9
+    kern_bytes_avg = float(np.mean([step_bytes[s] for s in timed_ev]))  # those launches' bytes
+    achieved = kern_bytes_avg / (kern_avg_ms * 1e-3) / 1e9
     value = bytes_avg / (ms_per_step * 1e-3) / 1e9
     tokens_per_s = B / (ms_per_step * 1e-3)
 
@@ -1397,6 +1478,9 @@ def main():
         "tokens_per_s": round(tokens_per_s, 1),
         "decode_kernel_ms": round(kern_avg_ms, 5),
         "decode_kernel_tokens_per_s": round(B / (kern_avg_ms * 1e-3), 1),
+        "timing_events": {"kind": ("HIP events without the system-scope fence" if EVENT_KIND == "device"
+                                   else "torch.cuda.Event (system-scope fence)"),
+                          "decode_calls_bracketed": len(timed_ev), "every": te},
         "partition_size": args.partition,
         "cache_hint": not args.no_cache_hint,
         "checked": bool(args.check),
@@ -1411,7 +1495,7 @@ def main():
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
                      "traffic_detail": traffic,
                      "kernel": "paged_attention_decode (decode + partition merge)",
-                     "bytes_per_launch": round(bytes_avg),
+                     "bytes_per_launch": round(kern_bytes_avg),
                      "measured_read": ceiling},
         "kernel_protocol": protocol,
         "stated_partition": stated,

@@ -17,16 +17,64 @@ Every computation is a call into ``libpkv.so``; this class only keeps the buffer
 The step's slots and positions are written into pinned host buffers that the append kernel
 reads in place, so a step uploads nothing but the copy-on-write pairs (when there are any)
 and the hint (when it changed).  ``nbuf`` sets of those buffers rotate; before the host
-rewrites a set it waits for the kernel that last read it.  Everything is enqueued on the
-current stream of the caches' device.
+rewrites a set it waits until the step that last used it is done on the device.  It learns
+that from marks, events recorded on the stream after a step's kernels.  Every recorded event
+leaves the GPU idle for a few microseconds between the kernels around it, so a mark is
+recorded only every ``mark_every`` steps (``mark_every`` <= ``nbuf``, so a mark at or after
+the step a set waits for is always there).  Everything is enqueued on the current stream of
+the caches' device.
 """
 from __future__ import annotations
 
+import collections
 import time
 
 import numpy as np
 
 from . import api
+
+
+class StepMarks:
+    """Marks after steps: ``after_step(s)`` records one (an event from ``new_event``) when
+    ``every`` steps have passed since the last, or takes the caller's own event, already
+    recorded after step s; ``wait_for(s)`` blocks the host until step s's device work is done,
+    by waiting on the first mark recorded at or after step s (recording one first if there is
+    none)."""
+
+    def __init__(self, new_event, every: int):
+        if every < 1:
+            raise ValueError("every must be at least 1")
+        self._new_event = new_event
+        self.every = int(every)
+        self._marks = collections.deque()  # (step, event, ours), steps increasing
+        self._free = []
+        self._last = None  # step of the latest mark
+        self._step = -1  # latest step seen by after_step
+        self.recorded = 0  # marks recorded here (not the caller's events)
+
+    def _record(self, step):
+        e = self._free.pop() if self._free else self._new_event()
+        e.record()
+        self.recorded += 1
+        self._marks.append((step, e, True))
+        self._last = step
+
+    def after_step(self, step: int, event=None):
+        self._step = step
+        if event is not None:
+            self._marks.append((step, event, False))
+            self._last = step
+        elif self._last is None or step - self._last >= self.every:
+            self._record(step)
+
+    def wait_for(self, step: int):
+        while self._marks and self._marks[0][0] < step:
+            _, e, ours = self._marks.popleft()
+            if ours:
+                self._free.append(e)
+        if not self._marks:
+            self._record(self._step)
+        self._marks[0][1].synchronize()
 
 
 class DecodeStep:
@@ -38,7 +86,8 @@ class DecodeStep:
     shared with other sequences as the decode's cached_blocks hint."""
 
     def __init__(self, alloc, seq_ids, k_cache, v_cache, num_q_heads: int, max_context_len: int,
-                 scale: float, partition_size: int = -1, cache_hint: bool = True, nbuf: int = 2):
+                 scale: float, partition_size: int = -1, cache_hint: bool = True, nbuf: int = 8,
+                 mark_every: int = 4):
         import torch
         dev = k_cache.device
         self.alloc = alloc
@@ -61,9 +110,9 @@ class DecodeStep:
         self._pos = [pin(B, torch.int32) for _ in range(self.nbuf)]
         self._pairs = [pin(2 * B, torch.int32) for _ in range(self.nbuf)]
         self._hint = [pin(B, torch.int32) for _ in range(self.nbuf)]
-        self._done = [torch.cuda.Event() for _ in range(self.nbuf)]
-        for e in self._done:
-            e.record()
+        if not 1 <= mark_every <= self.nbuf:
+            raise ValueError("mark_every must lie in [1, nbuf]")
+        self.marks = StepMarks(torch.cuda.Event, mark_every)
         self.pairs_d = torch.empty((max(B, 1), 2), dtype=torch.int32, device=dev)
         self.hint_d = torch.zeros(max(B, 1), dtype=torch.int32, device=dev) if cache_hint else None
         self._hint_sent = None
@@ -78,11 +127,14 @@ class DecodeStep:
     def __call__(self, k_new, v_new, q, out, events=None):
         """One step: k_new/v_new [B, Hkv, D] are the new tokens' K/V, q [B, Hq, D] their
         queries (GPU); the attention output goes to out [B, Hq, D].  ``events``: an optional
-        pair of torch events recorded around the decode call."""
+        pair of events (``record()``, ``synchronize()``) recorded around the decode call;
+        the second then also marks the step's end."""
         B = self.ids.size
-        i = self.steps % self.nbuf
+        step = self.steps
+        i = step % self.nbuf
         self.steps += 1
-        self._done[i].synchronize()  # the kernel that last read this buffer set is done
+        if step >= self.nbuf:
+            self.marks.wait_for(step - self.nbuf)  # the step that last used this buffer set
         h0 = time.perf_counter()
         pos = self._pos[i].numpy()[:B]
         self.alloc.pkv_seq_lengths(self.ids, pos)
@@ -112,12 +164,8 @@ class DecodeStep:
                                        self.max_context_len, self.scale, self.partition_size,
                                        self.workspace,
                                        self.hint_d[:B] if self.hint_d is not None else None)
-        # Every event recorded on the stream leaves the GPU idle for a few microseconds, so the
-        # buffer set's release is marked after the decode, by the timing event when there is
-        # one (the append kernel, its only reader, finished before).
+        # A timing event after the decode serves as this step's mark.
         if events is not None:
             events[1].record()
-            self._done[i] = events[1]
-        else:
-            self._done[i].record()
+        self.marks.after_step(step, events[1] if events is not None else None)
         return out
