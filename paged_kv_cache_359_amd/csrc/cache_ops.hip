@@ -134,7 +134,14 @@ __global__ __launch_bounds__(256) void append_and_cache_kernel(
 
 // Whole-block moves between the pools and a contiguous buffer (swap preemption): with
 // OUT, dst[i] = pool[blocks[i]]; otherwise pool[blocks[i]] = src[i].  Ids outside
-// [0, num_blocks) are skipped.
+// [0, num_blocks) are skipped.  Every byte is read once, so the loads are non-temporal, and
+// each thread has kMoveUnroll vectors of K and of V in flight before it stores any: few,
+// long-lived workgroups move the data (short ones spend their time being launched and
+// drained).  The stores are ordinary: non-temporal ones made the kernel's completion wait
+// tens of microseconds after its last wave.
+constexpr int kMoveUnroll = 4;
+typedef uint32_t move_vec __attribute__((ext_vector_type(4)));  // what the nt builtin takes
+
 template <bool OUT>
 __global__ __launch_bounds__(256) void move_blocks_kernel(uint4* k_cache, uint4* v_cache,
                                                           uint4* k_buf, uint4* v_buf,
@@ -143,15 +150,28 @@ __global__ __launch_bounds__(256) void move_blocks_kernel(uint4* k_cache, uint4*
   const int32_t id = blocks[blockIdx.x];
   if ((unsigned)id >= (unsigned)num_blocks) return;
   const int64_t po = int64_t(id) * blk_vecs, bo = int64_t(blockIdx.x) * blk_vecs;
-  for (int64_t i = int64_t(blockIdx.y) * blockDim.x + threadIdx.x; i < blk_vecs;
-       i += int64_t(gridDim.y) * blockDim.x) {
-    if constexpr (OUT) {
-      k_buf[bo + i] = k_cache[po + i];
-      v_buf[bo + i] = v_cache[po + i];
-    } else {
-      k_cache[po + i] = k_buf[bo + i];
-      v_cache[po + i] = v_buf[bo + i];
+  const move_vec* ks = reinterpret_cast<const move_vec*>(OUT ? k_cache + po : k_buf + bo);
+  const move_vec* vs = reinterpret_cast<const move_vec*>(OUT ? v_cache + po : v_buf + bo);
+  move_vec* kd = reinterpret_cast<move_vec*>(OUT ? k_buf + bo : k_cache + po);
+  move_vec* vd = reinterpret_cast<move_vec*>(OUT ? v_buf + bo : v_cache + po);
+  const int64_t step = int64_t(gridDim.y) * blockDim.x;
+  int64_t i = int64_t(blockIdx.y) * blockDim.x + threadIdx.x;
+  for (; i + (kMoveUnroll - 1) * step < blk_vecs; i += kMoveUnroll * step) {
+    move_vec kv[kMoveUnroll], vv[kMoveUnroll];
+#pragma unroll
+    for (int u = 0; u < kMoveUnroll; ++u) {
+      kv[u] = __builtin_nontemporal_load(ks + i + u * step);
+      vv[u] = __builtin_nontemporal_load(vs + i + u * step);
     }
+#pragma unroll
+    for (int u = 0; u < kMoveUnroll; ++u) {
+      kd[i + u * step] = kv[u];
+      vd[i + u * step] = vv[u];
+    }
+  }
+  for (; i < blk_vecs; i += step) {
+    kd[i] = __builtin_nontemporal_load(ks + i);
+    vd[i] = __builtin_nontemporal_load(vs + i);
   }
 }
 
@@ -187,7 +207,9 @@ pkv_status move_blocks(bool out, void* k_cache, void* v_cache, void* k_buf, void
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_buf) || !aligned16(v_buf))
     return PKV_ERR_INVALID_ARG;
   const int64_t blk_vecs = blk_bytes / 16;
-  int64_t ychunks = (blk_vecs + 255) / 256;
+  // Workgroups per block: each thread moves about 2 * kMoveUnroll vectors of K and of V.
+  int64_t ychunks = blk_vecs / (256 * 2 * kMoveUnroll);
+  if (ychunks < 1) ychunks = 1;
   if (ychunks > 64) ychunks = 64;
   clear_stale_error();
   auto k = out ? move_blocks_kernel<true> : move_blocks_kernel<false>;
