@@ -609,10 +609,7 @@ def main_prefill(args, cfg):
     """One step = the whole prefill path for the batch's chunk: fork each sequence's cached
     context (a template sequence), extend the fork by its new tokens (C++ allocator: new
     blocks, copy-on-write of a partly filled shared last block), upload tables/lengths/
-    slots, copy blocks, write the chunk's K/V, causal paged prefill; the forks are freed once
-    the step is done on the device.  Steps are issued back to back over two sets of forks
-    and staging buffers, as a serving loop would: the host prepares a step while the device
-    runs the one before."""
+    slots, copy blocks, write the chunk's K/V, causal paged prefill, free the forks."""
     import torch
     import workloads as W
     import paged_kv_cache_359_amd as pkv
@@ -645,20 +642,15 @@ def main_prefill(args, cfg):
     del rows
     max_blocks = -(-int(w.lengths.max()) // bs)
     out = torch.empty_like(w.q)
-    # Two sets of forks and staging buffers: the host prepares step s + 1 (allocator, tables,
-    # uploads) while the device still runs step s, and frees step s's forks only once the
-    # event after its prefill has completed.
-    NSET = 2
-    forks = [np.arange(B * (1 + p), B * (2 + p), dtype=np.int64) for p in range(NSET)]
-    pin = lambda shape, dt: torch.empty(shape, dtype=dt, pin_memory=True)  # noqa: E731
-    h_slots = [pin(T, torch.int64) for _ in range(NSET)]
-    h_pairs = [pin(2 * B, torch.int32) for _ in range(NSET)]
-    h_tables = [pin((B, max_blocks), torch.int32) for _ in range(NSET)]
-    h_lens = [pin(B, torch.int32) for _ in range(NSET)]
-    d_slots = [torch.empty(T, dtype=torch.int64, device=dev) for _ in range(NSET)]
-    d_pairs = [torch.empty((B, 2), dtype=torch.int32, device=dev) for _ in range(NSET)]
-    d_tables = [torch.empty((B, max_blocks), dtype=torch.int32, device=dev) for _ in range(NSET)]
-    d_lens = [torch.empty(B, dtype=torch.int32, device=dev) for _ in range(NSET)]
+    forks = np.arange(B, 2 * B, dtype=np.int64)
+    h_slots = torch.empty(T, dtype=torch.int64, pin_memory=True)
+    h_pairs = torch.empty(2 * B, dtype=torch.int32, pin_memory=True)
+    h_tables = torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True)
+    h_lens = torch.empty(B, dtype=torch.int32, pin_memory=True)
+    d_slots = torch.empty(T, dtype=torch.int64, device=dev)
+    d_pairs = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    d_tables = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
+    d_lens = torch.empty(B, dtype=torch.int32, device=dev)
     d_qs = torch.from_numpy(qs.astype(np.int32)).to(dev)
     max_q = int(w.n_new.max())
     max_ctx = int(w.lengths.max())
@@ -668,31 +660,29 @@ def main_prefill(args, cfg):
           for _ in range(total_steps)]
 
     def step(s):
-        p = s % NSET
-        if s >= NSET:  # the step that last used this set is done: its forks go back
-            ev[s - NSET][1].synchronize()
-            for f in forks[p]:
-                alloc.pkv_seq_free(int(f))
-        sl, pr = h_slots[p].numpy(), h_pairs[p].numpy()
+        sl, pr = h_slots.numpy(), h_pairs.numpy()
         ncow = 0
         for b in range(B):
-            alloc.pkv_seq_fork(b, int(forks[p][b]))
-            sb, pb = alloc.pkv_seq_extend(int(forks[p][b]), int(w.n_new[b]))
+            alloc.pkv_seq_fork(b, B + b)
+            sb, pb = alloc.pkv_seq_extend(B + b, int(w.n_new[b]))
             sl[qs[b]:qs[b + 1]] = sb
             pr[2 * ncow: 2 * ncow + pb.size] = pb.reshape(-1)
             ncow += pb.shape[0]
-        alloc.pkv_get_block_tables(forks[p], max_blocks, h_tables[p].numpy(), h_lens[p].numpy())
-        d_slots[p].copy_(h_slots[p], non_blocking=True)
-        d_tables[p].copy_(h_tables[p], non_blocking=True)
-        d_lens[p].copy_(h_lens[p], non_blocking=True)
+        alloc.pkv_get_block_tables(forks, max_blocks, h_tables.numpy(), h_lens.numpy())
+        d_slots.copy_(h_slots, non_blocking=True)
+        d_tables.copy_(h_tables, non_blocking=True)
+        d_lens.copy_(h_lens, non_blocking=True)
         if ncow:
-            d_pairs[p].view(-1)[: 2 * ncow].copy_(h_pairs[p][: 2 * ncow], non_blocking=True)
-            pkv.pkv_copy_blocks(k_cache, v_cache, d_pairs[p][:ncow])
-        pkv.pkv_reshape_and_cache(k_new, v_new, d_slots[p], k_cache, v_cache)
+            d_pairs.view(-1)[: 2 * ncow].copy_(h_pairs[: 2 * ncow], non_blocking=True)
+            pkv.pkv_copy_blocks(k_cache, v_cache, d_pairs[:ncow])
+        pkv.pkv_reshape_and_cache(k_new, v_new, d_slots, k_cache, v_cache)
         ev[s][0].record(stream)
-        pkv.pkv_paged_attention_prefill(out, w.q, k_cache, v_cache, d_tables[p], d_lens[p], d_qs,
+        pkv.pkv_paged_attention_prefill(out, w.q, k_cache, v_cache, d_tables, d_lens, d_qs,
                                         max_q, max_ctx, c.scale)
         ev[s][1].record(stream)
+        stream.synchronize()  # the staging buffers and the forks are reused next step
+        for b in range(B):
+            alloc.pkv_seq_free(B + b)
 
     for s in range(args.warmup):
         step(s)
